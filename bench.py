@@ -1,0 +1,185 @@
+"""Throughput of the four-layer bidirectional LSTM stack on one MI355X.
+
+One step = one bilstm_forward over a batch of synthetic windows (the whole hot path: four
+projections and eight direction recurrences). Default workload: 32 windows x 589 frames.
+
+Prints one JSON line: frames/s over the timed steps, per-phase times from the plan's HIP
+events, the recurrence's roofline figures and per-step latency against its on-chip bound,
+the projection's fraction of FP32-MFMA peak, and the oracle timed on the host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+PEAK_FP32_MFMA_TFLOPS = 157.3      # MI355X dense FP32 matrix peak (published)
+PEAK_FP32_VECTOR_TFLOPS = 157.3    # MI355X FP32 vector peak (published, packed dual-issue)
+CU_COUNT_NOMINAL = 256
+CLOCK_GHZ = 2.4
+FMA_PER_CLK_PER_CU = 64            # non-packed FP32 FMA: 4 SIMDs x 16 lanes
+
+RECUR_FMA_PER_FRAME_DIR = 512 * 128                   # R·h per step per direction
+
+
+def projection_flops(frames: int) -> float:
+    """Algorithmic FLOPs of the four projections: 2·M·1024·K summed over K = 60, 256, 256, 256."""
+    return 2.0 * frames * 1024 * (60 + 3 * 256)
+
+
+def recurrence_flops_per_layer(frames: int) -> float:
+    """Algorithmic FLOPs of one layer's recurrence, both directions: 2·65,536 per frame and direction."""
+    return 2.0 * 2 * frames * RECUR_FMA_PER_FRAME_DIR
+
+
+def cpu_baseline(x, layers, steps, max_threads=16, target_windows=None):
+    import oracle
+    oracle.build(force=False)
+    threads = max(1, min(max_threads, os.cpu_count() or 1))
+    windows = target_windows or min(x.shape[0], 2 * threads)
+    idx = list(range(windows))
+    t0 = time.perf_counter()
+    oracle.stack(x, layers, windows=idx, threads=threads)
+    wall = time.perf_counter() - t0
+    used = min(threads, windows)
+    return {"value": windows * steps / wall, "unit": "frames/s", "cores": used, "kind": "oracle",
+            "sample": f"{windows} of the {x.shape[0]} windows ({windows * steps} frames), one window per "
+                      f"task on {used} threads, fp64 single-threaded routine per window; wall {wall:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="b32", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--groups", type=int, default=0)
+    ap.add_argument("--tile", type=int, default=0)
+    ap.add_argument("--concurrent", type=int, default=-1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the stack shards by windows "
+                                   "(see DESIGN.md) but no multi-GPU path is built",
+                          "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+    import bidirectional_lstm_sequence_amd as bl
+
+    wl = workloads.WORKLOADS[args.workload]
+    x, layers = workloads.make_workload(wl)
+    frames = wl.batch * wl.steps
+    plan = bl.Plan(layers, wl.batch, wl.steps, groups=args.groups, tile=args.tile,
+                   concurrent=args.concurrent)
+    info = plan.info()
+    xd = torch.from_numpy(x).cuda()
+    yd = torch.empty((wl.batch, wl.steps, 256), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        plan.forward(xd, yd)
+    plan.check()
+
+    # timed region: exactly K forwards, bracketed by synchronisation; per-step HIP events on
+    # the caller's stream (the plan joins its side stream back into it)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for k in range(args.steps):
+        plan.forward(xd, yd)
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    plan.check()
+    step_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
+    total_ms = ev[0].elapsed_time(ev[args.steps])
+    value = frames * args.steps / (total_ms / 1e3)
+
+    # per-phase split, outside the timed region
+    plan.set_phase_events(True)
+    proj_ms = [[] for _ in range(4)]
+    rec_ms = [[] for _ in range(4)]
+    for _ in range(max(3, min(10, args.steps))):
+        plan.forward(xd, yd)
+        pt = plan.phase_times()
+        for l in range(4):
+            proj_ms[l].append(pt["projection_ms"][l])
+            rec_ms[l].append(pt["recurrence_ms"][l])
+    plan.set_phase_events(False)
+    proj_med = [statistics.median(v) for v in proj_ms]
+    rec_med = [statistics.median(v) for v in rec_ms]
+    plan.check()
+    plan.close()
+
+    # recurrence: the dominant kernel (both directions of a layer run concurrently, so one
+    # layer's recurrence phase is the duration of its two concurrent launches)
+    rec_layer_ms = statistics.mean(rec_med)
+    rec_tflops = recurrence_flops_per_layer(frames) / (rec_layer_ms / 1e3) / 1e12
+    us_per_step = rec_layer_ms * 1e3 / wl.steps
+    groups, tile = info["recur_groups"], info["recur_tile"]
+    fma_clk = RECUR_FMA_PER_FRAME_DIR * tile / groups / FMA_PER_CLK_PER_CU
+    xchg_ns = None
+    if not args.no_probe:
+        try:
+            xchg_ns = bl.probe_exchange(0, True, 2000)["one_way_ns"]
+        except Exception as e:  # measurement only
+            print(f"exchange probe failed: {e}", file=sys.stderr)
+    bound_us = fma_clk / (CLOCK_GHZ * 1e3) + ((xchg_ns or 0.0) / 1e3 if groups > 1 else 0.0)
+
+    # projection: fraction of FP32-MFMA peak over the four projection phases
+    proj_total_ms = sum(proj_med)
+    proj_tflops = projection_flops(frames) / (proj_total_ms / 1e3) / 1e12
+
+    out = {
+        "metric": "frames/sec through 4-layer BiLSTM (H=128) at B=32,T=589; per-step latency",
+        "value": value,
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded U(-1/sqrt(128), 1/sqrt(128)) weights, N(0,1) input windows",
+        "config": {"workload": f"{wl.name}: {wl.batch} windows x {wl.steps} frames, 4-layer BiLSTM "
+                               f"H=128, input 60", "batch": wl.batch, "seq_len": wl.steps,
+                   "recurrence_split": {"groups": groups, "tile": tile, "tiles": info["recur_tiles"],
+                                        "concurrent": info["concurrent"]}},
+        "roofline": {"kernel": "recurrence (one layer, both directions concurrent)", "bound": "alu",
+                     "achieved": rec_tflops, "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
+                     "frac": rec_tflops / PEAK_FP32_VECTOR_TFLOPS, "traffic": None},
+        "recurrence_step": {"us_per_step": us_per_step, "bound_us": bound_us,
+                            "frac_of_bound": bound_us / us_per_step, "exchange_one_way_ns": xchg_ns,
+                            "bound_terms": f"FMA {fma_clk:.0f} clk at {FMA_PER_CLK_PER_CU} FMA/clk/CU, "
+                                           f"{CLOCK_GHZ} GHz" + (" + one exchange" if groups > 1 else "")},
+        "projection": {"ms_total": proj_total_ms, "ms_per_layer": proj_med, "achieved_tflops": proj_tflops,
+                       "peak_tflops": PEAK_FP32_MFMA_TFLOPS, "frac": proj_tflops / PEAK_FP32_MFMA_TFLOPS},
+        "phases_ms": {"projection": proj_med, "recurrence": rec_med},
+        "step_ms": {"median": statistics.median(step_ms), "min": min(step_ms), "max": max(step_ms)},
+        "wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, layers, wl.steps)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

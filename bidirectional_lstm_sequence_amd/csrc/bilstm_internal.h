@@ -1,0 +1,76 @@
+// Internal declarations shared by the host plan code and the HIP kernels of the
+// bidirectional LSTM library. Not part of the public ABI (include/bilstm.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace bl {
+
+constexpr int kHidden = 128;               // H
+constexpr int kGates = 512;                // 4H gate rows per direction
+constexpr int kGateCols = 1024;            // both directions side by side in the gate buffer
+constexpr int kWidth = 256;                // 2H
+constexpr int kFeatures = 60;
+constexpr int kLayers = 4;
+
+// Projection GEMM tile (rows x gate columns) and K step.
+constexpr int kProjTileM = 128;
+constexpr int kProjTileN = 128;
+constexpr int kProjTileK = 32;
+constexpr int kProjThreads = 256;
+
+inline int padded_input(int in) { return (in + kProjTileK - 1) / kProjTileK * kProjTileK; }
+
+// Threads per recurrence workgroup for `groups` workgroups per (direction, tile).
+inline int recur_threads(int groups) {
+    const int units = kHidden / groups;
+    const int lanes = groups == 1 ? 4 : (groups == 2 ? 8 : 16);
+    return units * lanes;
+}
+
+// Exchange words of one direction: [tiles][2 parities][128 units][tile] u64 words.
+inline size_t exchange_words_per_direction(int tiles, int tile) {
+    return static_cast<size_t>(tiles) * 2 * kHidden * tile;
+}
+
+struct ProjArgs {
+    const float *x;      // [rows][in]
+    const float *w;      // [1024][kpad]
+    const float *bias;   // [1024]
+    float *gates;        // [rows][1024]
+    int rows;
+    int in;
+    int kpad;
+    int row_tiles;       // ceil(rows / kProjTileM)
+    int tiles;           // row_tiles * (1024 / kProjTileN)
+};
+
+struct RecurArgs {
+    const float *gates;            // [batch*steps][1024], bias included
+    const float *r;                // [2][512][128] packed rows 4j+g
+    float *y;                      // [batch][steps][256]
+    unsigned long long *exchange;  // [2][tiles][2][128][tile] words (groups > 1)
+    unsigned int *error;           // watchdog flag word
+    int batch;
+    int steps;
+    int direction;                 // direction of blockIdx.y == 0
+    int tiles;                     // window tiles in the whole batch
+    int tile_first;                // first tile of this launch
+    int tile_count;                // tiles in this launch
+    unsigned int flag_base;        // flags of this layer are flag_base + s + 1
+    unsigned long long timeout_ticks;  // watchdog, in wall-clock ticks
+};
+
+// Launchers (kernels_*.hip). They return the launch's hipError_t.
+hipError_t launch_projection(const ProjArgs &args, hipStream_t stream);
+hipError_t launch_recurrence(int groups, int tile, const RecurArgs &args, int directions,
+                             hipStream_t stream);
+hipError_t launch_exchange_clear(unsigned long long *words, size_t count, hipStream_t stream);
+hipError_t recurrence_occupancy(int groups, int tile, int *per_cu);
+hipError_t run_exchange_probe(int same_xcd, int round_trips, unsigned long long timeout_ticks,
+                              double ticks_per_ns, double *one_way_ns, int *xcd_a, int *xcd_b);
+
+}  // namespace bl

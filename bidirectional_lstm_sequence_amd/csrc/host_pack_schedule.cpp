@@ -1,0 +1,157 @@
+// Host-only parts of the library: the weight packer and the recurrence schedule. Neither
+// touches the GPU, so both are exported for tests that run without a device.
+#include <algorithm>
+#include <cstring>
+
+#include "../../include/bilstm.h"
+#include "bilstm_host.h"
+
+namespace bl {
+
+// Packed gate row of source row `src` (gate g = src / 128, unit j = src % 128): 4j + g, so a
+// hidden unit's four gates are adjacent (speakrs 0.6.0, page `lstmproj.rs`, module doc).
+static inline int packed_row(int src) { return 4 * (src % kHidden) + src / kHidden; }
+
+bilstm_status pack_layer(const bilstm_layer &layer, int in, float *w_out, float *r_out,
+                         float *bias_out) {
+    const int kpad = padded_input(in);
+    std::memset(w_out, 0, sizeof(float) * static_cast<size_t>(kGateCols) * kpad);
+    for (int d = 0; d < 2; ++d) {
+        for (int src = 0; src < kGates; ++src) {
+            const int row = d * kGates + packed_row(src);
+            const float *w = layer.w + (static_cast<size_t>(d) * kGates + src) * in;
+            std::memcpy(w_out + static_cast<size_t>(row) * kpad, w, sizeof(float) * in);
+            const float *r = layer.r + (static_cast<size_t>(d) * kGates + src) * kHidden;
+            std::memcpy(r_out + (static_cast<size_t>(d) * kGates + packed_row(src)) * kHidden, r,
+                        sizeof(float) * kHidden);
+            const float wb = layer.b[(static_cast<size_t>(d) * 2 + 0) * kGates + src];
+            const float rb = layer.b[(static_cast<size_t>(d) * 2 + 1) * kGates + src];
+            bias_out[row] = wb + rb;  // one fp32 round-to-nearest addition
+        }
+    }
+    return BILSTM_OK;
+}
+
+static bool valid_groups(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+static bool valid_tile(int t) { return t == 1 || t == 2 || t == 4; }
+
+bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
+                       const bilstm_options *opt, bilstm_plan_info *info) {
+    if (batch == 0 || steps == 0) {
+        return fail(BILSTM_INVALID_ARGUMENT, "schedule: batch (%u) and steps (%u) must be >= 1", batch, steps);
+    }
+    if (cu_count <= 0 || per_cu <= 0) {
+        return fail(BILSTM_INVALID_ARGUMENT, "schedule: cu_count (%d) and per_cu (%d) must be >= 1",
+                    cu_count, per_cu);
+    }
+    if (opt != nullptr) {
+        for (int i = 0; i < 4; ++i) {
+            if (opt->reserved[i] != 0) return fail(BILSTM_INVALID_ARGUMENT, "options: reserved[%d] must be 0", i);
+        }
+        if (opt->recur_groups != 0 && !valid_groups(opt->recur_groups)) {
+            return fail(BILSTM_UNSUPPORTED, "options: recur_groups %d is not one of 1, 2, 4, 8, 16",
+                        opt->recur_groups);
+        }
+        if (opt->recur_tile != 0 && !valid_tile(opt->recur_tile)) {
+            return fail(BILSTM_UNSUPPORTED, "options: recur_tile %d is not one of 1, 2, 4", opt->recur_tile);
+        }
+        if (opt->watchdog_us < 0) {
+            return fail(BILSTM_INVALID_ARGUMENT, "options: watchdog_us %d is negative", opt->watchdog_us);
+        }
+        if (opt->concurrent < -1 || opt->concurrent > 2) {
+            return fail(BILSTM_INVALID_ARGUMENT, "options: concurrent %d is not -1, 0, 1 or 2", opt->concurrent);
+        }
+    }
+    const int capacity = cu_count * per_cu;
+    const int want_groups = (opt != nullptr) ? opt->recur_groups : 0;
+    const int want_tile = (opt != nullptr) ? opt->recur_tile : 0;
+    const int want_conc = (opt != nullptr) ? opt->concurrent : -1;
+
+    // Workgroups per tile: one workgroup holds the whole recurrent matrix of a direction and
+    // needs no exchange. That is the default until the exchange variant is measured faster.
+    const int groups = want_groups != 0 ? want_groups : 1;
+    // Windows per tile: the fewest that let both directions' grids fit the GPU at once.
+    int tile = want_tile;
+    if (tile == 0) {
+        tile = 4;
+        for (int t : {1, 2, 4}) {
+            const long long tiles = (static_cast<long long>(batch) + t - 1) / t;
+            if (2 * tiles * groups <= capacity) {
+                tile = t;
+                break;
+            }
+        }
+    }
+    const int tiles = static_cast<int>((static_cast<long long>(batch) + tile - 1) / tile);
+    const long long grid = static_cast<long long>(tiles) * groups;
+
+    // Workgroups of a tile wait for each other when groups > 1, so each launch's grid must
+    // fit the resident capacity; both directions run at once only if both grids fit together.
+    int launches = 1;
+    if (groups > 1) {
+        const int per_launch = std::max(1, capacity / groups);
+        if (groups > capacity) {
+            return fail(BILSTM_UNSUPPORTED, "schedule: %d workgroups per tile exceed the resident capacity %d",
+                        groups, capacity);
+        }
+        launches = (tiles + per_launch - 1) / per_launch;
+    }
+    const bool joint_fits = groups == 1 || 2 * grid <= capacity;
+    int concurrent;
+    if (want_conc == -1) {
+        concurrent = joint_fits ? 1 : 0;
+    } else {
+        concurrent = want_conc;
+        if (concurrent != 0 && !joint_fits) {
+            return fail(BILSTM_UNSUPPORTED,
+                        "schedule: concurrent directions need both grids (2 x %lld workgroups) resident "
+                        "together, capacity is %d", grid, capacity);
+        }
+    }
+
+    info->batch = batch;
+    info->steps = steps;
+    info->recur_groups = groups;
+    info->recur_tile = tile;
+    info->recur_tiles = tiles;
+    info->recur_threads = recur_threads(groups);
+    info->recur_launches = launches;
+    info->concurrent = concurrent;
+    info->cu_count = cu_count;
+    info->recur_capacity = capacity;
+    return BILSTM_OK;
+}
+
+}  // namespace bl
+
+extern "C" bilstm_status bilstm_pack_layer(const bilstm_layer *layer, uint32_t in, float *w_out,
+                                           size_t w_out_len, float *r_out, size_t r_out_len,
+                                           float *bias_out, size_t bias_out_len) {
+    using namespace bl;
+    if (layer == nullptr || w_out == nullptr || r_out == nullptr || bias_out == nullptr ||
+        layer->w == nullptr || layer->r == nullptr || layer->b == nullptr) {
+        return fail(BILSTM_INVALID_ARGUMENT, "pack_layer: NULL pointer");
+    }
+    if (in == 0 || in % 4 != 0 || in > 4096) {
+        return fail(BILSTM_INVALID_ARGUMENT, "pack_layer: input width %u must be a positive multiple of 4", in);
+    }
+    const size_t kpad = static_cast<size_t>(padded_input(static_cast<int>(in)));
+    bilstm_status s;
+    if ((s = check_len("pack_layer W", 2ull * kGates * in, layer->w_len)) != BILSTM_OK) return s;
+    if ((s = check_len("pack_layer R", 2ull * kGates * kHidden, layer->r_len)) != BILSTM_OK) return s;
+    if ((s = check_len("pack_layer B", 4ull * kGates, layer->b_len)) != BILSTM_OK) return s;
+    if ((s = check_len("pack_layer packed W", kGateCols * kpad, w_out_len)) != BILSTM_OK) return s;
+    if ((s = check_len("pack_layer packed R", 2ull * kGates * kHidden, r_out_len)) != BILSTM_OK) return s;
+    if ((s = check_len("pack_layer packed bias", kGateCols, bias_out_len)) != BILSTM_OK) return s;
+    return pack_layer(*layer, static_cast<int>(in), w_out, r_out, bias_out);
+}
+
+extern "C" bilstm_status bilstm_schedule(uint32_t batch, uint32_t steps, int32_t cu_count,
+                                         int32_t per_cu, const bilstm_options *options,
+                                         bilstm_plan_info *info) {
+    if (info == nullptr) return bl::fail(BILSTM_INVALID_ARGUMENT, "schedule: info is NULL");
+    std::memset(info, 0, sizeof(*info));
+    info->proj_tile_m = bl::kProjTileM;
+    info->proj_tile_n = bl::kProjTileN;
+    return bl::schedule(batch, steps, cu_count, per_cu, options, info);
+}

@@ -1,0 +1,523 @@
+// The C ABI of the library: plan creation (weight packing, scratch, side stream), the
+// forward pass and the per-phase entry points (speakrs 0.6.0, page `lstmproj.rs`:
+// `with_recurrence`, `Oxide::enqueue`, `Oxide::recur`, `clear_state`, `check_len`, `to_u32`).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/bilstm.h"
+#include "bilstm_host.h"
+
+namespace bl {
+
+namespace {
+thread_local std::string g_last_error;
+
+// Watchdog of a recurrence wait, in milliseconds. A step normally takes microseconds; the
+// limit only has to end a wait whose producer can never arrive.
+constexpr double kWatchdogMs = 2000.0;
+}  // namespace
+
+bilstm_status fail(bilstm_status status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+bilstm_status check_len(const char *context, size_t expected, size_t actual) {
+    if (expected == actual) return BILSTM_OK;
+    return fail(BILSTM_BUFFER_LENGTH, "%s: expected %zu elements, got %zu", context, expected, actual);
+}
+
+}  // namespace bl
+
+using namespace bl;
+
+struct bilstm_plan {
+    int device = 0;
+    uint32_t batch = 0;
+    uint32_t steps = 0;
+    size_t rows = 0;
+    bilstm_plan_info info{};
+    int in[kLayers] = {kFeatures, kWidth, kWidth, kWidth};
+    int kpad[kLayers] = {0, 0, 0, 0};
+    float *w[kLayers] = {nullptr, nullptr, nullptr, nullptr};
+    float *r[kLayers] = {nullptr, nullptr, nullptr, nullptr};
+    float *bias[kLayers] = {nullptr, nullptr, nullptr, nullptr};
+    float *gates = nullptr;
+    unsigned long long *exchange = nullptr;
+    size_t exchange_words = 0;
+    unsigned int *error = nullptr;
+    hipStream_t side = nullptr;
+    hipEvent_t fork[kLayers] = {nullptr, nullptr, nullptr, nullptr};
+    hipEvent_t join[kLayers] = {nullptr, nullptr, nullptr, nullptr};
+    bool phase_events = false;
+    hipEvent_t ev_start = nullptr;
+    hipEvent_t ev_proj[kLayers] = {nullptr, nullptr, nullptr, nullptr};
+    hipEvent_t ev_recur[kLayers] = {nullptr, nullptr, nullptr, nullptr};
+    bool phases_recorded = false;
+    uint32_t epoch = 0;  // flags of the next pass start above this value
+    unsigned long long timeout_ticks = 0;
+    double watchdog_ms = 0.0;
+    uint64_t device_bytes = 0;
+};
+
+namespace {
+
+// Make `device` current for the scope and restore the caller's device afterwards.
+class DeviceScope {
+public:
+    explicit DeviceScope(int device) {
+        ok_ = hipGetDevice(&saved_) == hipSuccess;
+        err_ = hipSetDevice(device);
+    }
+    ~DeviceScope() {
+        if (ok_) (void)hipSetDevice(saved_);
+    }
+    hipError_t error() const { return err_; }
+
+private:
+    int saved_ = 0;
+    bool ok_ = false;
+    hipError_t err_ = hipSuccess;
+};
+
+#define BL_HIP(expr, context)                                                                \
+    do {                                                                                     \
+        hipError_t bl_e_ = (expr);                                                           \
+        if (bl_e_ != hipSuccess) {                                                           \
+            return fail(BILSTM_HIP_ERROR, "%s: %s failed: %s", context, #expr,               \
+                        hipGetErrorString(bl_e_));                                           \
+        }                                                                                    \
+    } while (0)
+
+template <typename T>
+bilstm_status device_alloc(bilstm_plan *p, T **out, size_t count, const char *what) {
+    void *ptr = nullptr;
+    const size_t bytes = count * sizeof(T) > 0 ? count * sizeof(T) : 16;
+    hipError_t e = hipMalloc(&ptr, bytes);
+    if (e != hipSuccess) {
+        return fail(BILSTM_HIP_ERROR, "plan_create: hipMalloc of %zu bytes for %s failed: %s", bytes,
+                    what, hipGetErrorString(e));
+    }
+    *out = static_cast<T *>(ptr);
+    p->device_bytes += bytes;
+    return BILSTM_OK;
+}
+
+void release(bilstm_plan *p) {
+    if (p == nullptr) return;
+    DeviceScope scope(p->device);
+    (void)hipDeviceSynchronize();
+    for (int l = 0; l < kLayers; ++l) {
+        if (p->w[l]) (void)hipFree(p->w[l]);
+        if (p->r[l]) (void)hipFree(p->r[l]);
+        if (p->bias[l]) (void)hipFree(p->bias[l]);
+        if (p->fork[l]) (void)hipEventDestroy(p->fork[l]);
+        if (p->join[l]) (void)hipEventDestroy(p->join[l]);
+        if (p->ev_proj[l]) (void)hipEventDestroy(p->ev_proj[l]);
+        if (p->ev_recur[l]) (void)hipEventDestroy(p->ev_recur[l]);
+    }
+    if (p->ev_start) (void)hipEventDestroy(p->ev_start);
+    if (p->gates) (void)hipFree(p->gates);
+    if (p->exchange) (void)hipFree(p->exchange);
+    if (p->error) (void)hipFree(p->error);
+    if (p->side) (void)hipStreamDestroy(p->side);
+    delete p;
+}
+
+bool is_gfx950(int device) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return false;
+    return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void *a, size_t a_bytes, const void *b, size_t b_bytes) {
+    const auto x = reinterpret_cast<uintptr_t>(a);
+    const auto y = reinterpret_cast<uintptr_t>(b);
+    return x < y + b_bytes && y < x + a_bytes;
+}
+
+// Zero the exchange words when the flags of the next pass would wrap, so no stale word can
+// carry a flag that pass expects (speakrs 0.6.0, page `lstmproj.rs`, `clear_state`: the
+// words are zeroed before a pass; here the zeroing happens at plan creation and whenever
+// the 32-bit flag space runs out, and every pass in between uses flags above all earlier
+// ones).
+bilstm_status reserve_flags(bilstm_plan *p, uint32_t count, hipStream_t stream, uint32_t *base) {
+    if (p->exchange == nullptr) {
+        *base = 0;
+        return BILSTM_OK;
+    }
+    if (static_cast<uint64_t>(p->epoch) + count + 1 > 0xFFFFFFFFull) {
+        BL_HIP(launch_exchange_clear(p->exchange, p->exchange_words, stream), "exchange clear");
+        p->epoch = 0;
+    }
+    *base = p->epoch;
+    p->epoch += count;
+    return BILSTM_OK;
+}
+
+bilstm_status enqueue_projection(bilstm_plan *p, int layer, const float *x, float *gates,
+                                 hipStream_t stream) {
+    ProjArgs args{};
+    args.x = x;
+    args.w = p->w[layer];
+    args.bias = p->bias[layer];
+    args.gates = gates;
+    args.rows = static_cast<int>(p->rows);
+    args.in = p->in[layer];
+    args.kpad = p->kpad[layer];
+    args.row_tiles = static_cast<int>((p->rows + kProjTileM - 1) / kProjTileM);
+    args.tiles = args.row_tiles * (kGateCols / kProjTileN);
+    BL_HIP(launch_projection(args, stream), "projection launch");
+    return BILSTM_OK;
+}
+
+// Both directions' recurrence of one layer (speakrs 0.6.0, page `lstmproj.rs`,
+// `Oxide::recur`: the reverse direction on the side stream when the schedule allows it,
+// joined back before the next layer).
+bilstm_status enqueue_recurrence(bilstm_plan *p, int layer, const float *gates, float *y,
+                                 uint32_t flag_base, hipStream_t stream) {
+    const bilstm_plan_info &s = p->info;
+    RecurArgs base{};
+    base.gates = gates;
+    base.r = p->r[layer];
+    base.y = y;
+    base.exchange = p->exchange;
+    base.error = p->error;
+    base.batch = static_cast<int>(p->batch);
+    base.steps = static_cast<int>(p->steps);
+    base.tiles = s.recur_tiles;
+    base.flag_base = flag_base;
+    base.timeout_ticks = p->timeout_ticks;
+
+    const int per_launch = (s.recur_tiles + s.recur_launches - 1) / s.recur_launches;
+    auto launch_direction = [&](int direction, int directions, hipStream_t on) -> bilstm_status {
+        for (int first = 0; first < s.recur_tiles; first += per_launch) {
+            RecurArgs a = base;
+            a.direction = direction;
+            a.tile_first = first;
+            a.tile_count = std::min(per_launch, s.recur_tiles - first);
+            BL_HIP(launch_recurrence(s.recur_groups, s.recur_tile, a, directions, on), "recurrence launch");
+        }
+        return BILSTM_OK;
+    };
+
+    bilstm_status st;
+    if (s.concurrent == 2) {
+        return launch_direction(0, 2, stream);
+    }
+    if (s.concurrent == 1) {
+        BL_HIP(hipEventRecord(p->fork[layer], stream), "fork");
+        BL_HIP(hipStreamWaitEvent(p->side, p->fork[layer], 0), "fork wait");
+        if ((st = launch_direction(0, 1, stream)) != BILSTM_OK) return st;
+        if ((st = launch_direction(1, 1, p->side)) != BILSTM_OK) return st;
+        BL_HIP(hipEventRecord(p->join[layer], p->side), "join");
+        BL_HIP(hipStreamWaitEvent(stream, p->join[layer], 0), "join wait");
+        return BILSTM_OK;
+    }
+    if ((st = launch_direction(0, 1, stream)) != BILSTM_OK) return st;
+    return launch_direction(1, 1, stream);
+}
+
+bilstm_status check_plan_buffers(const char *context, const bilstm_plan *p, const void *a,
+                                 const void *b) {
+    if (p == nullptr) return fail(BILSTM_INVALID_ARGUMENT, "%s: plan is NULL", context);
+    if (a == nullptr || b == nullptr) return fail(BILSTM_INVALID_ARGUMENT, "%s: NULL buffer", context);
+    if (!aligned16(a) || !aligned16(b)) {
+        return fail(BILSTM_INVALID_ARGUMENT, "%s: buffers must be 16-byte aligned", context);
+    }
+    return BILSTM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *bilstm_last_error(void) { return g_last_error.c_str(); }
+
+bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
+                                    const bilstm_layer layers[BILSTM_LAYERS],
+                                    const bilstm_options *options, bilstm_plan **out) {
+    if (out == nullptr) return fail(BILSTM_INVALID_ARGUMENT, "plan_create: out is NULL");
+    *out = nullptr;
+    if (layers == nullptr) return fail(BILSTM_INVALID_ARGUMENT, "plan_create: layers is NULL");
+    if (batch == 0 || steps == 0) {
+        return fail(BILSTM_INVALID_ARGUMENT, "plan_create: batch (%u) and steps (%u) must be >= 1", batch, steps);
+    }
+    const uint64_t rows = static_cast<uint64_t>(batch) * steps;
+    if (rows * kGateCols > 0xFFFFFFFFull) {
+        return fail(BILSTM_DIMENSION_OVERFLOW, "plan_create: batch*steps*1024 = %llu exceeds 32 bits",
+                    static_cast<unsigned long long>(rows * kGateCols));
+    }
+    if (4ull * steps + 2 > 0xFFFFFFFFull) {
+        return fail(BILSTM_DIMENSION_OVERFLOW, "plan_create: steps %u too large for the step flags", steps);
+    }
+    for (int l = 0; l < kLayers; ++l) {
+        const size_t in = l == 0 ? kFeatures : kWidth;
+        const bilstm_layer &L = layers[l];
+        if (L.w == nullptr || L.r == nullptr || L.b == nullptr) {
+            return fail(BILSTM_INVALID_ARGUMENT, "plan_create: layer %d has a NULL weight pointer", l);
+        }
+        char ctx[64];
+        bilstm_status s;
+        std::snprintf(ctx, sizeof(ctx), "plan_create layer %d W", l);
+        if ((s = check_len(ctx, 2 * kGates * in, L.w_len)) != BILSTM_OK) return s;
+        std::snprintf(ctx, sizeof(ctx), "plan_create layer %d R", l);
+        if ((s = check_len(ctx, 2ull * kGates * kHidden, L.r_len)) != BILSTM_OK) return s;
+        std::snprintf(ctx, sizeof(ctx), "plan_create layer %d B", l);
+        if ((s = check_len(ctx, 4ull * kGates, L.b_len)) != BILSTM_OK) return s;
+    }
+
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count == 0) {
+        return fail(BILSTM_UNSUPPORTED, "plan_create: no HIP device (%s)", hipGetErrorString(e));
+    }
+    if (device < 0 || device >= count) {
+        return fail(BILSTM_INVALID_ARGUMENT, "plan_create: device %d out of range (%d devices)", device, count);
+    }
+    if (!is_gfx950(device)) {
+        return fail(BILSTM_UNSUPPORTED, "plan_create: device %d is not a gfx950 (MI355X) GPU", device);
+    }
+    DeviceScope scope(device);
+    BL_HIP(scope.error(), "plan_create: hipSetDevice");
+
+    auto *p = new bilstm_plan();
+    p->device = device;
+    p->batch = batch;
+    p->steps = steps;
+    p->rows = rows;
+    auto fail_release = [&](bilstm_status s) {
+        release(p);
+        return s;
+    };
+
+    int cu_count = 0;
+    int wall_khz = 0;
+    e = hipDeviceGetAttribute(&cu_count, hipDeviceAttributeMultiprocessorCount, device);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, device);
+    if (e != hipSuccess || cu_count <= 0 || wall_khz <= 0) {
+        return fail_release(fail(BILSTM_HIP_ERROR, "plan_create: device attributes: %s", hipGetErrorString(e)));
+    }
+    const double watchdog_ms = (options != nullptr && options->watchdog_us > 0) ? options->watchdog_us / 1000.0
+                                                                                : kWatchdogMs;
+    p->timeout_ticks = static_cast<unsigned long long>(watchdog_ms * wall_khz);
+    p->watchdog_ms = watchdog_ms;
+
+    // choose the split, then size the launches from the chosen kernel's occupancy
+    bilstm_plan_info info{};
+    bilstm_options choose{};
+    if (options != nullptr) choose = *options;
+    choose.concurrent = -1;  // the concurrency request is checked once the occupancy is known
+    bilstm_status st = schedule(batch, steps, cu_count, 1, &choose, &info);
+    if (st != BILSTM_OK) return fail_release(st);
+    int per_cu = 0;
+    e = recurrence_occupancy(info.recur_groups, info.recur_tile, &per_cu);
+    if (e != hipSuccess || per_cu <= 0) {
+        return fail_release(fail(BILSTM_HIP_ERROR, "plan_create: recurrence occupancy: %s (%d per CU)",
+                                 hipGetErrorString(e), per_cu));
+    }
+    bilstm_options fixed{};
+    if (options != nullptr) fixed = *options;
+    fixed.recur_groups = info.recur_groups;
+    fixed.recur_tile = info.recur_tile;
+    st = schedule(batch, steps, cu_count, per_cu, &fixed, &info);
+    if (st != BILSTM_OK) return fail_release(st);
+    info.proj_tile_m = kProjTileM;
+    info.proj_tile_n = kProjTileN;
+    p->info = info;
+
+    // pack and upload the weights
+    for (int l = 0; l < kLayers; ++l) {
+        p->kpad[l] = padded_input(p->in[l]);
+        std::vector<float> w(static_cast<size_t>(kGateCols) * p->kpad[l]);
+        std::vector<float> r(2ull * kGates * kHidden);
+        std::vector<float> b(kGateCols);
+        pack_layer(layers[l], p->in[l], w.data(), r.data(), b.data());
+        if ((st = device_alloc(p, &p->w[l], w.size(), "W")) != BILSTM_OK) return fail_release(st);
+        if ((st = device_alloc(p, &p->r[l], r.size(), "R")) != BILSTM_OK) return fail_release(st);
+        if ((st = device_alloc(p, &p->bias[l], b.size(), "bias")) != BILSTM_OK) return fail_release(st);
+        e = hipMemcpy(p->w[l], w.data(), w.size() * sizeof(float), hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = hipMemcpy(p->r[l], r.data(), r.size() * sizeof(float), hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = hipMemcpy(p->bias[l], b.data(), b.size() * sizeof(float), hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            return fail_release(fail(BILSTM_HIP_ERROR, "plan_create: weight upload: %s", hipGetErrorString(e)));
+        }
+    }
+
+    if ((st = device_alloc(p, &p->gates, rows * kGateCols, "gates")) != BILSTM_OK) return fail_release(st);
+    if ((st = device_alloc(p, &p->error, 1, "error word")) != BILSTM_OK) return fail_release(st);
+    e = hipMemset(p->error, 0, sizeof(unsigned int));
+    if (info.recur_groups > 1) {
+        p->exchange_words = 2 * exchange_words_per_direction(info.recur_tiles, info.recur_tile);
+        if ((st = device_alloc(p, &p->exchange, p->exchange_words, "exchange")) != BILSTM_OK) {
+            return fail_release(st);
+        }
+        if (e == hipSuccess) e = hipMemset(p->exchange, 0, p->exchange_words * sizeof(unsigned long long));
+    }
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking);
+    for (int l = 0; l < kLayers && e == hipSuccess; ++l) {
+        e = hipEventCreateWithFlags(&p->fork[l], hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->join[l], hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreate(&p->ev_proj[l]);
+        if (e == hipSuccess) e = hipEventCreate(&p->ev_recur[l]);
+    }
+    if (e == hipSuccess) e = hipEventCreate(&p->ev_start);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        return fail_release(fail(BILSTM_HIP_ERROR, "plan_create: scratch setup: %s", hipGetErrorString(e)));
+    }
+    p->info.device_bytes = p->device_bytes;
+    *out = p;
+    return BILSTM_OK;
+}
+
+bilstm_status bilstm_plan_create(int device, uint32_t batch, uint32_t steps,
+                                 const bilstm_layer layers[BILSTM_LAYERS], bilstm_plan **out) {
+    return bilstm_plan_create_ex(device, batch, steps, layers, nullptr, out);
+}
+
+bilstm_status bilstm_forward(bilstm_plan *plan, const float *x, size_t x_len, float *y,
+                             size_t y_len, void *stream_ptr) {
+    bilstm_status st = check_plan_buffers("forward", plan, x, y);
+    if (st != BILSTM_OK) return st;
+    if ((st = check_len("forward input", plan->rows * kFeatures, x_len)) != BILSTM_OK) return st;
+    if ((st = check_len("forward output", plan->rows * kWidth, y_len)) != BILSTM_OK) return st;
+    if (overlap(x, x_len * sizeof(float), y, y_len * sizeof(float))) {
+        return fail(BILSTM_INVALID_ARGUMENT, "forward: input and output overlap");
+    }
+    auto stream = static_cast<hipStream_t>(stream_ptr);
+    DeviceScope scope(plan->device);
+    BL_HIP(scope.error(), "forward: hipSetDevice");
+
+    uint32_t base = 0;
+    if ((st = reserve_flags(plan, kLayers * plan->steps, stream, &base)) != BILSTM_OK) return st;
+    if (plan->phase_events) BL_HIP(hipEventRecord(plan->ev_start, stream), "phase event");
+    for (int l = 0; l < kLayers; ++l) {
+        // every layer after the first reads the previous layer's complete output from y
+        if ((st = enqueue_projection(plan, l, l == 0 ? x : y, plan->gates, stream)) != BILSTM_OK) return st;
+        if (plan->phase_events) BL_HIP(hipEventRecord(plan->ev_proj[l], stream), "phase event");
+        if ((st = enqueue_recurrence(plan, l, plan->gates, y, base + l * plan->steps, stream)) != BILSTM_OK) {
+            return st;
+        }
+        if (plan->phase_events) BL_HIP(hipEventRecord(plan->ev_recur[l], stream), "phase event");
+    }
+    plan->phases_recorded = plan->phase_events;
+    return BILSTM_OK;
+}
+
+bilstm_status bilstm_project(bilstm_plan *plan, int layer, const float *x, size_t x_len,
+                             float *gates, size_t gates_len, void *stream_ptr) {
+    bilstm_status st = check_plan_buffers("project", plan, x, gates);
+    if (st != BILSTM_OK) return st;
+    if (layer < 0 || layer >= kLayers) return fail(BILSTM_INVALID_ARGUMENT, "project: layer %d out of range", layer);
+    if ((st = check_len("project input", plan->rows * plan->in[layer], x_len)) != BILSTM_OK) return st;
+    if ((st = check_len("project gates", plan->rows * kGateCols, gates_len)) != BILSTM_OK) return st;
+    DeviceScope scope(plan->device);
+    BL_HIP(scope.error(), "project: hipSetDevice");
+    return enqueue_projection(plan, layer, x, gates, static_cast<hipStream_t>(stream_ptr));
+}
+
+bilstm_status bilstm_recur(bilstm_plan *plan, int layer, const float *gates, size_t gates_len,
+                           float *y, size_t y_len, void *stream_ptr) {
+    bilstm_status st = check_plan_buffers("recur", plan, gates, y);
+    if (st != BILSTM_OK) return st;
+    if (layer < 0 || layer >= kLayers) return fail(BILSTM_INVALID_ARGUMENT, "recur: layer %d out of range", layer);
+    if ((st = check_len("recur gates", plan->rows * kGateCols, gates_len)) != BILSTM_OK) return st;
+    if ((st = check_len("recur output", plan->rows * kWidth, y_len)) != BILSTM_OK) return st;
+    auto stream = static_cast<hipStream_t>(stream_ptr);
+    DeviceScope scope(plan->device);
+    BL_HIP(scope.error(), "recur: hipSetDevice");
+    uint32_t base = 0;
+    if ((st = reserve_flags(plan, plan->steps, stream, &base)) != BILSTM_OK) return st;
+    return enqueue_recurrence(plan, layer, gates, y, base, stream);
+}
+
+bilstm_status bilstm_plan_get_info(const bilstm_plan *plan, bilstm_plan_info *info) {
+    if (plan == nullptr || info == nullptr) return fail(BILSTM_INVALID_ARGUMENT, "get_info: NULL argument");
+    *info = plan->info;
+    return BILSTM_OK;
+}
+
+bilstm_status bilstm_check(bilstm_plan *plan) {
+    if (plan == nullptr) return fail(BILSTM_INVALID_ARGUMENT, "check: plan is NULL");
+    DeviceScope scope(plan->device);
+    BL_HIP(scope.error(), "check: hipSetDevice");
+    BL_HIP(hipDeviceSynchronize(), "check");
+    unsigned int flag = 0;
+    BL_HIP(hipMemcpy(&flag, plan->error, sizeof(flag), hipMemcpyDeviceToHost), "check");
+    if (flag != 0) {
+        BL_HIP(hipMemset(plan->error, 0, sizeof(unsigned int)), "check");
+        BL_HIP(hipDeviceSynchronize(), "check");
+        return fail(BILSTM_TIMEOUT, "check: a recurrence wait hit its %.3f ms watchdog; outputs are invalid",
+                    plan->watchdog_ms);
+    }
+    return BILSTM_OK;
+}
+
+bilstm_status bilstm_set_phase_events(bilstm_plan *plan, int enable) {
+    if (plan == nullptr) return fail(BILSTM_INVALID_ARGUMENT, "set_phase_events: plan is NULL");
+    plan->phase_events = enable != 0;
+    return BILSTM_OK;
+}
+
+bilstm_status bilstm_phase_times(bilstm_plan *plan, float *ms, size_t n) {
+    if (plan == nullptr || ms == nullptr) return fail(BILSTM_INVALID_ARGUMENT, "phase_times: NULL argument");
+    if (n < 2 * kLayers) return fail(BILSTM_BUFFER_LENGTH, "phase_times: need %d values, got %zu", 2 * kLayers, n);
+    if (!plan->phases_recorded) {
+        return fail(BILSTM_INVALID_ARGUMENT, "phase_times: no forward ran with phase events enabled");
+    }
+    DeviceScope scope(plan->device);
+    BL_HIP(scope.error(), "phase_times: hipSetDevice");
+    BL_HIP(hipEventSynchronize(plan->ev_recur[kLayers - 1]), "phase_times");
+    for (int l = 0; l < kLayers; ++l) {
+        hipEvent_t before = l == 0 ? plan->ev_start : plan->ev_recur[l - 1];
+        BL_HIP(hipEventElapsedTime(&ms[l], before, plan->ev_proj[l]), "phase_times");
+        BL_HIP(hipEventElapsedTime(&ms[kLayers + l], plan->ev_proj[l], plan->ev_recur[l]), "phase_times");
+    }
+    return BILSTM_OK;
+}
+
+void bilstm_destroy(bilstm_plan *plan) { release(plan); }
+
+bilstm_status bilstm_probe_exchange(int device, int same_xcd, int32_t round_trips, double *one_way_ns,
+                                    int32_t *xcd_a, int32_t *xcd_b) {
+    if (one_way_ns == nullptr || xcd_a == nullptr || xcd_b == nullptr) {
+        return fail(BILSTM_INVALID_ARGUMENT, "probe_exchange: NULL output");
+    }
+    if (round_trips <= 0 || round_trips > 1000000) {
+        return fail(BILSTM_INVALID_ARGUMENT, "probe_exchange: round_trips %d out of range", round_trips);
+    }
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || device < 0 || device >= count) {
+        return fail(BILSTM_INVALID_ARGUMENT, "probe_exchange: no device %d", device);
+    }
+    if (!is_gfx950(device)) return fail(BILSTM_UNSUPPORTED, "probe_exchange: device %d is not gfx950", device);
+    DeviceScope scope(device);
+    BL_HIP(scope.error(), "probe_exchange: hipSetDevice");
+    int wall_khz = 0;
+    BL_HIP(hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, device), "probe_exchange");
+    const double ticks_per_ns = wall_khz / 1.0e6;
+    const auto timeout = static_cast<unsigned long long>(kWatchdogMs * wall_khz);
+    int a = -1, b = -1;
+    hipError_t e = run_exchange_probe(same_xcd, round_trips, timeout, ticks_per_ns, one_way_ns, &a, &b);
+    if (e == hipErrorLaunchTimeOut) return fail(BILSTM_TIMEOUT, "probe_exchange: watchdog fired");
+    BL_HIP(e, "probe_exchange");
+    *xcd_a = a;
+    *xcd_b = b;
+    return BILSTM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,220 @@
+/*
+ * bilstm.h — C ABI of the MI355X (gfx950) four-layer bidirectional LSTM stack.
+ *
+ * The stack is the one of the speakrs 0.6.0 segmentation model (page `lstmproj.rs`,
+ * module doc and `PackedLayer` doc): hidden size H = 128, 4H = 512 gate rows per direction,
+ * input width 60 in the first layer and 256 (forward and reverse hidden states side by
+ * side) in the others, four layers, fp32 throughout. Per layer it runs a time-parallel input
+ * projection x·Wᵀ + (Wb + Rb) for every step of both directions, then a step-serial
+ * recurrence per direction with the recurrent matrix held on chip, the reverse direction
+ * concurrently with the forward one; the next layer waits for both.
+ *
+ * Cell (the pages give the data flow, not the equations; this is the standard LSTM cell
+ * with PyTorch's gate order): a = x_t·Wᵀ + Wb + Rb + R·h_{t-1}, rows in blocks i, f, g, o;
+ * i, f, o = σ(a), g = tanh(a); c_t = f c_{t-1} + i g; h_t = o tanh(c_t); h_0 = c_0 = 0.
+ * Direction 0 runs t = 0..T-1 and writes output columns 0..127; direction 1 runs
+ * t = T-1..0 and writes columns 128..255 (page `lstmproj.rs`, `DirectionLaunch` doc).
+ *
+ * Conventions shared by every entry point
+ *  - No C++ types cross this boundary. Device buffers are plain pointers to device memory
+ *    of the plan's device; host buffers are plain host pointers. Lengths are element counts
+ *    and are checked exactly (page `lstmproj.rs`, `check_len`): a mismatch returns
+ *    BILSTM_BUFFER_LENGTH; a size that does not fit the kernels' 32-bit indices returns
+ *    BILSTM_DIMENSION_OVERFLOW (page `lstmproj.rs`, `to_u32`).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Device work is
+ *    enqueued asynchronously on it; the plan's own side stream is joined back into it
+ *    before the call returns, so the caller's stream order covers all of the plan's work.
+ *  - On failure every call returns a nonzero bilstm_status and records a message for
+ *    bilstm_last_error(). Nothing is enqueued when validation fails.
+ *  - A plan serves one batch size and one sequence length (page `lstmproj.rs`, `Oxide`
+ *    doc). It owns its scratch (gate buffer, exchange words), so two calls on the same
+ *    plan must not run concurrently; calls on different plans may.
+ */
+#ifndef BILSTM_H
+#define BILSTM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BILSTM_HIDDEN 128   /* H */
+#define BILSTM_GATES 512    /* 4H gate rows per direction */
+#define BILSTM_FEATURES 60  /* input width of the first layer */
+#define BILSTM_WIDTH 256    /* 2H: output width of every layer, input width of layers 1..3 */
+#define BILSTM_LAYERS 4
+
+typedef struct bilstm_plan bilstm_plan; /* opaque; created and owned by the library */
+
+typedef enum {
+    BILSTM_OK = 0,
+    BILSTM_INVALID_ARGUMENT = 1,   /* NULL pointer, bad layer index, misaligned buffer ... */
+    BILSTM_BUFFER_LENGTH = 2,      /* a length differs from the one the plan needs */
+    BILSTM_DIMENSION_OVERFLOW = 3, /* a size exceeds the kernels' 32-bit indexing */
+    BILSTM_UNSUPPORTED = 4,        /* not a gfx950 device, or an option this build lacks */
+    BILSTM_HIP_ERROR = 5,          /* a HIP runtime call failed (message has the HIP error) */
+    BILSTM_TIMEOUT = 6             /* a recurrence wait hit its watchdog (see bilstm_check) */
+} bilstm_status;
+
+/*
+ * One layer's weights, HOST pointers, PyTorch nn.LSTM layout (page `lstmproj.rs`,
+ * `with_recurrence`: W is 2·512·in, R is 2·512·128, B is 4·512):
+ *   w [2][512][in]   direction 0 = forward (weight_ih_l{k}), 1 = reverse (weight_ih_l{k}_reverse),
+ *                    rows in blocks of 128: i, f, g, o; in = 60 for layer 0, else 256
+ *   r [2][512][128]  weight_hh
+ *   b [2][2][512]    per direction: Wb (bias_ih) then Rb (bias_hh)
+ * The library copies and repacks them at plan creation; the caller keeps ownership.
+ */
+typedef struct {
+    const float *w;
+    size_t w_len;
+    const float *r;
+    size_t r_len;
+    const float *b;
+    size_t b_len;
+} bilstm_layer;
+
+/*
+ * Plan options (page `lstmproj.rs`, `with_recurrence`: an explicit recurrence plan, so
+ * different kernels can run the same batch). Zero / -1 fields mean "the plan's choice".
+ */
+typedef struct {
+    int32_t recur_groups; /* workgroups per (direction, window tile): 1, 2, 4, 8 or 16; 0 = auto */
+    int32_t recur_tile;   /* windows per tile: 1, 2 or 4; 0 = auto */
+    int32_t concurrent;   /* directions: -1 auto, 0 both on the caller's stream, 1 reverse on
+                             the plan's side stream, 2 both directions in one launch */
+    int32_t watchdog_us;  /* bound of one recurrence wait in microseconds; 0 = 2 s. A wait that
+                             hits it sets the plan's error flag (bilstm_check) and stops waiting */
+    int32_t reserved[4];  /* must be zero */
+} bilstm_options;
+
+/* What a plan chose; filled by bilstm_plan_get_info. */
+typedef struct {
+    uint32_t batch;
+    uint32_t steps;
+    int32_t recur_groups;    /* workgroups per (direction, tile) */
+    int32_t recur_tile;      /* windows per tile */
+    int32_t recur_tiles;     /* number of window tiles */
+    int32_t recur_threads;   /* threads per recurrence workgroup */
+    int32_t recur_launches;  /* launches per direction per layer */
+    int32_t concurrent;      /* 1: reverse direction on the side stream */
+    int32_t proj_tile_m;     /* projection output tile, rows */
+    int32_t proj_tile_n;     /* projection output tile, gate columns */
+    int32_t cu_count;        /* compute units of the device */
+    int32_t recur_capacity;  /* recurrence workgroups the device keeps resident at once */
+    uint64_t device_bytes;   /* device memory the plan owns */
+} bilstm_plan_info;
+
+/*
+ * Create a plan for `batch` windows of `steps` frames on HIP device `device`, packing the
+ * four layers' weights (page `lstmproj.rs`, `with_recurrence`: gate rows interleaved so
+ * each hidden unit's four gates are adjacent, bias folded to Wb + Rb).
+ * Returns BILSTM_UNSUPPORTED on a device other than gfx950. *out receives the plan.
+ * batch and steps must be >= 1; batch·steps·256 must fit 32 bits.
+ */
+bilstm_status bilstm_plan_create(int device, uint32_t batch, uint32_t steps,
+                                 const bilstm_layer layers[BILSTM_LAYERS], bilstm_plan **out);
+
+/* As bilstm_plan_create, with explicit options (NULL = defaults). */
+bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
+                                    const bilstm_layer layers[BILSTM_LAYERS],
+                                    const bilstm_options *options, bilstm_plan **out);
+
+/*
+ * The whole stack (page `lstmproj.rs`, `Oxide::enqueue`).
+ *   x [batch][steps][60]  device, fp32, 16-byte aligned; read only; x_len = batch·steps·60
+ *   y [batch][steps][256] device, fp32, 16-byte aligned; y_len = batch·steps·256
+ * y doubles as the inter-layer buffer: each layer's projection reads the previous layer's
+ * complete output before its recurrence overwrites it (page `lstmproj.rs`, module doc).
+ * x and y must not overlap. Asynchronous on `stream`.
+ */
+bilstm_status bilstm_forward(bilstm_plan *plan, const float *x, size_t x_len, float *y,
+                             size_t y_len, void *stream);
+
+/*
+ * One layer's input projection alone (page `lstmproj.rs`, `InputProjection::enqueue`),
+ * into a caller buffer in the plan's gate layout:
+ *   x     [batch·steps][in]   device; in = 60 for layer 0, else 256
+ *   gates [batch·steps][1024] device; column d·512 + 4j + g holds direction d, hidden unit j,
+ *         gate g (0 i, 1 f, 2 g, 3 o), bias Wb + Rb included.
+ */
+bilstm_status bilstm_project(bilstm_plan *plan, int layer, const float *x, size_t x_len,
+                             float *gates, size_t gates_len, void *stream);
+
+/*
+ * One layer's recurrence alone, both directions (page `lstmproj.rs`, `Oxide::recur`),
+ * from gate pre-activations in the layout bilstm_project writes, into
+ *   y [batch][steps][256] device.
+ */
+bilstm_status bilstm_recur(bilstm_plan *plan, int layer, const float *gates, size_t gates_len,
+                           float *y, size_t y_len, void *stream);
+
+/* Fill *info with the plan's choices. */
+bilstm_status bilstm_plan_get_info(const bilstm_plan *plan, bilstm_plan_info *info);
+
+/*
+ * Wait for the plan's device work to finish and report whether any recurrence wait hit its
+ * watchdog since the last check (BILSTM_TIMEOUT; the outputs of that call are then
+ * garbage). Clears the flag. Blocks the calling thread.
+ */
+bilstm_status bilstm_check(bilstm_plan *plan);
+
+/*
+ * Per-phase timing (page `lstmproj.rs`: the `LstmPhases` hooks around the projection and
+ * the recurrence of each layer). When enabled, bilstm_forward records HIP events on
+ * `stream` around each phase. bilstm_phase_times then waits for the last forward and
+ * writes 8 values in milliseconds: projection of layers 0..3, then recurrence of layers
+ * 0..3 (both directions, including the join). n must be >= 8.
+ */
+bilstm_status bilstm_set_phase_events(bilstm_plan *plan, int enable);
+bilstm_status bilstm_phase_times(bilstm_plan *plan, float *ms, size_t n);
+
+/* Release everything the plan owns. Waits for its work first. NULL is a no-op. */
+void bilstm_destroy(bilstm_plan *plan);
+
+/* Text of the last error recorded on the calling thread ("" if none). */
+const char *bilstm_last_error(void);
+
+/* ---- host-only helpers: no GPU call, usable without a device ---------------------- */
+
+/*
+ * The weight packer alone (page `lstmproj.rs`, `with_recurrence`: pack_input_directions,
+ * pack_directions, pack_bias), host to host:
+ *   w_out    [1024][kpad]      row d·512 + 4j + g = w[d][g·128 + j][0..in), zero padded
+ *                              to kpad = in rounded up to a multiple of 32
+ *   r_out    [2][512][128]     row 4j + g of direction d = r[d][g·128 + j]
+ *   bias_out [1024]            bias_out[d·512 + 4j + g] = Wb[d][g·128+j] + Rb[d][g·128+j] (fp32)
+ * Returns BILSTM_BUFFER_LENGTH if a length is wrong (w_out_len must be 1024·kpad).
+ */
+bilstm_status bilstm_pack_layer(const bilstm_layer *layer, uint32_t in, float *w_out,
+                                size_t w_out_len, float *r_out, size_t r_out_len,
+                                float *bias_out, size_t bias_out_len);
+
+/*
+ * The recurrence schedule for `batch` windows on a device with `cu_count` compute units
+ * whose recurrence kernel keeps `per_cu` workgroups resident per CU (page `lstmproj.rs`,
+ * `RecurrencePlan` and its `Schedule`): fills `info` fields recur_* and concurrent.
+ * `options` may be NULL. Every launch's grid fits the resident capacity when workgroups
+ * of a tile wait for each other (recur_groups > 1).
+ */
+bilstm_status bilstm_schedule(uint32_t batch, uint32_t steps, int32_t cu_count, int32_t per_cu,
+                              const bilstm_options *options, bilstm_plan_info *info);
+
+/* ---- measurement ------------------------------------------------------------------- */
+
+/*
+ * Exchange latency probe: two workgroups pass a flagged 64-bit word back and forth
+ * `round_trips` times through global memory, the same kind of word the recurrence's
+ * hidden-state exchange uses. same_xcd = 1 places both on one XCD, 0 on two XCDs.
+ * Writes the mean one-way latency in nanoseconds and the XCD id each side ran on.
+ */
+bilstm_status bilstm_probe_exchange(int device, int same_xcd, int32_t round_trips,
+                                    double *one_way_ns, int32_t *xcd_a, int32_t *xcd_b);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BILSTM_H */

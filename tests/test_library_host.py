@@ -1,0 +1,167 @@
+"""Host-side tests of the HIP library: it loads, exports every symbol the header declares,
+and its packer, schedule and argument checks behave — all without a GPU."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bilstm.h")
+
+
+@pytest.fixture(scope="module")
+def bl():
+    import bidirectional_lstm_sequence_amd as bl
+    if not os.path.exists(bl.LIB_PATH):
+        from bidirectional_lstm_sequence_amd import _build
+        _build.build()
+    bl.library()
+    return bl
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:bilstm_status|void|const char\s*\*)\s*(bilstm_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ["bilstm_plan_create", "bilstm_forward", "bilstm_destroy", "bilstm_last_error"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(bl):
+    lib = ctypes.CDLL(bl.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in bilstm.h but not exported"
+    assert sorted(bl.EXPORTS) == declared_functions()
+
+
+def test_library_does_not_link_the_oracle(bl):
+    with open(bl.LIB_PATH, "rb") as f:
+        blob = f.read()
+    assert b"oracle_stack_window" not in blob and b"liboracle" not in blob
+
+
+def _interleaved_reference(layer, width):
+    """Packed layout written out from its definition: row d*512 + 4j + g <- source row g*128 + j."""
+    kpad = (width + 31) // 32 * 32
+    w = np.zeros((1024, kpad), np.float32)
+    r = np.zeros((2, 512, 128), np.float32)
+    b = np.zeros(1024, np.float32)
+    for d in range(2):
+        for g in range(4):
+            for j in range(128):
+                w[d * 512 + 4 * j + g, :width] = layer["w"][d, g * 128 + j]
+                r[d, 4 * j + g] = layer["r"][d, g * 128 + j]
+                b[d * 512 + 4 * j + g] = np.float32(layer["b"][d, 0, g * 128 + j]) + np.float32(layer["b"][d, 1, g * 128 + j])
+    return w, r, b
+
+
+@pytest.mark.parametrize("width", [60, 256])
+def test_pack_layer_interleaves_gates_and_folds_bias(bl, width):
+    layer = workloads.make_layers(21)[0 if width == 60 else 1]
+    w, r, b = bl.pack_layer(layer, width)
+    ew, er, eb = _interleaved_reference(layer, width)
+    np.testing.assert_array_equal(w, ew)
+    np.testing.assert_array_equal(r, er)
+    np.testing.assert_array_equal(b, eb)
+    # the padding columns are zero
+    assert not np.any(w[:, width:])
+
+
+def test_pack_layer_rejects_wrong_lengths(bl):
+    layer = workloads.make_layers(22)[0]
+    bad = dict(layer)
+    bad["w"] = layer["w"][:, :, :59].copy()
+    with pytest.raises(bl.BilstmError) as e:
+        bl.pack_layer(bad, 60)
+    assert e.value.name == "BILSTM_BUFFER_LENGTH"
+    assert "expected" in str(e.value)
+
+
+@pytest.mark.parametrize("batch", [1, 7, 8, 32, 100, 256, 1000])
+@pytest.mark.parametrize("groups", [0, 1, 2, 4, 8, 16])
+def test_schedule_fits_resident_capacity(bl, batch, groups):
+    cu, per_cu = 256, 1
+    try:
+        s = bl.schedule(batch, 589, cu, per_cu, groups=groups)
+    except bl.BilstmError as e:
+        assert e.name == "BILSTM_UNSUPPORTED"
+        return
+    cap = cu * per_cu
+    assert s["recur_tiles"] * s["recur_tile"] >= batch
+    assert (s["recur_tiles"] - 1) * s["recur_tile"] < batch
+    per_launch = -(-s["recur_tiles"] // s["recur_launches"])
+    if s["recur_groups"] > 1:
+        # workgroups of a tile wait for each other: every launch must be resident at once
+        assert per_launch * s["recur_groups"] <= cap
+        if s["concurrent"]:
+            assert 2 * s["recur_tiles"] * s["recur_groups"] <= cap
+    assert s["recur_threads"] == (128 // s["recur_groups"]) * {1: 4, 2: 8}.get(s["recur_groups"], 16)
+
+
+def test_schedule_default_prefers_small_tiles(bl):
+    assert bl.schedule(32, 589, 256, 1)["recur_tile"] == 1
+    s = bl.schedule(256, 589, 256, 1)
+    assert s["recur_tile"] == 2 and s["recur_tiles"] == 128
+
+
+def test_schedule_refuses_concurrency_that_cannot_be_resident(bl):
+    with pytest.raises(bl.BilstmError) as e:
+        bl.schedule(256, 589, 256, 1, groups=4, tile=1, concurrent=1)
+    assert e.value.name == "BILSTM_UNSUPPORTED"
+    s = bl.schedule(256, 589, 256, 1, groups=4, tile=1)
+    assert s["concurrent"] == 0 and s["recur_launches"] == 4
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(groups=3), "BILSTM_UNSUPPORTED"), (dict(tile=3), "BILSTM_UNSUPPORTED"),
+    (dict(concurrent=5), "BILSTM_INVALID_ARGUMENT")])
+def test_schedule_rejects_bad_options(bl, kwargs, status):
+    with pytest.raises(bl.BilstmError) as e:
+        bl.schedule(8, 589, 256, 1, **kwargs)
+    assert e.value.name == status
+
+
+def test_plan_create_argument_checks_without_gpu(bl):
+    lib = bl.library()
+    layers = workloads.make_layers(23)
+    keep = []
+    arr = (bl.Layer * 4)(*[bl._layer_struct(l, keep) for l in layers])
+    h = ctypes.c_void_p()
+    assert lib.bilstm_plan_create(0, 0, 589, arr, ctypes.byref(h)) == 1  # batch 0
+    assert "batch" in bl.last_error()
+    assert lib.bilstm_plan_create(0, 1, 589, None, ctypes.byref(h)) == 1
+    # wrong R length on layer 2
+    arr[2].r_len = arr[2].r_len - 1
+    assert lib.bilstm_plan_create(0, 1, 589, arr, ctypes.byref(h)) == 2
+    assert "layer 2 R" in bl.last_error()
+    arr[2].r_len = arr[2].r_len + 1
+    # more rows than 32-bit indexing allows
+    assert lib.bilstm_plan_create(0, 1 << 16, 1 << 10, arr, ctypes.byref(h)) == 3
+    # with valid arguments and no GPU here, the device check answers
+    st = lib.bilstm_plan_create(0, 1, 589, arr, ctypes.byref(h))
+    if not _have_gpu():
+        assert st == 4 and h.value is None
+
+
+def test_entry_points_reject_null_plan(bl):
+    lib = bl.library()
+    assert lib.bilstm_forward(None, None, 0, None, 0, None) == 1
+    assert lib.bilstm_check(None) == 1
+    lib.bilstm_destroy(None)  # NULL-safe
+
+
+def _have_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
