@@ -69,7 +69,21 @@ def main() -> int:
     ap.add_argument("--concurrent", type=int, default=-1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (3 times), to calibrate the HBM "
+                         "byte counters of a profiler run against a known size")
     args = ap.parse_args()
+
+    if args.copy_calibration > 0:
+        import torch
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4}))
+        return 0
 
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the stack shards by windows "

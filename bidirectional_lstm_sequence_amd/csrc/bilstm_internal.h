@@ -24,12 +24,9 @@ constexpr int kProjThreads = 256;
 
 inline int padded_input(int in) { return (in + kProjTileK - 1) / kProjTileK * kProjTileK; }
 
-// Threads per recurrence workgroup for `groups` workgroups per (direction, tile).
-inline int recur_threads(int groups) {
-    const int units = kHidden / groups;
-    const int lanes = groups == 1 ? 4 : (groups == 2 ? 8 : 16);
-    return units * lanes;
-}
+// Threads per recurrence workgroup for `groups` workgroups per (direction, tile): four lanes
+// per hidden unit.
+inline int recur_threads(int groups) { return 4 * (kHidden / groups); }
 
 // Exchange words of one direction: [tiles][2 parities][128 units][tile] u64 words.
 inline size_t exchange_words_per_direction(int tiles, int tile) {

@@ -32,7 +32,7 @@ bilstm_status pack_layer(const bilstm_layer &layer, int in, float *w_out, float 
     return BILSTM_OK;
 }
 
-static bool valid_groups(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+static bool valid_groups(int g) { return g == 1 || g == 2 || g == 4; }
 static bool valid_tile(int t) { return t == 1 || t == 2 || t == 4; }
 
 bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
@@ -49,7 +49,7 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
             if (opt->reserved[i] != 0) return fail(BILSTM_INVALID_ARGUMENT, "options: reserved[%d] must be 0", i);
         }
         if (opt->recur_groups != 0 && !valid_groups(opt->recur_groups)) {
-            return fail(BILSTM_UNSUPPORTED, "options: recur_groups %d is not one of 1, 2, 4, 8, 16",
+            return fail(BILSTM_UNSUPPORTED, "options: recur_groups %d is not one of 1, 2, 4",
                         opt->recur_groups);
         }
         if (opt->recur_tile != 0 && !valid_tile(opt->recur_tile)) {

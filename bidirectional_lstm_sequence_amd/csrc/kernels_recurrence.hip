@@ -8,27 +8,27 @@
 // Work split. A launch covers `tile_count` tiles of BT windows for one direction (or both,
 // gridDim.y = 2). Each tile is served by KG workgroups; workgroup `member` owns hidden
 // units [member·U, (member+1)·U), U = 128/KG, i.e. the 4U packed gate rows 4j+g of R, held
-// in VGPRs for the whole launch. Inside a workgroup, Q lanes (adjacent in the wave) share a
-// unit: lane q holds the unit's four gate rows over K chunks [q·16/Q, (q+1)·16/Q) of the
-// 16 eight-element chunks of h.
+// in VGPRs for the whole launch. Four adjacent lanes (a quad) share a unit: lane q holds the
+// unit's four gate rows over the K quarter [32q, 32q+32) — 128 values. Its register slot s
+// holds gate q XOR s, which turns the quad reduction into a reduce-scatter with no selects.
 //
 // One step s (t = s forward, T-1-s reverse):
-//  1. every lane: 4·BT dot products of its rows with its h chunks (h_{t-1} from LDS);
-//  2. the canonical sum: each chunk summed in k order from 0, chunks combined by a fixed
-//     balanced binary tree — in-lane for the lower levels, DPP butterflies across the Q
-//     lanes for the upper ones. The tree is the same for every KG, so every workgroup
-//     split gives bitwise identical results;
-//  3. lane q < BT (window q of the tile): a = gate input + sum; i, f, o = σ, g = tanh;
-//     c = f·c + i·g; h = o·tanh(c); h goes to LDS, to the output and, when KG > 1, to the
-//     exchange as one 64-bit word {flag, h};
+//  1. every lane: 4·BT dot products of its rows with its quarter of h_{t-1} (from LDS), each
+//     summed in k order from the first product;
+//  2. quad reduce-scatter with DPP: lane q ends with gate q's full sum, always combined as
+//     ((p0 + p1) + (p2 + p3)) over the quarters — one fixed order for every split;
+//  3. lane q: a = gate input + sum; the activation of gate q (σ for i, f, o; tanh for g,
+//     as 2σ(2a) - 1); the lane of window b collects the four activations, updates
+//     c = f·c + i·g and h = o·tanh(c), and writes h to LDS, to the output and, when KG > 1,
+//     to the exchange as one 64-bit word {flag, h};
 //  4. KG > 1: the other workgroups' h words of step s are polled until their flag is
 //     flag_base + s + 1 and copied into LDS (step-parity double buffer);
 //  5. one workgroup barrier.
 //
-// Gate inputs are prefetched several steps ahead. With KG = 1 every window lane keeps a
-// register ring. With KG > 1, waves that poll must not hold outstanding prefetches (the
-// poll's wait would drain them), so wave 0 prefetches the workgroup's gates into an LDS
-// ring and does not poll; waves 1.. poll.
+// Gate inputs are prefetched several steps ahead. With KG = 1 every lane keeps a register
+// ring. With KG > 1, waves that poll must not hold outstanding prefetches (the poll's wait
+// would drain them), so wave 0 prefetches the workgroup's gates into an LDS ring and does not
+// poll; waves 1.. poll.
 //
 // Waits are bounded: a poll that sees no progress for `timeout_ticks` wall-clock ticks
 // sets the error word and stops waiting, so the grid always drains.
@@ -41,14 +41,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kRing = 4;  // prefetch depth in steps
 
-template <int KG>
-struct Split {
-    static constexpr int U = kHidden / KG;                         // units per workgroup
-    static constexpr int Q = KG == 1 ? 4 : (KG == 2 ? 8 : 16);     // lanes per unit
-    static constexpr int NT = U * Q;                               // threads
-    static constexpr int NCH = 16 / Q;                             // K chunks per lane
-};
-
 // Padded h index: 4 floats of padding after every 32, so the four K quarters of h start on
 // different LDS banks.
 __device__ __forceinline__ int hpad(int k) { return k + (k >> 5) * 4; }
@@ -58,17 +50,14 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
+constexpr int kXor1 = 0xB1;       // quad_perm 1,0,3,2
+constexpr int kXor2 = 0x4E;       // quad_perm 2,3,0,1
+template <int L>
+constexpr int kBcast = L * 0x55;  // quad_perm L,L,L,L: every lane reads quad lane L
 
 // e^{-a} for a >= 0, on the hardware exp2.
 __device__ __forceinline__ float exp_neg(float a) {
     return __builtin_amdgcn_exp2f(a * -1.4426950408889634f);
-}
-
-// σ(z) = 1/(1+e^{-z}), evaluated through e^{-|z|} so it never overflows.
-__device__ __forceinline__ float sigmoid_f(float z) {
-    const float e = exp_neg(fabsf(z));
-    const float r = __builtin_amdgcn_rcpf(1.0f + e);
-    return z >= 0.0f ? r : e * r;
 }
 
 // tanh(z) = sign(z)·(1 - e^{-2|z|})/(1 + e^{-2|z|}).
@@ -76,6 +65,16 @@ __device__ __forceinline__ float tanh_f(float z) {
     const float e = exp_neg(2.0f * fabsf(z));
     const float t = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
     return copysignf(t, z);
+}
+
+// Activation of gate q on lane q: σ(a) for q = 0, 1, 3; tanh(a) = 2σ(2a) - 1 for q = 2.
+// σ(z) is evaluated through e^{-|z|}, so it never overflows.
+__device__ __forceinline__ float gate_act(float a, bool is_g) {
+    const float z = is_g ? 2.0f * a : a;
+    const float e = exp_neg(fabsf(z));
+    const float r = __builtin_amdgcn_rcpf(1.0f + e);
+    const float sg = z >= 0.0f ? r : e * r;
+    return is_g ? fmaf(2.0f, sg, -1.0f) : sg;
 }
 
 template <int BT>
@@ -95,9 +94,10 @@ __device__ __forceinline__ void store_word(unsigned long long *p, unsigned long 
 }
 
 template <int KG, int BT>
-__global__ __launch_bounds__(Split<KG>::NT) void recurrence_kernel(RecurArgs a) {
-    using S = Split<KG>;
-    constexpr int U = S::U, Q = S::Q, NT = S::NT, NCH = S::NCH;
+__global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArgs a) {
+    constexpr int U = kHidden / KG;  // units per workgroup
+    constexpr int NT = 4 * U;        // threads
+    static_assert(KG == 1 || NT >= 128, "a polling wave besides the staging wave");
 
     // ---- which tile, member and direction ------------------------------------------------
     int tile, member;
@@ -116,65 +116,66 @@ __global__ __launch_bounds__(Split<KG>::NT) void recurrence_kernel(RecurArgs a) 
     const int steps = a.steps;
 
     const int tid = threadIdx.x;
-    const int u = tid / Q;
-    const int q = tid % Q;
-    const int ug = member * U + u;  // global hidden unit of this lane
+    const int u = tid >> 2;
+    const int q = tid & 3;
+    const int ug = member * U + u;  // global hidden unit of this quad
 
     __shared__ __attribute__((aligned(16))) float hs[2][kHPad * BT];
     __shared__ __attribute__((aligned(16))) float gs[KG > 1 ? 2 : 1][KG > 1 ? U * 4 * BT : 4];
 
-    // ---- recurrent weights into VGPRs ------------------------------------------------------
-    float rr[4][NCH][8];
+    // ---- recurrent weights into VGPRs: slot s = gate q^s, K quarter q ----------------------
+    float rr[4][32];
     {
         const float *rdir = a.r + static_cast<size_t>(dir) * kGates * kHidden;
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int s = 0; s < 4; ++s) {
+            const v4f *p = reinterpret_cast<const v4f *>(
+                rdir + static_cast<size_t>(4 * ug + (q ^ s)) * kHidden + 32 * q);
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int chunk = q * NCH + c;
-                const v4f *p = reinterpret_cast<const v4f *>(
-                    rdir + static_cast<size_t>(4 * ug + g) * kHidden + chunk * 8);
-                const v4f lo = p[0], hi = p[1];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    rr[g][c][e] = lo[e];
-                    rr[g][c][4 + e] = hi[e];
-                }
+            for (int v = 0; v < 8; ++v) {
+                const v4f x = p[v];
+                rr[s][4 * v + 0] = x[0];
+                rr[s][4 * v + 1] = x[1];
+                rr[s][4 * v + 2] = x[2];
+                rr[s][4 * v + 3] = x[3];
             }
+        }
     }
 
     // h_{-1} = 0
     for (int i = tid; i < 2 * kHPad * BT; i += NT) (&hs[0][0])[i] = 0.0f;
 
     const bool window_lane = q < BT;
-    const int win = tile * BT + (window_lane ? q : 0);
-    const bool valid = window_lane && win < a.batch;
-    const size_t gate_col = static_cast<size_t>(dir) * kGates;
+    const int win0 = tile * BT;
+    const size_t gate_col = static_cast<size_t>(dir) * kGates + 4 * ug + q;
     auto time_of = [&](int s) { return dir == 0 ? s : steps - 1 - s; };
+    // this lane's gate input (gate q of unit ug) for window b of the tile at step s
+    auto gate_in = [&](int b, int s) -> float {
+        const int w = win0 + b;
+        if (w >= a.batch || s >= steps) return 0.0f;
+        return a.gates[(static_cast<size_t>(w) * steps + time_of(s)) * kGateCols + gate_col];
+    };
 
-    // KG == 1: per-lane register ring of this lane's float4 of gates.
-    v4f ring[kRing];
+    // KG == 1: per-lane register ring of gate inputs.
+    float ring[kRing][BT];
     // KG > 1: wave 0 stages the workgroup's gates; lane j of wave 0 moves float4 j, j + 64 ...
+    // (float4 j = window j / U, unit member·U + j % U)
     constexpr int kStageVec = KG > 1 ? (U * BT + 63) / 64 : 1;
     v4f stage[kRing][kStageVec];
     const bool stager = (KG > 1) && (tid < 64);
-
-    auto gate_ptr = [&](int w, int s) {
-        return a.gates + (static_cast<size_t>(w) * steps + time_of(s)) * kGateCols + gate_col;
-    };
-    // float4 j of the workgroup's per-step gates: window j / U, unit member·U + j % U
     auto stage_load = [&](int j, int s) -> v4f {
-        const int bw = tile * BT + j / U;
-        if (j >= U * BT || bw >= a.batch || s >= steps) return v4f{0.f, 0.f, 0.f, 0.f};
-        return *reinterpret_cast<const v4f *>(gate_ptr(bw, s) + 4 * (member * U + j % U));
+        const int w = win0 + j / U;
+        if (j >= U * BT || w >= a.batch || s >= steps) return v4f{0.f, 0.f, 0.f, 0.f};
+        return *reinterpret_cast<const v4f *>(
+            a.gates + (static_cast<size_t>(w) * steps + time_of(s)) * kGateCols +
+            static_cast<size_t>(dir) * kGates + 4 * (member * U + j % U));
     };
 
     if constexpr (KG == 1) {
 #pragma unroll
-        for (int p = 0; p < kRing; ++p) {
-            ring[p] = v4f{0.f, 0.f, 0.f, 0.f};
-            if (valid && p < steps) ring[p] = *reinterpret_cast<const v4f *>(gate_ptr(win, p) + 4 * ug);
-        }
+        for (int p = 0; p < kRing; ++p)
+#pragma unroll
+            for (int b = 0; b < BT; ++b) ring[p][b] = gate_in(b, p);
     } else {
         if (stager) {
             // step 0 straight into LDS slot 0; steps 1..kRing into the register ring
@@ -195,6 +196,7 @@ __global__ __launch_bounds__(Split<KG>::NT) void recurrence_kernel(RecurArgs a) 
     if constexpr (KG > 1) {
         xdir = a.exchange + (static_cast<size_t>(dir) * a.tiles + tile) * 2 * kHidden * BT;
     }
+    const bool is_g = q == 2;
     float cst = 0.0f;  // cell state of (unit ug, window q) on window lanes
     bool timed_out = false;
 
@@ -206,73 +208,62 @@ __global__ __launch_bounds__(Split<KG>::NT) void recurrence_kernel(RecurArgs a) 
                 const int cur = s & 1;
                 const int nxt = cur ^ 1;
 
-                // (1) partial dot products over this lane's chunks
-                float acc[4][NCH][BT];
+                // (1) partial dot products over this lane's K quarter
+                float acc[4][BT];
+                {
+                    const float *hp = &hs[cur][36 * q * BT];
 #pragma unroll
-                for (int c = 0; c < NCH; ++c) {
-                    const int chunk = q * NCH + c;
-                    const float *hp = &hs[cur][hpad(chunk * 8) * BT];
-                    float hv[8 * BT];
+                    for (int v = 0; v < 8 * BT; ++v) {
+                        const v4f h4 = *reinterpret_cast<const v4f *>(hp + 4 * v);
 #pragma unroll
-                    for (int v = 0; v < 2 * BT; ++v) {
-                        const v4f t4 = *reinterpret_cast<const v4f *>(hp + 4 * v);
-                        hv[4 * v + 0] = t4[0];
-                        hv[4 * v + 1] = t4[1];
-                        hv[4 * v + 2] = t4[2];
-                        hv[4 * v + 3] = t4[3];
-                    }
+                        for (int e = 0; e < 4; ++e) {
+                            const int idx = 4 * v + e;  // = k_local·BT + b
+                            const int kk = idx / BT;
+                            const int b = idx % BT;
 #pragma unroll
-                    for (int g = 0; g < 4; ++g)
-#pragma unroll
-                        for (int b = 0; b < BT; ++b) {
-                            float sacc = rr[g][c][0] * hv[b];
-#pragma unroll
-                            for (int e = 1; e < 8; ++e) sacc = fmaf(rr[g][c][e], hv[e * BT + b], sacc);
-                            acc[g][c][b] = sacc;
+                            for (int sl = 0; sl < 4; ++sl) {
+                                acc[sl][b] = kk == 0 ? rr[sl][0] * h4[e] : fmaf(rr[sl][kk], h4[e], acc[sl][b]);
+                            }
                         }
+                    }
                 }
 
-                // (2) canonical tree: in-lane levels, then DPP butterflies over the Q lanes
-                float sum[4][BT];
+                // (2) reduce-scatter: lane q keeps gate q, sum ((p0+p1)+(p2+p3))
+                float sum[BT];
 #pragma unroll
-                for (int g = 0; g < 4; ++g)
-#pragma unroll
-                    for (int b = 0; b < BT; ++b) {
-                        float v;
-                        if constexpr (NCH == 4) {
-                            v = (acc[g][0][b] + acc[g][1][b]) + (acc[g][2][b] + acc[g][3][b]);
-                        } else if constexpr (NCH == 2) {
-                            v = acc[g][0][b] + acc[g][1][b];
-                        } else {
-                            v = acc[g][0][b];
-                        }
-                        if constexpr (Q >= 2) v = v + dpp<0xB1>(v);   // quad_perm 1,0,3,2
-                        if constexpr (Q >= 4) v = v + dpp<0x4E>(v);   // quad_perm 2,3,0,1
-                        if constexpr (Q >= 8) v = v + dpp<0x141>(v);  // row_half_mirror
-                        if constexpr (Q >= 16) v = v + dpp<0x140>(v); // row_mirror
-                        sum[g][b] = v;
-                    }
+                for (int b = 0; b < BT; ++b) {
+                    const float t0 = acc[0][b] + dpp<kXor1>(acc[1][b]);  // gates q, via quads {q, q^1}
+                    const float t2 = acc[2][b] + dpp<kXor1>(acc[3][b]);  // gate q^2
+                    sum[b] = t0 + dpp<kXor2>(t2);
+                }
 
-                // (3) the cell update on window lanes
+                // (3) activations of gate q for each window, then the cell update on window lanes
+                float act[BT];
+                if constexpr (KG == 1) {
+#pragma unroll
+                    for (int b = 0; b < BT; ++b) act[b] = gate_act(ring[p][b] + sum[b], is_g);
+                } else {
+#pragma unroll
+                    for (int b = 0; b < BT; ++b) act[b] = gate_act(gs[cur][4 * (b * U + u) + q] + sum[b], is_g);
+                }
+                float fg[BT], gg[BT], og[BT];
+#pragma unroll
+                for (int b = 0; b < BT; ++b) {
+                    fg[b] = dpp<kBcast<1>>(act[b]);
+                    gg[b] = dpp<kBcast<2>>(act[b]);
+                    og[b] = dpp<kBcast<3>>(act[b]);
+                }
+                // window lane q (< BT) takes window q: its i is lane 0's activation of window q
+                float ig[BT];
+#pragma unroll
+                for (int b = 0; b < BT; ++b) ig[b] = dpp<kBcast<0>>(act[b]);
+                const float i_w = pick<BT>(ig, q), f_w = pick<BT>(fg, q);
+                const float g_w = pick<BT>(gg, q), o_w = pick<BT>(og, q);
+                cst = fmaf(f_w, cst, i_w * g_w);
+                const float hval = o_w * tanh_f(cst);
+
                 const unsigned int flag = a.flag_base + static_cast<unsigned int>(s) + 1u;
-                float hval = 0.0f;
                 if (window_lane) {
-                    v4f gi;
-                    if constexpr (KG == 1) {
-                        gi = ring[p];
-                    } else {
-                        gi = *reinterpret_cast<const v4f *>(&gs[cur][4 * (q * U + u)]);
-                    }
-                    const float ai = gi[0] + pick<BT>(sum[0], q);
-                    const float af = gi[1] + pick<BT>(sum[1], q);
-                    const float ag = gi[2] + pick<BT>(sum[2], q);
-                    const float ao = gi[3] + pick<BT>(sum[3], q);
-                    const float ig = sigmoid_f(ai);
-                    const float fg = sigmoid_f(af);
-                    const float gg = tanh_f(ag);
-                    const float og = sigmoid_f(ao);
-                    cst = fmaf(fg, cst, ig * gg);
-                    hval = og * tanh_f(cst);
                     hs[nxt][hpad(ug) * BT + q] = hval;
                     if constexpr (KG > 1) {
                         const unsigned long long word =
@@ -283,9 +274,8 @@ __global__ __launch_bounds__(Split<KG>::NT) void recurrence_kernel(RecurArgs a) 
 
                 if constexpr (KG == 1) {
                     // refill this ring slot with step s + kRing
-                    if (valid && s + kRing < steps) {
-                        ring[p] = *reinterpret_cast<const v4f *>(gate_ptr(win, s + kRing) + 4 * ug);
-                    }
+#pragma unroll
+                    for (int b = 0; b < BT; ++b) ring[p][b] = gate_in(b, s + kRing);
                 } else {
                     if (stager) {
                         // stage[p] holds step s+1 (loaded kRing steps ago): into LDS slot nxt,
@@ -323,8 +313,8 @@ __global__ __launch_bounds__(Split<KG>::NT) void recurrence_kernel(RecurArgs a) 
                     }
                 }
 
-                if (valid) {
-                    a.y[(static_cast<size_t>(win) * steps + time_of(s)) * kWidth + dir * kHidden + ug] = hval;
+                if (window_lane && win0 + q < a.batch) {
+                    a.y[(static_cast<size_t>(win0 + q) * steps + time_of(s)) * kWidth + dir * kHidden + ug] = hval;
                 }
                 __syncthreads();
             }
@@ -353,18 +343,21 @@ __global__ void exchange_probe_kernel(unsigned long long *words, int partner, in
     unsigned long long t_start = 0, t_end = 0;
     bool ok = true;
     for (int r = 1; r <= rounds && ok; ++r) {
+        const unsigned long long word = static_cast<unsigned long long>(r) << 32;
         if (is_a) {
             if (r == 1) t_start = wall_clock64();
-            store_word(mine, static_cast<unsigned long long>(r) << 32);
+            store_word(mine, word);
         }
         const unsigned long long t0 = wall_clock64();
-        while (static_cast<unsigned int>(load_word(theirs) >> 32) != static_cast<unsigned int>(r)) {
+        while (true) {
+            const unsigned long long v = load_word(theirs);
+            if (static_cast<unsigned int>(v >> 32) == static_cast<unsigned int>(r)) break;
             if (wall_clock64() - t0 > timeout_ticks) {
                 ok = false;
                 break;
             }
         }
-        if (!is_a) store_word(mine, static_cast<unsigned long long>(r) << 32);
+        if (!is_a) store_word(mine, word);
     }
     t_end = wall_clock64();
     if (is_a) {
@@ -379,20 +372,18 @@ __global__ void exchange_probe_kernel(unsigned long long *words, int partner, in
 
 template <int KG, int BT>
 hipError_t launch_typed(const RecurArgs &args, int directions, hipStream_t stream) {
-    using S = Split<KG>;
     const int nwg = KG == 1 ? args.tile_count : (args.tile_count + 7) / 8 * 8 * KG;
-    hipLaunchKernelGGL((recurrence_kernel<KG, BT>), dim3(nwg, directions), dim3(S::NT), 0, stream, args);
+    hipLaunchKernelGGL((recurrence_kernel<KG, BT>), dim3(nwg, directions), dim3(recur_threads(KG)), 0,
+                       stream, args);
     return hipGetLastError();
 }
 
 template <int KG, int BT>
 hipError_t occupancy_typed(int *per_cu) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, recurrence_kernel<KG, BT>, Split<KG>::NT, 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, recurrence_kernel<KG, BT>, recur_threads(KG), 0);
 }
 
-#define BL_FOR_EACH_SPLIT(X) \
-    X(1, 1) X(1, 2) X(1, 4) X(2, 1) X(2, 2) X(2, 4) X(4, 1) X(4, 2) X(4, 4) X(8, 1) X(8, 2) X(8, 4) \
-    X(16, 1) X(16, 2) X(16, 4)
+#define BL_FOR_EACH_SPLIT(X) X(1, 1) X(1, 2) X(1, 4) X(2, 1) X(2, 2) X(2, 4) X(4, 1) X(4, 2) X(4, 4)
 
 }  // namespace
 

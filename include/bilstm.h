@@ -81,7 +81,7 @@ typedef struct {
  * different kernels can run the same batch). Zero / -1 fields mean "the plan's choice".
  */
 typedef struct {
-    int32_t recur_groups; /* workgroups per (direction, window tile): 1, 2, 4, 8 or 16; 0 = auto */
+    int32_t recur_groups; /* workgroups per (direction, window tile): 1, 2 or 4; 0 = auto */
     int32_t recur_tile;   /* windows per tile: 1, 2 or 4; 0 = auto */
     int32_t concurrent;   /* directions: -1 auto, 0 both on the caller's stream, 1 reverse on
                              the plan's side stream, 2 both directions in one launch */
@@ -208,6 +208,8 @@ bilstm_status bilstm_schedule(uint32_t batch, uint32_t steps, int32_t cu_count, 
  * Exchange latency probe: two workgroups pass a flagged 64-bit word back and forth
  * `round_trips` times through global memory, the same kind of word the recurrence's
  * hidden-state exchange uses. same_xcd = 1 places both on one XCD, 0 on two XCDs.
+ * Both sides use agent-scope relaxed 64-bit atomics, as the recurrence does: on gfx950 these
+ * are the accesses that make one CU's store visible to another CU's load.
  * Writes the mean one-way latency in nanoseconds and the XCD id each side ran on.
  */
 bilstm_status bilstm_probe_exchange(int device, int same_xcd, int32_t round_trips,

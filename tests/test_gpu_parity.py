@@ -86,7 +86,7 @@ def test_projection_matches_oracle(bl, orc, layer_index, rows):
     plan.close()
 
 
-SPLITS = [(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (4, 1), (4, 4), (8, 1), (8, 2), (16, 1), (16, 4)]
+SPLITS = [(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (2, 4), (4, 1), (4, 2), (4, 4)]
 
 
 @pytest.mark.parametrize("groups,tile", SPLITS)

@@ -104,7 +104,7 @@ def test_schedule_fits_resident_capacity(bl, batch, groups):
         assert per_launch * s["recur_groups"] <= cap
         if s["concurrent"]:
             assert 2 * s["recur_tiles"] * s["recur_groups"] <= cap
-    assert s["recur_threads"] == (128 // s["recur_groups"]) * {1: 4, 2: 8}.get(s["recur_groups"], 16)
+    assert s["recur_threads"] == 4 * (128 // s["recur_groups"])
 
 
 def test_schedule_default_prefers_small_tiles(bl):
