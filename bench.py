@@ -11,6 +11,7 @@ the projection's fraction of FP32-MFMA peak, and the oracle timed on the host's 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -41,6 +42,32 @@ def projection_flops(frames: int) -> float:
 def recurrence_flops_per_layer(frames: int) -> float:
     """Algorithmic FLOPs of one layer's recurrence, both directions: 2·65,536 per frame and direction."""
     return 2.0 * 2 * frames * RECUR_FMA_PER_FRAME_DIR
+
+
+def kernel_source_digest() -> str:
+    """Digest of the recurrence kernel's sources, to tell whether recorded counters still apply."""
+    h = hashlib.sha256()
+    for name in ("kernels_recurrence.hip", "bilstm_internal.h"):
+        with open(os.path.join(ROOT, "bidirectional_lstm_sequence_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str, info: dict):
+    """HBM bytes per recurrence launch from the rocprofv3 counters recorded in profiles/, if they
+    were taken on this kernel source, workload and launch configuration; else None."""
+    path = os.path.join(ROOT, "profiles", "recurrence_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if (rec.get("source_sha256") != kernel_source_digest() or rec.get("workload") != workload
+            or rec.get("concurrent") != info["concurrent"] or rec.get("groups") != info["recur_groups"]
+            or rec.get("tile") != info["recur_tile"]):
+        return None
+    return {"bytes_per_launch": rec["fetch_bytes"] + rec["write_bytes"], "fetch_bytes": rec["fetch_bytes"],
+            "write_bytes": rec["write_bytes"], "source": "profiles/recurrence_traffic.json"}
 
 
 def cpu_baseline(x, layers, steps, max_threads=16, target_windows=None):
@@ -109,12 +136,15 @@ def main() -> int:
     plan.check()
 
     # timed region: exactly K forwards, bracketed by synchronisation; per-step HIP events on
-    # the caller's stream (the plan joins its side stream back into it)
+    # the caller's stream (the plan joins any side stream back into it). The last step runs
+    # with the plan's phase events on, which time each phase and the recurrence launch.
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev[0].record(stream)
     for k in range(args.steps):
+        if k == args.steps - 1:
+            plan.set_phase_events(True)
         plan.forward(xd, yd)
         ev[k + 1].record(stream)
     torch.cuda.synchronize()
@@ -123,28 +153,33 @@ def main() -> int:
     step_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
     total_ms = ev[0].elapsed_time(ev[args.steps])
     value = frames * args.steps / (total_ms / 1e3)
+    timed_phases = plan.phase_times()
 
-    # per-phase split, outside the timed region
-    plan.set_phase_events(True)
-    proj_ms = [[] for _ in range(4)]
-    rec_ms = [[] for _ in range(4)]
-    for _ in range(max(3, min(10, args.steps))):
+    # more phase samples after the timed region (medians)
+    proj_ms = [[v] for v in timed_phases["projection_ms"]]
+    rec_ms = [[v] for v in timed_phases["recurrence_ms"]]
+    launch_ms = [[v] for v in timed_phases["recurrence_launch_ms"]]
+    for _ in range(max(2, min(9, args.steps))):
         plan.forward(xd, yd)
         pt = plan.phase_times()
         for l in range(4):
             proj_ms[l].append(pt["projection_ms"][l])
             rec_ms[l].append(pt["recurrence_ms"][l])
+            launch_ms[l].append(pt["recurrence_launch_ms"][l])
     plan.set_phase_events(False)
     proj_med = [statistics.median(v) for v in proj_ms]
     rec_med = [statistics.median(v) for v in rec_ms]
     plan.check()
     plan.close()
 
-    # recurrence: the dominant kernel (both directions of a layer run concurrently, so one
-    # layer's recurrence phase is the duration of its two concurrent launches)
+    # recurrence: the dominant kernel. Its achieved rate is the algorithmic FLOPs of one launch
+    # over that launch's duration in the timed region (events on the caller's stream).
+    launch_dirs = 2 if info["concurrent"] == 2 else 1
+    launch_dur_ms = statistics.mean(timed_phases["recurrence_launch_ms"])
+    rec_tflops = launch_dirs * recurrence_flops_per_layer(frames) / 2 / (launch_dur_ms / 1e3) / 1e12
     rec_layer_ms = statistics.mean(rec_med)
-    rec_tflops = recurrence_flops_per_layer(frames) / (rec_layer_ms / 1e3) / 1e12
     us_per_step = rec_layer_ms * 1e3 / wl.steps
+    traffic = recorded_traffic(wl.name, info)
     groups, tile = info["recur_groups"], info["recur_tile"]
     fma_clk = RECUR_FMA_PER_FRAME_DIR * tile / groups / FMA_PER_CLK_PER_CU
     xchg_ns = None
@@ -176,9 +211,13 @@ def main() -> int:
                                f"H=128, input 60", "batch": wl.batch, "seq_len": wl.steps,
                    "recurrence_split": {"groups": groups, "tile": tile, "tiles": info["recur_tiles"],
                                         "concurrent": info["concurrent"]}},
-        "roofline": {"kernel": "recurrence (one layer, both directions concurrent)", "bound": "alu",
-                     "achieved": rec_tflops, "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
-                     "frac": rec_tflops / PEAK_FP32_VECTOR_TFLOPS, "traffic": None},
+        "roofline": {"kernel": f"recurrence_kernel<{groups}, {tile}> ({launch_dirs} direction(s) per launch)",
+                     "bound": "alu", "achieved": rec_tflops, "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
+                     "frac": rec_tflops / PEAK_FP32_VECTOR_TFLOPS,
+                     "traffic": traffic["bytes_per_launch"] if traffic else None,
+                     "launch_ms": launch_dur_ms,
+                     "flop_per_launch": launch_dirs * recurrence_flops_per_layer(frames) / 2,
+                     "traffic_detail": traffic},
         "recurrence_step": {"us_per_step": us_per_step, "bound_us": bound_us,
                             "frac_of_bound": bound_us / us_per_step, "exchange_one_way_ns": xchg_ns,
                             "bound_terms": f"FMA {fma_clk:.0f} clk at {FMA_PER_CLK_PER_CU} FMA/clk/CU, "

@@ -273,9 +273,11 @@ class Plan:
         _check(self._lib.bilstm_set_phase_events(self._h, 1 if enable else 0))
 
     def phase_times(self) -> dict:
-        ms = (ctypes.c_float * 8)()
-        _check(self._lib.bilstm_phase_times(self._h, ms, 8))
-        return {"projection_ms": [ms[i] for i in range(4)], "recurrence_ms": [ms[4 + i] for i in range(4)]}
+        """Per-phase milliseconds of the last forward run with phase events on."""
+        ms = (ctypes.c_float * 12)()
+        _check(self._lib.bilstm_phase_times(self._h, ms, 12))
+        return {"projection_ms": [ms[i] for i in range(4)], "recurrence_ms": [ms[4 + i] for i in range(4)],
+                "recurrence_launch_ms": [ms[8 + i] for i in range(4)]}
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:

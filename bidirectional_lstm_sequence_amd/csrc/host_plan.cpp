@@ -64,6 +64,8 @@ struct bilstm_plan {
     hipEvent_t ev_start = nullptr;
     hipEvent_t ev_proj[kLayers] = {nullptr, nullptr, nullptr, nullptr};
     hipEvent_t ev_recur[kLayers] = {nullptr, nullptr, nullptr, nullptr};
+    hipEvent_t ev_launch0[kLayers] = {nullptr, nullptr, nullptr, nullptr};
+    hipEvent_t ev_launch1[kLayers] = {nullptr, nullptr, nullptr, nullptr};
     bool phases_recorded = false;
     uint32_t epoch = 0;  // flags of the next pass start above this value
     unsigned long long timeout_ticks = 0;
@@ -126,6 +128,8 @@ void release(bilstm_plan *p) {
         if (p->join[l]) (void)hipEventDestroy(p->join[l]);
         if (p->ev_proj[l]) (void)hipEventDestroy(p->ev_proj[l]);
         if (p->ev_recur[l]) (void)hipEventDestroy(p->ev_recur[l]);
+        if (p->ev_launch0[l]) (void)hipEventDestroy(p->ev_launch0[l]);
+        if (p->ev_launch1[l]) (void)hipEventDestroy(p->ev_launch1[l]);
     }
     if (p->ev_start) (void)hipEventDestroy(p->ev_start);
     if (p->gates) (void)hipFree(p->gates);
@@ -188,7 +192,7 @@ bilstm_status enqueue_projection(bilstm_plan *p, int layer, const float *x, floa
 // `Oxide::recur`: the reverse direction on the side stream when the schedule allows it,
 // joined back before the next layer).
 bilstm_status enqueue_recurrence(bilstm_plan *p, int layer, const float *gates, float *y,
-                                 uint32_t flag_base, hipStream_t stream) {
+                                 uint32_t flag_base, hipStream_t stream, bool layer_events) {
     const bilstm_plan_info &s = p->info;
     RecurArgs base{};
     base.gates = gates;
@@ -203,13 +207,19 @@ bilstm_status enqueue_recurrence(bilstm_plan *p, int layer, const float *gates, 
     base.timeout_ticks = p->timeout_ticks;
 
     const int per_launch = (s.recur_tiles + s.recur_launches - 1) / s.recur_launches;
+    // With phase events on, the first launch on the caller's stream is bracketed by its own
+    // event pair, so its duration can be read separately from the phase.
+    const bool mark = p->phase_events && layer_events;
     auto launch_direction = [&](int direction, int directions, hipStream_t on) -> bilstm_status {
         for (int first = 0; first < s.recur_tiles; first += per_launch) {
             RecurArgs a = base;
             a.direction = direction;
             a.tile_first = first;
             a.tile_count = std::min(per_launch, s.recur_tiles - first);
+            const bool bracket = mark && on == stream && direction == 0 && first == 0;
+            if (bracket) BL_HIP(hipEventRecord(p->ev_launch0[layer], stream), "phase event");
             BL_HIP(launch_recurrence(s.recur_groups, s.recur_tile, a, directions, on), "recurrence launch");
+            if (bracket) BL_HIP(hipEventRecord(p->ev_launch1[layer], stream), "phase event");
         }
         return BILSTM_OK;
     };
@@ -311,8 +321,8 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
     if (e != hipSuccess || cu_count <= 0 || wall_khz <= 0) {
         return fail_release(fail(BILSTM_HIP_ERROR, "plan_create: device attributes: %s", hipGetErrorString(e)));
     }
-    const double watchdog_ms = (options != nullptr && options->watchdog_us > 0) ? options->watchdog_us / 1000.0
-                                                                                : kWatchdogMs;
+    const int32_t wd_us = options != nullptr ? options->watchdog_us : 0;
+    const double watchdog_ms = wd_us > 0 ? wd_us / 1000.0 : (wd_us < 0 ? 0.0 : kWatchdogMs);
     p->timeout_ticks = static_cast<unsigned long long>(watchdog_ms * wall_khz);
     p->watchdog_ms = watchdog_ms;
 
@@ -373,6 +383,8 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
         if (e == hipSuccess) e = hipEventCreateWithFlags(&p->join[l], hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreate(&p->ev_proj[l]);
         if (e == hipSuccess) e = hipEventCreate(&p->ev_recur[l]);
+        if (e == hipSuccess) e = hipEventCreate(&p->ev_launch0[l]);
+        if (e == hipSuccess) e = hipEventCreate(&p->ev_launch1[l]);
     }
     if (e == hipSuccess) e = hipEventCreate(&p->ev_start);
     if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -409,7 +421,7 @@ bilstm_status bilstm_forward(bilstm_plan *plan, const float *x, size_t x_len, fl
         // every layer after the first reads the previous layer's complete output from y
         if ((st = enqueue_projection(plan, l, l == 0 ? x : y, plan->gates, stream)) != BILSTM_OK) return st;
         if (plan->phase_events) BL_HIP(hipEventRecord(plan->ev_proj[l], stream), "phase event");
-        if ((st = enqueue_recurrence(plan, l, plan->gates, y, base + l * plan->steps, stream)) != BILSTM_OK) {
+        if ((st = enqueue_recurrence(plan, l, plan->gates, y, base + l * plan->steps, stream, true)) != BILSTM_OK) {
             return st;
         }
         if (plan->phase_events) BL_HIP(hipEventRecord(plan->ev_recur[l], stream), "phase event");
@@ -442,7 +454,7 @@ bilstm_status bilstm_recur(bilstm_plan *plan, int layer, const float *gates, siz
     BL_HIP(scope.error(), "recur: hipSetDevice");
     uint32_t base = 0;
     if ((st = reserve_flags(plan, plan->steps, stream, &base)) != BILSTM_OK) return st;
-    return enqueue_recurrence(plan, layer, gates, y, base, stream);
+    return enqueue_recurrence(plan, layer, gates, y, base, stream, false);
 }
 
 bilstm_status bilstm_plan_get_info(const bilstm_plan *plan, bilstm_plan_info *info) {
@@ -475,7 +487,7 @@ bilstm_status bilstm_set_phase_events(bilstm_plan *plan, int enable) {
 
 bilstm_status bilstm_phase_times(bilstm_plan *plan, float *ms, size_t n) {
     if (plan == nullptr || ms == nullptr) return fail(BILSTM_INVALID_ARGUMENT, "phase_times: NULL argument");
-    if (n < 2 * kLayers) return fail(BILSTM_BUFFER_LENGTH, "phase_times: need %d values, got %zu", 2 * kLayers, n);
+    if (n < 3 * kLayers) return fail(BILSTM_BUFFER_LENGTH, "phase_times: need %d values, got %zu", 3 * kLayers, n);
     if (!plan->phases_recorded) {
         return fail(BILSTM_INVALID_ARGUMENT, "phase_times: no forward ran with phase events enabled");
     }
@@ -486,6 +498,7 @@ bilstm_status bilstm_phase_times(bilstm_plan *plan, float *ms, size_t n) {
         hipEvent_t before = l == 0 ? plan->ev_start : plan->ev_recur[l - 1];
         BL_HIP(hipEventElapsedTime(&ms[l], before, plan->ev_proj[l]), "phase_times");
         BL_HIP(hipEventElapsedTime(&ms[kLayers + l], plan->ev_proj[l], plan->ev_recur[l]), "phase_times");
+        BL_HIP(hipEventElapsedTime(&ms[2 * kLayers + l], plan->ev_launch0[l], plan->ev_launch1[l]), "phase_times");
     }
     return BILSTM_OK;
 }

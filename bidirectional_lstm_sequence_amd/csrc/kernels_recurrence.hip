@@ -55,26 +55,15 @@ constexpr int kXor2 = 0x4E;       // quad_perm 2,3,0,1
 template <int L>
 constexpr int kBcast = L * 0x55;  // quad_perm L,L,L,L: every lane reads quad lane L
 
-// e^{-a} for a >= 0, on the hardware exp2.
-__device__ __forceinline__ float exp_neg(float a) {
-    return __builtin_amdgcn_exp2f(a * -1.4426950408889634f);
+// σ(z) = 1/(1 + e^{-z}) on the hardware exp2 and reciprocal. For very negative z, e^{-z}
+// overflows to +inf and the reciprocal returns the exact limit 0, so no clamp is needed.
+__device__ __forceinline__ float sigmoid_f(float z) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
 }
 
-// tanh(z) = sign(z)·(1 - e^{-2|z|})/(1 + e^{-2|z|}).
+// tanh(z) = 2σ(2z) - 1.
 __device__ __forceinline__ float tanh_f(float z) {
-    const float e = exp_neg(2.0f * fabsf(z));
-    const float t = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
-    return copysignf(t, z);
-}
-
-// Activation of gate q on lane q: σ(a) for q = 0, 1, 3; tanh(a) = 2σ(2a) - 1 for q = 2.
-// σ(z) is evaluated through e^{-|z|}, so it never overflows.
-__device__ __forceinline__ float gate_act(float a, bool is_g) {
-    const float z = is_g ? 2.0f * a : a;
-    const float e = exp_neg(fabsf(z));
-    const float r = __builtin_amdgcn_rcpf(1.0f + e);
-    const float sg = z >= 0.0f ? r : e * r;
-    return is_g ? fmaf(2.0f, sg, -1.0f) : sg;
+    return fmaf(2.0f, sigmoid_f(2.0f * z), -1.0f);
 }
 
 template <int BT>
@@ -92,6 +81,11 @@ __device__ __forceinline__ unsigned long long load_word(const unsigned long long
 __device__ __forceinline__ void store_word(unsigned long long *p, unsigned long long v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+template <int N>
+struct Slot {
+    static constexpr int value = N;
+};
 
 template <int KG, int BT>
 __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArgs a) {
@@ -119,6 +113,11 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
     const int u = tid >> 2;
     const int q = tid & 3;
     const int ug = member * U + u;  // global hidden unit of this quad
+    const int win0 = tile * BT;
+    // Window this lane writes: lane q < BT takes window q of the tile; the other lanes of the
+    // quad, and lanes of windows past the batch, duplicate window 0 (always valid) so every
+    // lane runs the same straight-line code and their stores are idempotent.
+    const int qe = (q < BT && win0 + q < a.batch) ? q : 0;
 
     __shared__ __attribute__((aligned(16))) float hs[2][kHPad * BT];
     __shared__ __attribute__((aligned(16))) float gs[KG > 1 ? 2 : 1][KG > 1 ? U * 4 * BT : 4];
@@ -145,16 +144,17 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
     // h_{-1} = 0
     for (int i = tid; i < 2 * kHPad * BT; i += NT) (&hs[0][0])[i] = 0.0f;
 
-    const bool window_lane = q < BT;
-    const int win0 = tile * BT;
-    const size_t gate_col = static_cast<size_t>(dir) * kGates + 4 * ug + q;
     auto time_of = [&](int s) { return dir == 0 ? s : steps - 1 - s; };
-    // this lane's gate input (gate q of unit ug) for window b of the tile at step s
+    // Gate input of gate q, unit ug, window b of the tile at step s. Steps past the end and
+    // windows past the batch read in-bounds stand-ins (last step, window 0) whose values
+    // nobody uses, so the loads need no branch.
+    const size_t gate_col = static_cast<size_t>(dir) * kGates + 4 * ug + q;
     auto gate_in = [&](int b, int s) -> float {
-        const int w = win0 + b;
-        if (w >= a.batch || s >= steps) return 0.0f;
-        return a.gates[(static_cast<size_t>(w) * steps + time_of(s)) * kGateCols + gate_col];
+        const int w = (win0 + b < a.batch) ? win0 + b : win0;
+        const int sc = s < steps ? s : steps - 1;
+        return a.gates[(static_cast<size_t>(w) * steps + time_of(sc)) * kGateCols + gate_col];
     };
+    float *const ycol = a.y + static_cast<size_t>(win0 + qe) * steps * kWidth + dir * kHidden + ug;
 
     // KG == 1: per-lane register ring of gate inputs.
     float ring[kRing][BT];
@@ -190,6 +190,10 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
                 for (int v = 0; v < kStageVec; ++v) stage[p][v] = stage_load(tid + 64 * v, p + 1);
         }
     }
+    // Drain the prologue's loads (R, the first gate inputs) here, once. Left outstanding, they
+    // make the compiler's wait counting conservative inside the step loop, where it would then
+    // wait for every in-flight load — including the gate prefetches — at each step.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     unsigned long long *xdir = nullptr;
@@ -197,129 +201,141 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
         xdir = a.exchange + (static_cast<size_t>(dir) * a.tiles + tile) * 2 * kHidden * BT;
     }
     const bool is_g = q == 2;
-    float cst = 0.0f;  // cell state of (unit ug, window q) on window lanes
+    float cst = 0.0f;  // cell state of (unit ug, window qe)
     bool timed_out = false;
 
-    for (int s0 = 0; s0 < steps; s0 += kRing) {
-#pragma unroll
-        for (int p = 0; p < kRing; ++p) {
-            const int s = s0 + p;
-            if (s < steps) {
-                const int cur = s & 1;
-                const int nxt = cur ^ 1;
+    // One step s; P is the step's slot in the prefetch ring (s mod kRing), a compile-time
+    // constant so the ring stays in registers.
+    auto step = [&](int s, auto slot) {
+        constexpr int P = decltype(slot)::value;
+        const int cur = s & 1;
+        const int nxt = cur ^ 1;
 
-                // (1) partial dot products over this lane's K quarter
-                float acc[4][BT];
-                {
-                    const float *hp = &hs[cur][36 * q * BT];
+        // (1) partial dot products over this lane's K quarter
+        float acc[4][BT];
+        {
+            const float *hp = &hs[cur][36 * q * BT];
 #pragma unroll
-                    for (int v = 0; v < 8 * BT; ++v) {
-                        const v4f h4 = *reinterpret_cast<const v4f *>(hp + 4 * v);
+            for (int v = 0; v < 8 * BT; ++v) {
+                const v4f h4 = *reinterpret_cast<const v4f *>(hp + 4 * v);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int idx = 4 * v + e;  // = k_local·BT + b
-                            const int kk = idx / BT;
-                            const int b = idx % BT;
+                for (int e = 0; e < 4; ++e) {
+                    const int idx = 4 * v + e;  // = k_local·BT + b
+                    const int kk = idx / BT;
+                    const int b = idx % BT;
 #pragma unroll
-                            for (int sl = 0; sl < 4; ++sl) {
-                                acc[sl][b] = kk == 0 ? rr[sl][0] * h4[e] : fmaf(rr[sl][kk], h4[e], acc[sl][b]);
-                            }
-                        }
+                    for (int sl = 0; sl < 4; ++sl) {
+                        acc[sl][b] = kk == 0 ? rr[sl][0] * h4[e] : fmaf(rr[sl][kk], h4[e], acc[sl][b]);
                     }
                 }
-
-                // (2) reduce-scatter: lane q keeps gate q, sum ((p0+p1)+(p2+p3))
-                float sum[BT];
-#pragma unroll
-                for (int b = 0; b < BT; ++b) {
-                    const float t0 = acc[0][b] + dpp<kXor1>(acc[1][b]);  // gates q, via quads {q, q^1}
-                    const float t2 = acc[2][b] + dpp<kXor1>(acc[3][b]);  // gate q^2
-                    sum[b] = t0 + dpp<kXor2>(t2);
-                }
-
-                // (3) activations of gate q for each window, then the cell update on window lanes
-                float act[BT];
-                if constexpr (KG == 1) {
-#pragma unroll
-                    for (int b = 0; b < BT; ++b) act[b] = gate_act(ring[p][b] + sum[b], is_g);
-                } else {
-#pragma unroll
-                    for (int b = 0; b < BT; ++b) act[b] = gate_act(gs[cur][4 * (b * U + u) + q] + sum[b], is_g);
-                }
-                float fg[BT], gg[BT], og[BT];
-#pragma unroll
-                for (int b = 0; b < BT; ++b) {
-                    fg[b] = dpp<kBcast<1>>(act[b]);
-                    gg[b] = dpp<kBcast<2>>(act[b]);
-                    og[b] = dpp<kBcast<3>>(act[b]);
-                }
-                // window lane q (< BT) takes window q: its i is lane 0's activation of window q
-                float ig[BT];
-#pragma unroll
-                for (int b = 0; b < BT; ++b) ig[b] = dpp<kBcast<0>>(act[b]);
-                const float i_w = pick<BT>(ig, q), f_w = pick<BT>(fg, q);
-                const float g_w = pick<BT>(gg, q), o_w = pick<BT>(og, q);
-                cst = fmaf(f_w, cst, i_w * g_w);
-                const float hval = o_w * tanh_f(cst);
-
-                const unsigned int flag = a.flag_base + static_cast<unsigned int>(s) + 1u;
-                if (window_lane) {
-                    hs[nxt][hpad(ug) * BT + q] = hval;
-                    if constexpr (KG > 1) {
-                        const unsigned long long word =
-                            (static_cast<unsigned long long>(flag) << 32) | __float_as_uint(hval);
-                        store_word(xdir + (static_cast<size_t>(cur) * kHidden + ug) * BT + q, word);
-                    }
-                }
-
-                if constexpr (KG == 1) {
-                    // refill this ring slot with step s + kRing
-#pragma unroll
-                    for (int b = 0; b < BT; ++b) ring[p][b] = gate_in(b, s + kRing);
-                } else {
-                    if (stager) {
-                        // stage[p] holds step s+1 (loaded kRing steps ago): into LDS slot nxt,
-                        // then load step s + 1 + kRing in its place
-#pragma unroll
-                        for (int v = 0; v < kStageVec; ++v) {
-                            const int j = tid + 64 * v;
-                            if (j < U * BT) *reinterpret_cast<v4f *>(&gs[nxt][4 * j]) = stage[p][v];
-                            stage[p][v] = stage_load(j, s + 1 + kRing);
-                        }
-                    } else {
-                        // (4) gather the other workgroups' h of step s
-                        constexpr int kOthers = (kHidden - U) * BT;
-                        const unsigned long long *xs = xdir + static_cast<size_t>(cur) * kHidden * BT;
-                        for (int idx = tid - 64; idx < kOthers; idx += NT - 64) {
-                            const int uo = idx / BT;
-                            const int b = idx - uo * BT;
-                            const int ugo = uo < member * U ? uo : uo + U;
-                            const unsigned long long *wp = xs + static_cast<size_t>(ugo) * BT + b;
-                            unsigned long long w = load_word(wp);
-                            if (static_cast<unsigned int>(w >> 32) != flag && !timed_out) {
-                                const unsigned long long t0 = wall_clock64();
-                                while (true) {
-                                    w = load_word(wp);
-                                    if (static_cast<unsigned int>(w >> 32) == flag) break;
-                                    if (wall_clock64() - t0 > a.timeout_ticks) {
-                                        atomicOr(a.error, 1u);
-                                        timed_out = true;
-                                        break;
-                                    }
-                                }
-                            }
-                            hs[nxt][hpad(ugo) * BT + b] = __uint_as_float(static_cast<unsigned int>(w));
-                        }
-                    }
-                }
-
-                if (window_lane && win0 + q < a.batch) {
-                    a.y[(static_cast<size_t>(win0 + q) * steps + time_of(s)) * kWidth + dir * kHidden + ug] = hval;
-                }
-                __syncthreads();
             }
         }
+
+        // (2) reduce-scatter: lane q keeps gate q, sum ((p0+p1)+(p2+p3))
+        float sum[BT];
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+            const float t0 = acc[0][b] + dpp<kXor1>(acc[1][b]);  // gate q, quads {q, q^1}
+            const float t2 = acc[2][b] + dpp<kXor1>(acc[3][b]);  // gate q^2
+            sum[b] = t0 + dpp<kXor2>(t2);
+        }
+
+        // (3) activation of gate q for each window (tanh(a) = 2σ(2a) - 1 for gate g), then
+        // every lane updates the cell of window qe
+        float act[BT];
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+            float gin;
+            if constexpr (KG == 1) {
+                gin = ring[P][b];
+            } else {
+                gin = gs[cur][4 * (b * U + u) + q];
+            }
+            const float sg = sigmoid_f(is_g ? 2.0f * (gin + sum[b]) : gin + sum[b]);
+            act[b] = is_g ? fmaf(2.0f, sg, -1.0f) : sg;
+        }
+        float ig[BT], fg[BT], gg[BT], og[BT];
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+            ig[b] = dpp<kBcast<0>>(act[b]);
+            fg[b] = dpp<kBcast<1>>(act[b]);
+            gg[b] = dpp<kBcast<2>>(act[b]);
+            og[b] = dpp<kBcast<3>>(act[b]);
+        }
+        const float i_w = pick<BT>(ig, qe), f_w = pick<BT>(fg, qe);
+        const float g_w = pick<BT>(gg, qe), o_w = pick<BT>(og, qe);
+        cst = fmaf(f_w, cst, i_w * g_w);
+        const float hval = o_w * tanh_f(cst);
+
+        // h to LDS for the next step (lanes of one window write the same value)
+        hs[nxt][hpad(ug) * BT + qe] = hval;
+        const unsigned int flag = a.flag_base + static_cast<unsigned int>(s) + 1u;
+        if constexpr (KG > 1) {
+            if (q < BT) {
+                const unsigned long long word =
+                    (static_cast<unsigned long long>(flag) << 32) | __float_as_uint(hval);
+                store_word(xdir + (static_cast<size_t>(cur) * kHidden + ug) * BT + q, word);
+            }
+        }
+
+        if constexpr (KG == 1) {
+            // refill this ring slot with step s + kRing
+#pragma unroll
+            for (int b = 0; b < BT; ++b) ring[P][b] = gate_in(b, s + kRing);
+        } else {
+            if (stager) {
+                // stage[P] holds step s+1 (loaded kRing steps ago): into LDS slot nxt, then
+                // load step s + 1 + kRing in its place
+#pragma unroll
+                for (int v = 0; v < kStageVec; ++v) {
+                    const int j = tid + 64 * v;
+                    if (j < U * BT) *reinterpret_cast<v4f *>(&gs[nxt][4 * j]) = stage[P][v];
+                    stage[P][v] = stage_load(j, s + 1 + kRing);
+                }
+            } else {
+                // (4) gather the other workgroups' h of step s
+                constexpr int kOthers = (kHidden - U) * BT;
+                const unsigned long long *xs = xdir + static_cast<size_t>(cur) * kHidden * BT;
+                for (int idx = tid - 64; idx < kOthers; idx += NT - 64) {
+                    const int uo = idx / BT;
+                    const int b = idx - uo * BT;
+                    const int ugo = uo < member * U ? uo : uo + U;
+                    const unsigned long long *wp = xs + static_cast<size_t>(ugo) * BT + b;
+                    unsigned long long w = load_word(wp);
+                    if (static_cast<unsigned int>(w >> 32) != flag && !timed_out) {
+                        const unsigned long long t0 = wall_clock64();
+                        while (true) {
+                            w = load_word(wp);
+                            if (static_cast<unsigned int>(w >> 32) == flag) break;
+                            if (wall_clock64() - t0 > a.timeout_ticks) {
+                                atomicOr(a.error, 1u);
+                                timed_out = true;
+                                break;
+                            }
+                        }
+                    }
+                    hs[nxt][hpad(ugo) * BT + b] = __uint_as_float(static_cast<unsigned int>(w));
+                }
+            }
+        }
+
+        ycol[static_cast<size_t>(time_of(s)) * kWidth] = hval;
+        __syncthreads();
+    };
+
+    // Full groups of kRing steps run as straight-line code (no per-step guards), which keeps
+    // the compiler's memory-wait counting exact; the last partial group is guarded.
+    int s0 = 0;
+    for (; s0 + kRing <= steps; s0 += kRing) {
+        step(s0 + 0, Slot<0>{});
+        step(s0 + 1, Slot<1>{});
+        step(s0 + 2, Slot<2>{});
+        step(s0 + 3, Slot<3>{});
     }
+    static_assert(kRing == 4, "the unrolled groups assume a ring of 4");
+    if (s0 + 0 < steps) step(s0 + 0, Slot<0>{});
+    if (s0 + 1 < steps) step(s0 + 1, Slot<1>{});
+    if (s0 + 2 < steps) step(s0 + 2, Slot<2>{});
 }
 
 __global__ void exchange_clear_kernel(unsigned long long *words, size_t count) {

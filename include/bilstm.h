@@ -83,10 +83,14 @@ typedef struct {
 typedef struct {
     int32_t recur_groups; /* workgroups per (direction, window tile): 1, 2 or 4; 0 = auto */
     int32_t recur_tile;   /* windows per tile: 1, 2 or 4; 0 = auto */
-    int32_t concurrent;   /* directions: -1 auto, 0 both on the caller's stream, 1 reverse on
-                             the plan's side stream, 2 both directions in one launch */
-    int32_t watchdog_us;  /* bound of one recurrence wait in microseconds; 0 = 2 s. A wait that
-                             hits it sets the plan's error flag (bilstm_check) and stops waiting */
+    int32_t concurrent;   /* directions: -1 auto (2 when both grids fit together, else 0),
+                             0 one after the other on the caller's stream, 1 reverse on the
+                             plan's side stream joined back by events, 2 both directions in one
+                             launch on the caller's stream */
+    int32_t watchdog_us;  /* bound of one recurrence wait in microseconds; 0 = 2 s; -1 = give
+                             up on the first unsuccessful poll (for failure-handling tests).
+                             A wait that hits it sets the plan's error flag (bilstm_check) and
+                             stops waiting */
     int32_t reserved[4];  /* must be zero */
 } bilstm_options;
 
@@ -99,7 +103,7 @@ typedef struct {
     int32_t recur_tiles;     /* number of window tiles */
     int32_t recur_threads;   /* threads per recurrence workgroup */
     int32_t recur_launches;  /* launches per direction per layer */
-    int32_t concurrent;      /* 1: reverse direction on the side stream */
+    int32_t concurrent;      /* 0 serial, 1 side stream, 2 one launch for both directions */
     int32_t proj_tile_m;     /* projection output tile, rows */
     int32_t proj_tile_n;     /* projection output tile, gate columns */
     int32_t cu_count;        /* compute units of the device */
@@ -165,8 +169,10 @@ bilstm_status bilstm_check(bilstm_plan *plan);
  * Per-phase timing (page `lstmproj.rs`: the `LstmPhases` hooks around the projection and
  * the recurrence of each layer). When enabled, bilstm_forward records HIP events on
  * `stream` around each phase. bilstm_phase_times then waits for the last forward and
- * writes 8 values in milliseconds: projection of layers 0..3, then recurrence of layers
- * 0..3 (both directions, including the join). n must be >= 8.
+ * writes 12 values in milliseconds: projection of layers 0..3; recurrence phase of layers
+ * 0..3 (both directions, including any join); duration of the first recurrence launch on the
+ * caller's stream of layers 0..3 (the launch running both directions when they share one
+ * launch, else the forward direction's). n must be >= 12.
  */
 bilstm_status bilstm_set_phase_events(bilstm_plan *plan, int enable);
 bilstm_status bilstm_phase_times(bilstm_plan *plan, float *ms, size_t n);

@@ -219,13 +219,15 @@ def test_time_reversal_layer0_bitwise(bl):
     plan_s.close()
 
 
-def test_watchdog_reports_timeout_and_grid_drains(bl):
-    """A 1 µs bound on each exchange wait: waits give up, the kernels still finish, and the
-    plan reports BILSTM_TIMEOUT instead of hanging."""
+@pytest.mark.parametrize("concurrent", [0, 2])
+def test_watchdog_reports_timeout_and_grid_drains(bl, concurrent):
+    """Exchange waits that give up on their first unsuccessful poll (forced from the host):
+    the kernels still finish, and the plan reports BILSTM_TIMEOUT instead of hanging. The
+    first step's waits always miss at least once (the producers are still loading R)."""
     x, layers = workloads.make_workload("b8")
     xs = np.ascontiguousarray(x[:, :64])
-    note("watchdog 1us groups=4")
-    plan = bl.Plan(layers, 8, 64, groups=4, tile=1, watchdog_us=1)
+    note(f"watchdog first-miss groups=4 concurrent={concurrent}")
+    plan = bl.Plan(layers, 8, 64, groups=4, tile=1, concurrent=concurrent, watchdog_us=-1)
     plan.forward(torch.from_numpy(xs).cuda())
     with pytest.raises(bl.BilstmError) as e:
         plan.check()
