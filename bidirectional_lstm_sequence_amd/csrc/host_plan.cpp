@@ -153,11 +153,10 @@ bool overlap(const void *a, size_t a_bytes, const void *b, size_t b_bytes) {
     return x < y + b_bytes && y < x + a_bytes;
 }
 
-// Zero the exchange words when the flags of the next pass would wrap, so no stale word can
-// carry a flag that pass expects (speakrs 0.6.0, page `lstmproj.rs`, `clear_state`: the
-// words are zeroed before a pass; here the zeroing happens at plan creation and whenever
-// the 32-bit flag space runs out, and every pass in between uses flags above all earlier
-// ones).
+// Reserve `count` flag values for the next pass. Stale words must never match a flag a wait
+// expects (speakrs 0.6.0, page `lstmproj.rs`, `clear_state`, where the words are zeroed at the
+// start of every pass). Here they are zeroed at plan creation and whenever the 32-bit flag
+// space would wrap; in between, each pass uses flag values above every earlier pass's.
 bilstm_status reserve_flags(bilstm_plan *p, uint32_t count, hipStream_t stream, uint32_t *base) {
     if (p->exchange == nullptr) {
         *base = 0;

@@ -1,7 +1,6 @@
 // Time-parallel input projection of one layer, both directions in one GEMM, on gfx950 FP32
-// MFMA (speakrs 0.6.0, page `lstmproj.rs`: module doc, `InputProjection::enqueue` — a
-// tiled projection computes x·Wᵀ for every step of each direction, gate columns reordered
-// so each hidden unit's four gates are adjacent).
+// MFMA (speakrs 0.6.0, page `lstmproj.rs`: module doc, `InputProjection::enqueue` — x·Wᵀ
+// for all steps at once, with W's gate rows permuted per hidden unit).
 //
 //   gates[m][n] = bias[n] + sum_k x[m][k] · w[n][k]      m < rows, n < 1024, k < in
 //

@@ -2,8 +2,8 @@
 // exchange latency probe (speakrs 0.6.0, page `lstmproj.rs`: module doc — one launch per
 // direction runs that direction's whole recurrence with the recurrent weights held on chip;
 // `RecurrencePlan` doc — several workgroups per window tile split the units and exchange h,
-// or one workgroup holds the whole matrix and needs no exchange; `Exchange` and
-// `clear_state` — flagged words zeroed before a pass).
+// or, on the A100 variant, a single block keeps all of R and exchanges nothing; `Exchange`
+// and `clear_state` — flagged words zeroed before a pass).
 //
 // Work split. A launch covers `tile_count` tiles of BT windows for one direction (or both,
 // gridDim.y = 2). Each tile is served by KG workgroups; workgroup `member` owns hidden

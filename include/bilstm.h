@@ -84,7 +84,7 @@ typedef struct {
     int32_t recur_groups; /* workgroups per (direction, window tile): 1, 2 or 4; 0 = auto */
     int32_t recur_tile;   /* windows per tile: 1, 2 or 4; 0 = auto */
     int32_t concurrent;   /* directions: -1 auto (2 when both grids fit together, else 0),
-                             0 one after the other on the caller's stream, 1 reverse on the
+                             0 serially on the caller's stream, 1 reverse on the
                              plan's side stream joined back by events, 2 both directions in one
                              launch on the caller's stream */
     int32_t watchdog_us;  /* bound of one recurrence wait in microseconds; 0 = 2 s; -1 = give
@@ -113,8 +113,8 @@ typedef struct {
 
 /*
  * Create a plan for `batch` windows of `steps` frames on HIP device `device`, packing the
- * four layers' weights (page `lstmproj.rs`, `with_recurrence`: gate rows interleaved so
- * each hidden unit's four gates are adjacent, bias folded to Wb + Rb).
+ * four layers' weights (page `lstmproj.rs`, `with_recurrence`: gate rows permuted so rows
+ * 4j..4j+3 hold hidden unit j's i, f, g, o; bias folded to Wb + Rb).
  * Returns BILSTM_UNSUPPORTED on a device other than gfx950. *out receives the plan.
  * batch and steps must be >= 1; batch·steps·256 must fit 32 bits.
  */
@@ -130,8 +130,9 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
  * The whole stack (page `lstmproj.rs`, `Oxide::enqueue`).
  *   x [batch][steps][60]  device, fp32, 16-byte aligned; read only; x_len = batch·steps·60
  *   y [batch][steps][256] device, fp32, 16-byte aligned; y_len = batch·steps·256
- * y doubles as the inter-layer buffer: each layer's projection reads the previous layer's
- * complete output before its recurrence overwrites it (page `lstmproj.rs`, module doc).
+ * y doubles as the inter-layer buffer, updated in place layer by layer: a layer's
+ * projection has consumed all of the previous layer's output by the time its recurrence
+ * starts writing (page `lstmproj.rs`, module doc).
  * x and y must not overlap. Asynchronous on `stream`.
  */
 bilstm_status bilstm_forward(bilstm_plan *plan, const float *x, size_t x_len, float *y,
