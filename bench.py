@@ -26,10 +26,12 @@ sys.path.insert(0, ROOT)
 import workloads  # noqa: E402
 
 PEAK_FP32_MFMA_TFLOPS = 157.3      # MI355X dense FP32 matrix peak (published)
-PEAK_FP32_VECTOR_TFLOPS = 157.3    # MI355X FP32 vector peak (published, packed dual-issue)
+PEAK_FP32_VECTOR_TFLOPS = 157.3    # MI355X FP32 vector peak (published)
 CU_COUNT_NOMINAL = 256
 CLOCK_GHZ = 2.4
-FMA_PER_CLK_PER_CU = 64            # non-packed FP32 FMA: 4 SIMDs x 16 lanes
+# FP32 FMA per clock per CU implied by the published vector peak:
+# 157.3e12 / (256 CUs x 2.4e9 Hz x 2 flop) = 128
+FMA_PER_CLK_PER_CU = 128
 
 RECUR_FMA_PER_FRAME_DIR = 512 * 128                   # R·h per step per direction
 
@@ -94,6 +96,7 @@ def main() -> int:
     ap.add_argument("--groups", type=int, default=0)
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--concurrent", type=int, default=-1)
+    ap.add_argument("--slices", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -125,7 +128,7 @@ def main() -> int:
     x, layers = workloads.make_workload(wl)
     frames = wl.batch * wl.steps
     plan = bl.Plan(layers, wl.batch, wl.steps, groups=args.groups, tile=args.tile,
-                   concurrent=args.concurrent)
+                   concurrent=args.concurrent, slices=args.slices)
     info = plan.info()
     xd = torch.from_numpy(x).cuda()
     yd = torch.empty((wl.batch, wl.steps, 256), dtype=torch.float32, device="cuda")
@@ -155,28 +158,41 @@ def main() -> int:
     value = frames * args.steps / (total_ms / 1e3)
     timed_phases = plan.phase_times()
 
-    # more phase samples after the timed region (medians)
-    proj_ms = [[v] for v in timed_phases["projection_ms"]]
-    rec_ms = [[v] for v in timed_phases["recurrence_ms"]]
-    launch_ms = [[v] for v in timed_phases["recurrence_launch_ms"]]
-    for _ in range(max(2, min(9, args.steps))):
-        plan.forward(xd, yd)
-        pt = plan.phase_times()
+    # The recurrence launch bracketed by the plan's events in the last timed forward (the first
+    # slice's launch when the batch runs in slices): the dominant kernel's duration.
+    launch_dur_ms = statistics.mean(timed_phases["recurrence_launch_ms"])
+    slice_windows = info["slice_windows"] if info["slices"] > 1 else wl.batch
+    launch_dirs = 2 if info["concurrent"] == 2 else 1
+    flop_per_launch = launch_dirs * recurrence_flops_per_layer(slice_windows * wl.steps) / 2
+
+    # Each kernel alone, outside the timed region, on the whole batch: the projection of every
+    # layer (bilstm_project) and the recurrence of every layer (bilstm_recur), each between HIP
+    # events on the caller's stream; medians over repetitions.
+    reps = max(3, min(9, args.steps))
+    gates = torch.empty((frames, 1024), dtype=torch.float32, device="cuda")
+    y2 = torch.empty_like(yd)
+    proj_ms = [[] for _ in range(4)]
+    rec_ms = [[] for _ in range(4)]
+    layer_in = [xd.view(frames, 60)] + [yd.view(frames, 256)] * 3
+    for _ in range(reps):
         for l in range(4):
-            proj_ms[l].append(pt["projection_ms"][l])
-            rec_ms[l].append(pt["recurrence_ms"][l])
-            launch_ms[l].append(pt["recurrence_launch_ms"][l])
-    plan.set_phase_events(False)
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record(stream)
+            plan.project(l, layer_in[l], gates)
+            e1.record(stream)
+            plan.recur(l, gates, y2)
+            e2.record(stream)
+            torch.cuda.synchronize()
+            proj_ms[l].append(e0.elapsed_time(e1))
+            rec_ms[l].append(e1.elapsed_time(e2))
+    plan.check()
     proj_med = [statistics.median(v) for v in proj_ms]
     rec_med = [statistics.median(v) for v in rec_ms]
-    plan.check()
     plan.close()
 
     # recurrence: the dominant kernel. Its achieved rate is the algorithmic FLOPs of one launch
-    # over that launch's duration in the timed region (events on the caller's stream).
-    launch_dirs = 2 if info["concurrent"] == 2 else 1
-    launch_dur_ms = statistics.mean(timed_phases["recurrence_launch_ms"])
-    rec_tflops = launch_dirs * recurrence_flops_per_layer(frames) / 2 / (launch_dur_ms / 1e3) / 1e12
+    # over that launch's duration in the timed region (events on the stream it runs on).
+    rec_tflops = flop_per_launch / (launch_dur_ms / 1e3) / 1e12
     rec_layer_ms = statistics.mean(rec_med)
     us_per_step = rec_layer_ms * 1e3 / wl.steps
     traffic = recorded_traffic(wl.name, info)
@@ -190,9 +206,11 @@ def main() -> int:
             print(f"exchange probe failed: {e}", file=sys.stderr)
     bound_us = fma_clk / (CLOCK_GHZ * 1e3) + ((xchg_ns or 0.0) / 1e3 if groups > 1 else 0.0)
 
-    # projection: fraction of FP32-MFMA peak over the four projection phases
+    # projection: fraction of FP32-MFMA peak over the four projections
     proj_total_ms = sum(proj_med)
     proj_tflops = projection_flops(frames) / (proj_total_ms / 1e3) / 1e12
+    proj_layer_tflops = [2.0 * frames * 1024 * k / (ms / 1e3) / 1e12
+                         for k, ms in zip((60, 256, 256, 256), proj_med)]
 
     out = {
         "metric": "frames/sec through 4-layer BiLSTM (H=128) at B=32,T=589; per-step latency",
@@ -210,21 +228,26 @@ def main() -> int:
         "config": {"workload": f"{wl.name}: {wl.batch} windows x {wl.steps} frames, 4-layer BiLSTM "
                                f"H=128, input 60", "batch": wl.batch, "seq_len": wl.steps,
                    "recurrence_split": {"groups": groups, "tile": tile, "tiles": info["recur_tiles"],
-                                        "concurrent": info["concurrent"]}},
+                                        "concurrent": info["concurrent"]},
+                   "slices": info["slices"], "slice_windows": info["slice_windows"]},
         "roofline": {"kernel": f"recurrence_kernel<{groups}, {tile}> ({launch_dirs} direction(s) per launch)",
                      "bound": "alu", "achieved": rec_tflops, "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
                      "frac": rec_tflops / PEAK_FP32_VECTOR_TFLOPS,
                      "traffic": traffic["bytes_per_launch"] if traffic else None,
                      "launch_ms": launch_dur_ms,
-                     "flop_per_launch": launch_dirs * recurrence_flops_per_layer(frames) / 2,
+                     "flop_per_launch": flop_per_launch,
+                     "windows_per_launch": slice_windows,
                      "traffic_detail": traffic},
         "recurrence_step": {"us_per_step": us_per_step, "bound_us": bound_us,
                             "frac_of_bound": bound_us / us_per_step, "exchange_one_way_ns": xchg_ns,
                             "bound_terms": f"FMA {fma_clk:.0f} clk at {FMA_PER_CLK_PER_CU} FMA/clk/CU, "
                                            f"{CLOCK_GHZ} GHz" + (" + one exchange" if groups > 1 else "")},
         "projection": {"ms_total": proj_total_ms, "ms_per_layer": proj_med, "achieved_tflops": proj_tflops,
+                       "tflops_per_layer": proj_layer_tflops,
                        "peak_tflops": PEAK_FP32_MFMA_TFLOPS, "frac": proj_tflops / PEAK_FP32_MFMA_TFLOPS},
-        "phases_ms": {"projection": proj_med, "recurrence": rec_med},
+        "kernels_alone_ms": {"projection": proj_med, "recurrence": rec_med},
+        "phases_ms_first_slice": {"projection": timed_phases["projection_ms"],
+                                  "recurrence": timed_phases["recurrence_ms"]},
         "step_ms": {"median": statistics.median(step_ms), "min": min(step_ms), "max": max(step_ms)},
         "wall_s": wall,
     }

@@ -21,6 +21,16 @@ constexpr int kProjTileM = 128;
 constexpr int kProjTileN = 128;
 constexpr int kProjTileK = 32;
 constexpr int kProjThreads = 256;
+// LDS of one projection workgroup (two stages of A and B tiles, rows padded to 36 floats) and
+// of one CU.
+constexpr size_t kProjLdsBytes = 2 * 2 * kProjTileM * (kProjTileK + 4) * sizeof(float);
+constexpr size_t kCuLdsBytes = 160 * 1024;
+
+// Batch slices of a forward pass (concurrent chains of layers on their own streams). A HIP
+// process gets 4 hardware queues by default; streams beyond that share queues and serialize
+// (measured: 4 slices ran slower than 1), so the automatic choice stays at 2.
+constexpr int kMaxSlices = 8;
+constexpr int kAutoSlices = 2;
 
 inline int padded_input(int in) { return (in + kProjTileK - 1) / kProjTileK * kProjTileK; }
 
@@ -58,13 +68,18 @@ struct RecurArgs {
     int tile_first;                // first tile of this launch
     int tile_count;                // tiles in this launch
     unsigned int flag_base;        // flags of this layer are flag_base + s + 1
+    unsigned int flag_skew;        // added to the flag a wait expects: 0, or a value no
+                                   // producer writes (forced-timeout tests)
     unsigned long long timeout_ticks;  // watchdog, in wall-clock ticks
 };
 
 // Launchers (kernels_*.hip). They return the launch's hipError_t.
-hipError_t launch_projection(const ProjArgs &args, hipStream_t stream);
+// The projection on `workgroups` persistent workgroups (one per CU; rounded to a multiple of 8).
+hipError_t launch_projection(const ProjArgs &args, int workgroups, hipStream_t stream);
 hipError_t launch_recurrence(int groups, int tile, const RecurArgs &args, int directions,
-                             hipStream_t stream);
+                             size_t dynamic_lds, hipStream_t stream);
+// Allow `bytes` of dynamic LDS per recurrence workgroup of this split.
+hipError_t recurrence_allow_lds(int groups, int tile, size_t bytes);
 hipError_t launch_exchange_clear(unsigned long long *words, size_t count, hipStream_t stream);
 hipError_t recurrence_occupancy(int groups, int tile, int *per_cu);
 hipError_t run_exchange_probe(int same_xcd, int round_trips, unsigned long long timeout_ticks,

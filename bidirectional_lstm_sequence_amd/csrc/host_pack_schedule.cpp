@@ -46,8 +46,11 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
                     cu_count, per_cu);
     }
     if (opt != nullptr) {
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 3; ++i) {
             if (opt->reserved[i] != 0) return fail(BILSTM_INVALID_ARGUMENT, "options: reserved[%d] must be 0", i);
+        }
+        if (opt->slices < 0 || opt->slices > kMaxSlices) {
+            return fail(BILSTM_INVALID_ARGUMENT, "options: slices %d is not in 0..%d", opt->slices, kMaxSlices);
         }
         if (opt->recur_groups != 0 && !valid_groups(opt->recur_groups)) {
             return fail(BILSTM_UNSUPPORTED, "options: recur_groups %d is not one of 1, 2, 4",
@@ -113,8 +116,31 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
         }
     }
 
+    // Batch slices: while one slice's recurrence runs (on 2·tiles/slices of the CUs), another
+    // slice's projection uses the CUs it leaves idle. Only single-workgroup tiles: a split
+    // tile's workgroups wait for each other, and two slices' launches partly resident at once
+    // could then wait on each other for good.
+    const int want_slices = (opt != nullptr) ? opt->slices : 0;
+    int slices = 1;
+    if (want_slices > 1) {
+        if (groups != 1 || concurrent == 1) {
+            return fail(BILSTM_UNSUPPORTED, "schedule: %d slices need recur_groups = 1 and concurrent != 1",
+                        want_slices);
+        }
+        slices = want_slices;
+    } else if (want_slices == 0 && groups == 1 && concurrent != 1) {
+        // auto: slice when the recurrence leaves at least half of the CUs idle
+        if (2 * grid * 2 <= cu_count && static_cast<long long>(batch) >= 2LL * tile) slices = kAutoSlices;
+    }
+    // windows per slice: a whole number of tiles
+    const long long tiles_per_slice = (static_cast<long long>(tiles) + slices - 1) / slices;
+    const int slice_windows = static_cast<int>(std::min<long long>(tiles_per_slice * tile, batch));
+    slices = static_cast<int>((static_cast<long long>(batch) + slice_windows - 1) / slice_windows);
+
     info->batch = batch;
     info->steps = steps;
+    info->slices = slices;
+    info->slice_windows = slice_windows;
     info->recur_groups = groups;
     info->recur_tile = tile;
     info->recur_tiles = tiles;

@@ -67,8 +67,17 @@ struct bilstm_plan {
     hipEvent_t ev_launch0[kLayers] = {nullptr, nullptr, nullptr, nullptr};
     hipEvent_t ev_launch1[kLayers] = {nullptr, nullptr, nullptr, nullptr};
     bool phases_recorded = false;
+    // batch slices: each runs its own chain of layers on its own stream
+    hipStream_t slice_stream[kMaxSlices] = {};
+    hipEvent_t slice_fork = nullptr;
+    hipEvent_t slice_first[kMaxSlices] = {};  // after the slice's first projection
+    hipEvent_t slice_join[kMaxSlices] = {};
+    size_t reserve_lds = 0;  // dynamic LDS of a recurrence workgroup (keeps its CU to itself)
+    int proj_workgroups = 0;         // persistent projection workgroups on an idle GPU
+    int proj_workgroups_sliced = 0;  // ... beside the other slices' recurrences
     uint32_t epoch = 0;  // flags of the next pass start above this value
     unsigned long long timeout_ticks = 0;
+    unsigned int flag_skew = 0;
     double watchdog_ms = 0.0;
     uint64_t device_bytes = 0;
 };
@@ -132,6 +141,12 @@ void release(bilstm_plan *p) {
         if (p->ev_launch1[l]) (void)hipEventDestroy(p->ev_launch1[l]);
     }
     if (p->ev_start) (void)hipEventDestroy(p->ev_start);
+    for (int i = 0; i < kMaxSlices; ++i) {
+        if (p->slice_stream[i]) (void)hipStreamDestroy(p->slice_stream[i]);
+        if (p->slice_first[i]) (void)hipEventDestroy(p->slice_first[i]);
+        if (p->slice_join[i]) (void)hipEventDestroy(p->slice_join[i]);
+    }
+    if (p->slice_fork) (void)hipEventDestroy(p->slice_fork);
     if (p->gates) (void)hipFree(p->gates);
     if (p->exchange) (void)hipFree(p->exchange);
     if (p->error) (void)hipFree(p->error);
@@ -171,27 +186,29 @@ bilstm_status reserve_flags(bilstm_plan *p, uint32_t count, hipStream_t stream, 
     return BILSTM_OK;
 }
 
+// The projection of rows [row_first, row_first + rows) of x into the same rows of gates.
 bilstm_status enqueue_projection(bilstm_plan *p, int layer, const float *x, float *gates,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, size_t row_first, size_t rows, int workgroups) {
     ProjArgs args{};
-    args.x = x;
+    args.x = x + row_first * p->in[layer];
     args.w = p->w[layer];
     args.bias = p->bias[layer];
-    args.gates = gates;
-    args.rows = static_cast<int>(p->rows);
+    args.gates = gates + row_first * kGateCols;
+    args.rows = static_cast<int>(rows);
     args.in = p->in[layer];
     args.kpad = p->kpad[layer];
-    args.row_tiles = static_cast<int>((p->rows + kProjTileM - 1) / kProjTileM);
+    args.row_tiles = static_cast<int>((rows + kProjTileM - 1) / kProjTileM);
     args.tiles = args.row_tiles * (kGateCols / kProjTileN);
-    BL_HIP(launch_projection(args, stream), "projection launch");
+    BL_HIP(launch_projection(args, workgroups, stream), "projection launch");
     return BILSTM_OK;
 }
 
-// Both directions' recurrence of one layer (speakrs 0.6.0, page `lstmproj.rs`,
-// `Oxide::recur`: the reverse direction on the side stream when the schedule allows it,
-// joined back before the next layer).
+// Both directions' recurrence of one layer over window tiles [tile_lo, tile_hi) (speakrs
+// 0.6.0, page `lstmproj.rs`, `Oxide::recur`: the reverse direction on the side stream when
+// the schedule allows it, joined back before the next layer).
 bilstm_status enqueue_recurrence(bilstm_plan *p, int layer, const float *gates, float *y,
-                                 uint32_t flag_base, hipStream_t stream, bool layer_events) {
+                                 uint32_t flag_base, hipStream_t stream, bool layer_events,
+                                 int tile_lo, int tile_hi) {
     const bilstm_plan_info &s = p->info;
     RecurArgs base{};
     base.gates = gates;
@@ -204,20 +221,22 @@ bilstm_status enqueue_recurrence(bilstm_plan *p, int layer, const float *gates, 
     base.tiles = s.recur_tiles;
     base.flag_base = flag_base;
     base.timeout_ticks = p->timeout_ticks;
+    base.flag_skew = p->flag_skew;
 
     const int per_launch = (s.recur_tiles + s.recur_launches - 1) / s.recur_launches;
+    const size_t lds = p->reserve_lds;
     // With phase events on, the first launch on the caller's stream is bracketed by its own
     // event pair, so its duration can be read separately from the phase.
     const bool mark = p->phase_events && layer_events;
     auto launch_direction = [&](int direction, int directions, hipStream_t on) -> bilstm_status {
-        for (int first = 0; first < s.recur_tiles; first += per_launch) {
+        for (int first = tile_lo; first < tile_hi; first += per_launch) {
             RecurArgs a = base;
             a.direction = direction;
             a.tile_first = first;
-            a.tile_count = std::min(per_launch, s.recur_tiles - first);
-            const bool bracket = mark && on == stream && direction == 0 && first == 0;
+            a.tile_count = std::min(per_launch, tile_hi - first);
+            const bool bracket = mark && on == stream && direction == 0 && first == tile_lo;
             if (bracket) BL_HIP(hipEventRecord(p->ev_launch0[layer], stream), "phase event");
-            BL_HIP(launch_recurrence(s.recur_groups, s.recur_tile, a, directions, on), "recurrence launch");
+            BL_HIP(launch_recurrence(s.recur_groups, s.recur_tile, a, directions, lds, on), "recurrence launch");
             if (bracket) BL_HIP(hipEventRecord(p->ev_launch1[layer], stream), "phase event");
         }
         return BILSTM_OK;
@@ -324,6 +343,9 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
     const double watchdog_ms = wd_us > 0 ? wd_us / 1000.0 : (wd_us < 0 ? 0.0 : kWatchdogMs);
     p->timeout_ticks = static_cast<unsigned long long>(watchdog_ms * wall_khz);
     p->watchdog_ms = watchdog_ms;
+    // watchdog_us = -1: every wait expects a flag that no producer ever writes, so its first
+    // poll misses and it gives up at once: a forced, deterministic timeout
+    p->flag_skew = wd_us < 0 ? 0x80000000u : 0u;
 
     // choose the split, then size the launches from the chosen kernel's occupancy
     bilstm_plan_info info{};
@@ -347,6 +369,14 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
     info.proj_tile_m = kProjTileM;
     info.proj_tile_n = kProjTileN;
     p->info = info;
+    // One persistent projection workgroup per CU; beside the recurrences of the other slices
+    // (each of their workgroups keeps a CU to itself), one per CU they leave free.
+    p->proj_workgroups = cu_count;
+    {
+        const int slice_tiles = (info.slice_windows + info.recur_tile - 1) / info.recur_tile;
+        const int busy = 2 * slice_tiles * info.recur_groups * (info.slices - 1);
+        p->proj_workgroups_sliced = std::max(8, cu_count - busy);
+    }
 
     // pack and upload the weights
     for (int l = 0; l < kLayers; ++l) {
@@ -386,6 +416,22 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
         if (e == hipSuccess) e = hipEventCreate(&p->ev_launch1[l]);
     }
     if (e == hipSuccess) e = hipEventCreate(&p->ev_start);
+    if (info.slices > 1) {
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->slice_fork, hipEventDisableTiming);
+        for (int i = 0; i < info.slices && e == hipSuccess; ++i) {
+            // slice 0 runs on the caller's stream; each other slice gets a stream of its own
+            if (i > 0) e = hipStreamCreateWithFlags(&p->slice_stream[i], hipStreamNonBlocking);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&p->slice_first[i], hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&p->slice_join[i], hipEventDisableTiming);
+        }
+        // A recurrence workgroup claims enough LDS that no projection workgroup fits beside it
+        // on its CU: the projections of other slices then run only on CUs no recurrence uses,
+        // and the latency-bound recurrence keeps its CU's issue slots and LDS to itself.
+        if (e == hipSuccess) {
+            p->reserve_lds = kCuLdsBytes - kProjLdsBytes + 4096;
+            e = recurrence_allow_lds(info.recur_groups, info.recur_tile, p->reserve_lds);
+        }
+    }
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         return fail_release(fail(BILSTM_HIP_ERROR, "plan_create: scratch setup: %s", hipGetErrorString(e)));
@@ -415,15 +461,52 @@ bilstm_status bilstm_forward(bilstm_plan *plan, const float *x, size_t x_len, fl
 
     uint32_t base = 0;
     if ((st = reserve_flags(plan, kLayers * plan->steps, stream, &base)) != BILSTM_OK) return st;
+    const bilstm_plan_info &info = plan->info;
+    const int slices = info.slices;
+    if (slices > 1) {
+        // fork: every slice stream starts after the caller's prior work
+        BL_HIP(hipEventRecord(plan->slice_fork, stream), "slice fork");
+        for (int i = 1; i < slices; ++i) {
+            BL_HIP(hipStreamWaitEvent(plan->slice_stream[i], plan->slice_fork, 0), "slice fork wait");
+        }
+    }
     if (plan->phase_events) BL_HIP(hipEventRecord(plan->ev_start, stream), "phase event");
     for (int l = 0; l < kLayers; ++l) {
-        // every layer after the first reads the previous layer's complete output from y
-        if ((st = enqueue_projection(plan, l, l == 0 ? x : y, plan->gates, stream)) != BILSTM_OK) return st;
-        if (plan->phase_events) BL_HIP(hipEventRecord(plan->ev_proj[l], stream), "phase event");
-        if ((st = enqueue_recurrence(plan, l, plan->gates, y, base + l * plan->steps, stream, true)) != BILSTM_OK) {
-            return st;
+        for (int i = 0; i < slices; ++i) {
+            // slice i holds windows [w0, w1); its chain runs on its own stream
+            const uint32_t w0 = static_cast<uint32_t>(i) * info.slice_windows;
+            const uint32_t w1 = std::min<uint32_t>(plan->batch, w0 + info.slice_windows);
+            hipStream_t on = i > 0 ? plan->slice_stream[i] : stream;
+            // The first projections run one slice after another, so the slices' recurrences
+            // start staggered and each later projection meets recurrences, not projections.
+            if (slices > 1 && l == 0 && i > 0) {
+                BL_HIP(hipStreamWaitEvent(on, plan->slice_first[i - 1], 0), "slice stagger");
+            }
+            // every layer after the first reads the previous layer's complete output from y
+            if ((st = enqueue_projection(plan, l, l == 0 ? x : y, plan->gates, on,
+                                         static_cast<size_t>(w0) * plan->steps,
+                                         static_cast<size_t>(w1 - w0) * plan->steps,
+                                         slices > 1 ? plan->proj_workgroups_sliced : plan->proj_workgroups)) !=
+                BILSTM_OK) {
+                return st;
+            }
+            if (slices > 1 && l == 0) BL_HIP(hipEventRecord(plan->slice_first[i], on), "slice stagger");
+            if (plan->phase_events && i == 0) BL_HIP(hipEventRecord(plan->ev_proj[l], on), "phase event");
+            const int t0 = static_cast<int>(w0 / info.recur_tile);
+            const int t1 = static_cast<int>((w1 + info.recur_tile - 1) / info.recur_tile);
+            if ((st = enqueue_recurrence(plan, l, plan->gates, y, base + l * plan->steps, on, i == 0, t0, t1)) !=
+                BILSTM_OK) {
+                return st;
+            }
+            if (plan->phase_events && i == 0) BL_HIP(hipEventRecord(plan->ev_recur[l], on), "phase event");
         }
-        if (plan->phase_events) BL_HIP(hipEventRecord(plan->ev_recur[l], stream), "phase event");
+    }
+    if (slices > 1) {
+        // join: the caller's stream waits for every other slice
+        for (int i = 1; i < slices; ++i) {
+            BL_HIP(hipEventRecord(plan->slice_join[i], plan->slice_stream[i]), "slice join");
+            BL_HIP(hipStreamWaitEvent(stream, plan->slice_join[i], 0), "slice join wait");
+        }
     }
     plan->phases_recorded = plan->phase_events;
     return BILSTM_OK;
@@ -438,7 +521,8 @@ bilstm_status bilstm_project(bilstm_plan *plan, int layer, const float *x, size_
     if ((st = check_len("project gates", plan->rows * kGateCols, gates_len)) != BILSTM_OK) return st;
     DeviceScope scope(plan->device);
     BL_HIP(scope.error(), "project: hipSetDevice");
-    return enqueue_projection(plan, layer, x, gates, static_cast<hipStream_t>(stream_ptr));
+    return enqueue_projection(plan, layer, x, gates, static_cast<hipStream_t>(stream_ptr), 0, plan->rows,
+                              plan->proj_workgroups);
 }
 
 bilstm_status bilstm_recur(bilstm_plan *plan, int layer, const float *gates, size_t gates_len,
@@ -453,7 +537,7 @@ bilstm_status bilstm_recur(bilstm_plan *plan, int layer, const float *gates, siz
     BL_HIP(scope.error(), "recur: hipSetDevice");
     uint32_t base = 0;
     if ((st = reserve_flags(plan, plan->steps, stream, &base)) != BILSTM_OK) return st;
-    return enqueue_recurrence(plan, layer, gates, y, base, stream, false);
+    return enqueue_recurrence(plan, layer, gates, y, base, stream, false, 0, plan->info.recur_tiles);
 }
 
 bilstm_status bilstm_plan_get_info(const bilstm_plan *plan, bilstm_plan_info *info) {

@@ -8,46 +8,57 @@
 // [1024][kpad] (row d·512 + 4j + g, zero padded to kpad), bias [1024] = Wb + Rb.
 //
 // Design for CDNA4:
-//  * 128x128 output tile per 256-thread workgroup, 4 waves of 64x64, each a 4x4 grid of
-//    v_mfma_f32_16x16x4_f32 tiles (FP32 in, FP32 accumulate).
-//  * K steps of 32 staged through LDS, double buffered. Both operands are stored K-major per
-//    row with a 36-float stride, so a ds_read_b128 of 8 consecutive rows touches 32 distinct
-//    banks.
-//  * Inside one MFMA the K slots are permuted: lane group g (lanes 16g..16g+15) supplies
-//    k = k0 + 4g + e in the e-th of four consecutive MFMAs, so each lane fetches four
-//    consecutive K values of its row with one ds_read_b128. A and B use the same
-//    permutation, so the product is unchanged.
-//  * Workgroup ids are remapped so each XCD (ids congruent mod 8) runs a contiguous run of
-//    tiles: the eight column tiles of a row block share that XCD's L2 for their A rows.
-//  * The per-row K order is fixed and independent of the row's position, so a row's gates
-//    are bitwise the same whatever the batch.
+//  * Persistent: one 256-thread workgroup per CU (its registers and LDS keep a second one
+//    out) walks the 128x128 output tiles q = wq, wq + grid, ... The walk is XCD-ordered: the
+//    ids congruent mod 8 run on one XCD, and the workgroups of one XCD take consecutive tiles,
+//    so the eight column tiles of a row block are computed on the same XCD and share its L2
+//    for their x rows.
+//  * Four waves of 64x64, each a 2x2 grid of v_mfma_f32_32x32x2_f32 blocks (FP32 in, FP32
+//    accumulate in AGPRs). The 32x32x2 form keeps the matrix pipe busy with one wave per SIMD
+//    and few independent accumulators (measured 147 TFLOP/s in a pure MFMA loop).
+//  * K steps of 32 staged through LDS, double buffered, with a 36-float row stride
+//    (conflict-free ds_read_b128). Inside an MFMA group of four, lane half h supplies
+//    k = k0 + 4h + e in the e-th MFMA, so every lane fetches four consecutive K values of its
+//    row with one ds_read_b128; A and B use the same permutation, so the product is unchanged.
+//    Fragments of the next group are read while the current group's MFMAs run.
+//  * The next tile's first K step is loaded during the current tile's last one.
+//  * Output: a finished tile's sums (plus bias) stay in registers and are written out in
+//    chunks during the next tile's K steps, so the stores overlap compute instead of leaving
+//    the matrix pipe idle while every tile of a round drains at once. In the 32x32 output
+//    layout one store instruction writes two full 128-byte row segments.
+//  * Every row's K order is fixed and independent of the row's position and of the grid, so a
+//    row's gates are bitwise the same whatever the batch or the number of workgroups.
+#include <algorithm>
+
 #include "bilstm_internal.h"
 
 namespace bl {
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int BM = kProjTileM;
 constexpr int BN = kProjTileN;
 constexpr int BK = kProjTileK;
-constexpr int kStride = BK + 4;                    // LDS row stride, floats
+constexpr int kStride = BK + 4;                              // LDS row stride, floats
+constexpr int kThreadsPerRow = BK / 4;                       // float4 loads along K per row
 constexpr int kLoadsPerThread = BM * BK / 4 / kProjThreads;  // float4 per operand per thread
+constexpr int kGroups = BK / 8;                              // MFMA groups (K = 8 each) per K step
 
 static_assert(BM == 128 && BN == 128 && BK == 32 && kProjThreads == 256, "tile shape");
 static_assert(kLoadsPerThread == 4, "loads per thread");
+static_assert(2 * 2 * BM * kStride * sizeof(float) == kProjLdsBytes, "LDS size");
 
-__global__ __launch_bounds__(kProjThreads) void projection_kernel(ProjArgs a) {
+template <int KSTEPS>
+__global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a) {
     __shared__ __attribute__((aligned(16))) float lds_a[2][BM * kStride];
     __shared__ __attribute__((aligned(16))) float lds_b[2][BN * kStride];
 
     const int nwg = gridDim.x;  // a multiple of 8
-    const int wg = blockIdx.x;
-    const int tile = (wg & 7) * (nwg >> 3) + (wg >> 3);
-    if (tile >= a.tiles) return;
+    const int per_xcd = nwg >> 3;
+    const int first = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     constexpr int kColTiles = kGateCols / BN;
-    const int m0 = (tile / kColTiles) * BM;
-    const int n0 = (tile % kColTiles) * BN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -55,14 +66,14 @@ __global__ __launch_bounds__(kProjThreads) void projection_kernel(ProjArgs a) {
     const int wm = wave >> 1;
     const int wn = wave & 1;
 
+    // ---- global -> registers -> LDS staging of one K step -----------------------------------
     v4f ra[kLoadsPerThread], rb[kLoadsPerThread];
-
-    auto load_tiles = [&](int k0) {
+    auto load = [&](int m0, int n0, int k0) {
 #pragma unroll
         for (int j = 0; j < kLoadsPerThread; ++j) {
             const int f = tid + kProjThreads * j;
-            const int row = f >> 3;
-            const int k = k0 + (f & 7) * 4;
+            const int row = f / kThreadsPerRow;
+            const int k = k0 + (f % kThreadsPerRow) * 4;
             const int m = m0 + row;
             v4f va = {0.f, 0.f, 0.f, 0.f};
             if (m < a.rows && k < a.in) {
@@ -72,78 +83,139 @@ __global__ __launch_bounds__(kProjThreads) void projection_kernel(ProjArgs a) {
             rb[j] = *reinterpret_cast<const v4f *>(a.w + static_cast<size_t>(n0 + row) * a.kpad + k);
         }
     };
-    auto store_tiles = [&](int buf) {
+    auto store = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < kLoadsPerThread; ++j) {
             const int f = tid + kProjThreads * j;
-            const int row = f >> 3;
-            const int c = (f & 7) * 4;
-            *reinterpret_cast<v4f *>(&lds_a[buf][row * kStride + c]) = ra[j];
-            *reinterpret_cast<v4f *>(&lds_b[buf][row * kStride + c]) = rb[j];
+            const int off = (f / kThreadsPerRow) * kStride + (f % kThreadsPerRow) * 4;
+            *reinterpret_cast<v4f *>(&lds_a[buf][off]) = ra[j];
+            *reinterpret_cast<v4f *>(&lds_b[buf][off]) = rb[j];
         }
     };
 
-    v4f acc[4][4];
+    // ---- MFMA fragments: lane l holds row l % 32 of a 32-row block, K quarter 4·(l / 32) ----
+    const int frag_row = lane & 31;
+    const int frag_k = (lane >> 5) * 4;
+    auto frags = [&](int buf, int g, v4f (&af)[2], v4f (&bf)[2]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    const int ksteps = a.kpad / BK;
-    load_tiles(0);
-    store_tiles(0);
-    __syncthreads();
-
-    const int frag_row = lane & 15;
-    const int frag_k = (lane >> 4) * 4;
-    for (int kt = 0; kt < ksteps; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < ksteps) load_tiles((kt + 1) * BK);
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            v4f af[4], bf[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                af[t] = *reinterpret_cast<const v4f *>(
-                    &lds_a[cur][(wm * 64 + t * 16 + frag_row) * kStride + ks * 16 + frag_k]);
-                bf[t] = *reinterpret_cast<const v4f *>(
-                    &lds_b[cur][(wn * 64 + t * 16 + frag_row) * kStride + ks * 16 + frag_k]);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-                    for (int tj = 0; tj < 4; ++tj)
-                        acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[ti][e], bf[tj][e],
-                                                                          acc[ti][tj], 0, 0, 0);
+        for (int t = 0; t < 2; ++t) {
+            af[t] = *reinterpret_cast<const v4f *>(
+                &lds_a[buf][(wm * 64 + t * 32 + frag_row) * kStride + g * 8 + frag_k]);
+            bf[t] = *reinterpret_cast<const v4f *>(
+                &lds_b[buf][(wn * 64 + t * 32 + frag_row) * kStride + g * 8 + frag_k]);
         }
-        if (kt + 1 < ksteps) store_tiles(cur ^ 1);
-        __syncthreads();
+    };
+
+    // ---- output of the previous tile, written during the current one ----------------------
+    // 32x32 block layout: register r of lane l is row 8·(r / 4) + 4·(l / 32) + r % 4, column
+    // l % 32 of the block.
+    float pend[2][2][16];
+    int pm0 = 0, pn0 = 0;
+    bool have = false;
+    auto put = [&](int i, int j, int r) {
+        const int m = pm0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int n = pn0 + wn * 64 + j * 32 + (lane & 31);
+        if (m < a.rows) a.gates[static_cast<size_t>(m) * kGateCols + n] = pend[i][j][r];
+    };
+    constexpr int kChunk = 64 / KSTEPS;  // pending values written per K step
+    auto put_chunk = [&](int s) {
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+            const int idx = s * kChunk + c;
+            put(idx >> 5, (idx >> 4) & 1, idx & 15);
+        }
+    };
+
+    int q = first;
+    int base = 0;  // LDS buffer of the tile's first K step
+    if (q < a.tiles) {
+        load((q / kColTiles) * BM, (q % kColTiles) * BN, 0);
+        store(0);
     }
+    __syncthreads();
+    v4f af[2][2], bf[2][2];
+    frags(0, 0, af[0], bf[0]);
 
-    // Epilogue: lane l of a 16x16 MFMA tile holds rows 4·(l/16) + r, r = 0..3, column l % 16.
+    for (; q < a.tiles; q += nwg) {
+        const int m0 = (q / kColTiles) * BM;
+        const int n0 = (q % kColTiles) * BN;
+        const int qn = q + nwg;
+        const bool next = qn < a.tiles;
+
+        v16f acc[2][2];
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj) {
-        const int n = n0 + wn * 64 + tj * 16 + (lane & 15);
-        const float bv = a.bias[n];
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + wm * 64 + ti * 16 + (lane >> 4) * 4 + r;
-                if (m < a.rows) a.gates[static_cast<size_t>(m) * kGateCols + n] = acc[ti][tj][r] + bv;
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+#pragma unroll
+        for (int kt = 0; kt < KSTEPS; ++kt) {
+            const int cur = (base + kt) & 1;
+            const bool more = kt + 1 < KSTEPS;
+            // the next K step of this tile, or the first K step of the next tile
+            if (more) {
+                load(m0, n0, (kt + 1) * BK);
+            } else if (next) {
+                load((qn / kColTiles) * BM, (qn % kColTiles) * BN, 0);
             }
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g) {
+                const int p = g & 1;
+                if (g + 1 < kGroups) frags(cur, g + 1, af[p ^ 1], bf[p ^ 1]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[p][i][e], bf[p][j][e],
+                                                                             acc[i][j], 0, 0, 0);
+                if (g == kGroups / 2 && have) put_chunk(kt);
+            }
+            if (more || next) store(cur ^ 1);
+            __syncthreads();
+            if (more || next) frags(cur ^ 1, 0, af[0], bf[0]);
         }
+
+        // this tile's sums plus bias become the pending output of the next tile
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float bv = a.bias[n0 + wn * 64 + j * 32 + (lane & 31)];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) pend[i][j][r] = acc[i][j][r] + bv;
+        }
+        pm0 = m0;
+        pn0 = n0;
+        have = true;
+        base = (base + KSTEPS) & 1;
+    }
+    if (have) {
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) put_chunk(s);
     }
 }
 
 }  // namespace
 
-hipError_t launch_projection(const ProjArgs &args, hipStream_t stream) {
+hipError_t launch_projection(const ProjArgs &args, int workgroups, hipStream_t stream) {
     if (args.tiles <= 0) return hipSuccess;
-    const int nwg = (args.tiles + 7) / 8 * 8;
-    hipLaunchKernelGGL(projection_kernel, dim3(nwg), dim3(kProjThreads), 0, stream, args);
+    // a multiple of 8 (the XCD-ordered walk), at most one workgroup per tile group of 8
+    int nwg = std::min(workgroups, (args.tiles + 7) / 8 * 8);
+    nwg = std::max(8, nwg / 8 * 8);
+    switch (args.kpad / kProjTileK) {
+        case 2:
+            hipLaunchKernelGGL(projection_kernel<2>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
+            break;
+        case 8:
+            hipLaunchKernelGGL(projection_kernel<8>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

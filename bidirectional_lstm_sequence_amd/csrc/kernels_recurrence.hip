@@ -296,17 +296,18 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
                 // (4) gather the other workgroups' h of step s
                 constexpr int kOthers = (kHidden - U) * BT;
                 const unsigned long long *xs = xdir + static_cast<size_t>(cur) * kHidden * BT;
+                const unsigned int expect = flag + a.flag_skew;
                 for (int idx = tid - 64; idx < kOthers; idx += NT - 64) {
                     const int uo = idx / BT;
                     const int b = idx - uo * BT;
                     const int ugo = uo < member * U ? uo : uo + U;
                     const unsigned long long *wp = xs + static_cast<size_t>(ugo) * BT + b;
                     unsigned long long w = load_word(wp);
-                    if (static_cast<unsigned int>(w >> 32) != flag && !timed_out) {
+                    if (static_cast<unsigned int>(w >> 32) != expect && !timed_out) {
                         const unsigned long long t0 = wall_clock64();
                         while (true) {
                             w = load_word(wp);
-                            if (static_cast<unsigned int>(w >> 32) == flag) break;
+                            if (static_cast<unsigned int>(w >> 32) == expect) break;
                             if (wall_clock64() - t0 > a.timeout_ticks) {
                                 atomicOr(a.error, 1u);
                                 timed_out = true;
@@ -387,11 +388,17 @@ __global__ void exchange_probe_kernel(unsigned long long *words, int partner, in
 }
 
 template <int KG, int BT>
-hipError_t launch_typed(const RecurArgs &args, int directions, hipStream_t stream) {
+hipError_t launch_typed(const RecurArgs &args, int directions, size_t lds, hipStream_t stream) {
     const int nwg = KG == 1 ? args.tile_count : (args.tile_count + 7) / 8 * 8 * KG;
-    hipLaunchKernelGGL((recurrence_kernel<KG, BT>), dim3(nwg, directions), dim3(recur_threads(KG)), 0,
+    hipLaunchKernelGGL((recurrence_kernel<KG, BT>), dim3(nwg, directions), dim3(recur_threads(KG)), lds,
                        stream, args);
     return hipGetLastError();
+}
+
+template <int KG, int BT>
+hipError_t allow_lds_typed(size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&recurrence_kernel<KG, BT>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
 }
 
 template <int KG, int BT>
@@ -404,10 +411,18 @@ hipError_t occupancy_typed(int *per_cu) {
 }  // namespace
 
 hipError_t launch_recurrence(int groups, int tile, const RecurArgs &args, int directions,
-                             hipStream_t stream) {
+                             size_t dynamic_lds, hipStream_t stream) {
     if (args.tile_count <= 0) return hipSuccess;
 #define BL_CASE(KG, BT) \
-    if (groups == KG && tile == BT) return launch_typed<KG, BT>(args, directions, stream);
+    if (groups == KG && tile == BT) return launch_typed<KG, BT>(args, directions, dynamic_lds, stream);
+    BL_FOR_EACH_SPLIT(BL_CASE)
+#undef BL_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t recurrence_allow_lds(int groups, int tile, size_t bytes) {
+#define BL_CASE(KG, BT) \
+    if (groups == KG && tile == BT) return allow_lds_typed<KG, BT>(bytes);
     BL_FOR_EACH_SPLIT(BL_CASE)
 #undef BL_CASE
     return hipErrorInvalidValue;

@@ -87,11 +87,21 @@ typedef struct {
                              0 serially on the caller's stream, 1 reverse on the
                              plan's side stream joined back by events, 2 both directions in one
                              launch on the caller's stream */
-    int32_t watchdog_us;  /* bound of one recurrence wait in microseconds; 0 = 2 s; -1 = give
-                             up on the first unsuccessful poll (for failure-handling tests).
-                             A wait that hits it sets the plan's error flag (bilstm_check) and
-                             stops waiting */
-    int32_t reserved[4];  /* must be zero */
+    int32_t watchdog_us;  /* bound of one recurrence wait in microseconds; 0 = 2 s; -1 =
+                             forced timeout for failure-handling tests: every exchange wait
+                             expects a flag no producer writes and gives up on its first poll.
+                             A wait that hits its bound sets the plan's error flag
+                             (bilstm_check) and stops waiting; the kernels still finish */
+    int32_t slices;       /* batch slices for bilstm_forward: the windows are cut into this many
+                             contiguous slices, each run as its own chain of layers on its own
+                             stream, so one slice's projection overlaps other slices'
+                             recurrences on the CUs the recurrence leaves idle. Windows are
+                             independent, so the output does not depend on it (bitwise).
+                             0 = auto (2 when the recurrence leaves at least half of the CUs
+                             idle, else 1), 1 = off, at most 8 (beyond the process's hardware
+                             queues, 4 by default, streams share queues and run one after
+                             another); needs recur_groups = 1 and concurrent != 1 */
+    int32_t reserved[3];  /* must be zero */
 } bilstm_options;
 
 /* What a plan chose; filled by bilstm_plan_get_info. */
@@ -109,6 +119,8 @@ typedef struct {
     int32_t cu_count;        /* compute units of the device */
     int32_t recur_capacity;  /* recurrence workgroups the device keeps resident at once */
     uint64_t device_bytes;   /* device memory the plan owns */
+    int32_t slices;          /* batch slices bilstm_forward runs as concurrent chains */
+    int32_t slice_windows;   /* windows per slice (the last slice may hold fewer) */
 } bilstm_plan_info;
 
 /*

@@ -183,6 +183,18 @@ def test_stack_bit_stable_and_batch_invariant(bl):
     assert np.array_equal(y8.view(np.uint32), runs[0][:8].view(np.uint32))
 
 
+@pytest.mark.parametrize("name,steps,slices", [("b8", 200, 2), ("b8", 200, 3), ("b32", 150, 4), ("b32", 150, 8)])
+def test_batch_slices_agree_bitwise(bl, name, steps, slices):
+    """Windows are independent, so running the batch as concurrent slices changes nothing."""
+    x, layers = workloads.make_workload(name)
+    xs = np.ascontiguousarray(x[:, :steps])
+    note(f"batch slices {name} steps={steps} slices={slices}")
+    got, info = run_stack(bl, xs, layers, slices=slices)
+    base, binfo = run_stack(bl, xs, layers, slices=1)
+    assert binfo["slices"] == 1 and info["slices"] == min(slices, xs.shape[0])
+    assert np.array_equal(got.view(np.uint32), base.view(np.uint32))
+
+
 @pytest.mark.parametrize("concurrent", [0, 1, 2])
 def test_direction_modes_agree(bl, concurrent):
     x, layers = workloads.make_workload("b8")
@@ -221,9 +233,9 @@ def test_time_reversal_layer0_bitwise(bl):
 
 @pytest.mark.parametrize("concurrent", [0, 2])
 def test_watchdog_reports_timeout_and_grid_drains(bl, concurrent):
-    """Exchange waits that give up on their first unsuccessful poll (forced from the host):
-    the kernels still finish, and the plan reports BILSTM_TIMEOUT instead of hanging. The
-    first step's waits always miss at least once (the producers are still loading R)."""
+    """Exchange waits forced to time out from the host (watchdog_us = -1: each wait expects a
+    flag no producer writes and gives up on its first poll): the kernels still finish, and
+    the plan reports BILSTM_TIMEOUT instead of hanging."""
     x, layers = workloads.make_workload("b8")
     xs = np.ascontiguousarray(x[:, :64])
     note(f"watchdog first-miss groups=4 concurrent={concurrent}")

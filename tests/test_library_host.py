@@ -121,9 +121,35 @@ def test_schedule_refuses_concurrency_that_cannot_be_resident(bl):
     assert s["concurrent"] == 0 and s["recur_launches"] == 4
 
 
+@pytest.mark.parametrize("batch", [1, 2, 5, 8, 31, 32, 64, 100, 256])
+@pytest.mark.parametrize("slices", [0, 1, 2, 3, 4, 8])
+def test_schedule_slices_cover_the_batch(bl, batch, slices):
+    """Slices are whole tiles, cover every window once, and the auto choice slices only when
+    the recurrence leaves at least half of the CUs idle."""
+    s = bl.schedule(batch, 589, 256, 1, slices=slices)
+    n, w, tile = s["slices"], s["slice_windows"], s["recur_tile"]
+    assert 1 <= n <= max(1, slices if slices else 2)
+    assert w % tile == 0 or w == batch
+    assert (n - 1) * w < batch <= n * w
+    if slices == 0:
+        idle_half = 4 * s["recur_tiles"] * s["recur_groups"] <= 256
+        assert (n > 1) == (idle_half and batch >= 2 * tile)
+
+
+def test_schedule_slices_need_single_workgroup_tiles(bl):
+    for kwargs in (dict(groups=2), dict(concurrent=1)):
+        with pytest.raises(bl.BilstmError) as e:
+            bl.schedule(32, 589, 256, 1, slices=4, **kwargs)
+        assert e.value.name == "BILSTM_UNSUPPORTED"
+        assert bl.schedule(32, 589, 256, 1, **kwargs)["slices"] == 1
+    assert bl.schedule(32, 589, 256, 1)["slices"] == 2
+    assert bl.schedule(256, 589, 256, 1)["slices"] == 1
+
+
 @pytest.mark.parametrize("kwargs,status", [
     (dict(groups=3), "BILSTM_UNSUPPORTED"), (dict(tile=3), "BILSTM_UNSUPPORTED"),
-    (dict(concurrent=5), "BILSTM_INVALID_ARGUMENT")])
+    (dict(concurrent=5), "BILSTM_INVALID_ARGUMENT"), (dict(slices=9), "BILSTM_INVALID_ARGUMENT"),
+    (dict(slices=-1), "BILSTM_INVALID_ARGUMENT")])
 def test_schedule_rejects_bad_options(bl, kwargs, status):
     with pytest.raises(bl.BilstmError) as e:
         bl.schedule(8, 589, 256, 1, **kwargs)
