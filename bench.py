@@ -66,7 +66,7 @@ def recorded_traffic(workload: str, info: dict):
         return None
     if (rec.get("source_sha256") != kernel_source_digest() or rec.get("workload") != workload
             or rec.get("concurrent") != info["concurrent"] or rec.get("groups") != info["recur_groups"]
-            or rec.get("tile") != info["recur_tile"]):
+            or rec.get("tile") != info["recur_tile"] or rec.get("slices") != info["slices"]):
         return None
     return {"bytes_per_launch": rec["fetch_bytes"] + rec["write_bytes"], "fetch_bytes": rec["fetch_bytes"],
             "write_bytes": rec["write_bytes"], "source": "profiles/recurrence_traffic.json"}
