@@ -74,6 +74,10 @@ def _load():
         f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, fp, fp, fp, fp,
                       rp, rp]
         f.restype = ctypes.c_int
+        f = getattr(lib, f"oracle_heads_{suffix}")
+        f.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                      ctypes.c_double, fp, rp, fp, fp, fp, fp, fp, fp, rp]
+        f.restype = ctypes.c_int
     _libs[path] = lib
     return lib
 
@@ -175,3 +179,32 @@ def stack(x: np.ndarray, layers, precision: str = "f64", threads: int = 1,
         with ThreadPoolExecutor(max_workers=threads) as pool:
             outs = list(pool.map(lambda b: stack_window(x[b], layers, precision, _flat=flat), idx))
     return np.stack(outs) if outs else np.empty((0,) + (x.shape[1], 2 * layers[0]["r"].shape[2]))
+
+
+def heads(y: np.ndarray, head: dict, precision: str = "f64") -> np.ndarray:
+    """The segmentation heads over ``y [rows, in]`` -> log-probabilities ``[rows, classes]``.
+
+    ``head`` holds float32 ``w0 [in, mid0]``, ``b0 [mid0]``, ``w1 [mid0, mid1]``, ``b1``,
+    ``w2 [mid1, classes]``, ``b2`` (row-major [k][n]) and ``slope`` (LeakyReLU). ``y`` may be
+    float32 (the library's output) or float64 (the oracle's own stack output).
+    """
+    lib = _load()
+    dt, ct = _real(precision)
+    w0, b0, w1, b1, w2, b2 = (_f32(head[k]) for k in ("w0", "b0", "w1", "b1", "w2", "b2"))
+    rows, width = y.shape
+    mid0, mid1, classes = w0.shape[1], w1.shape[1], w2.shape[1]
+    if w0.shape[0] != width or w1.shape[0] != mid0 or w2.shape[0] != mid1:
+        raise ValueError("head weight shapes do not chain")
+    out = np.empty((rows, classes), dtype=dt)
+    fn = getattr(lib, f"oracle_heads_{precision}")
+    if y.dtype == np.float32:
+        yf, yr = _f32(y), None
+    else:
+        yf, yr = None, np.ascontiguousarray(y, dtype=dt)
+    rc = fn(rows, width, mid0, mid1, classes, float(head["slope"]),
+            _ptr(yf, ctypes.c_float) if yf is not None else None,
+            _ptr(yr, ct) if yr is not None else None,
+            *(_ptr(a, ctypes.c_float) for a in (w0, b0, w1, b1, w2, b2)), _ptr(out, ct))
+    if rc != 0:
+        raise RuntimeError(f"oracle_heads failed ({rc})")
+    return out

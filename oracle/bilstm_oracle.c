@@ -19,9 +19,14 @@
  *   *_f64  double accumulation, activations and inter-layer values: the reference.
  *   *_f32  float throughout: diagnostic, to show the intrinsic fp32 noise floor.
  *
+ * The segmentation heads after the stack (the `segdense.rs` page: linear0, linear1 and the
+ * classifier with their LeakyReLU and log-softmax epilogues) are in the same body.
+ *
  * Pins (tests/test_oracle_pins.py): a hand-derived one-unit closed form, agreement with
  * torch.nn.LSTM in float64, |h| < 1, the R = 0 scan closed form and per-step independence
- * with the forget gate off, and time-reversal symmetry with the directions swapped.
+ * with the forget gate off, and time-reversal symmetry with the directions swapped; for the
+ * heads, a hand-derived one-unit case, agreement with torch's linear / leaky_relu /
+ * log_softmax in float64, normalisation and shift invariance of the log-softmax.
  */
 #include <math.h>
 #include <stdlib.h>
@@ -30,19 +35,23 @@
 #define REAL double
 #define EXPR exp
 #define TANHR tanh
+#define LOGR log
 #define NAME(x) x##_f64
 #include "lstm_body.inc"
 #undef REAL
 #undef EXPR
 #undef TANHR
+#undef LOGR
 #undef NAME
 
 #define REAL float
 #define EXPR expf
 #define TANHR tanhf
+#define LOGR logf
 #define NAME(x) x##_f32
 #include "lstm_body.inc"
 #undef REAL
 #undef EXPR
 #undef TANHR
+#undef LOGR
 #undef NAME

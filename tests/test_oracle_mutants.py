@@ -29,6 +29,13 @@ MUTANTS = {
                                             "for (int j = 0; j < hidden && d == 0; ++j) {\n            h[j] = (REAL)0;"),
     "input projection transposed": ("acc += (REAL)wrow[k] * xv;",
                                     "acc += (REAL)w[((size_t)d * gates + (k % gates)) * in + (r % in)] * xv;"),
+    "heads: ReLU instead of LeakyReLU": ("return v >= (REAL)0 ? v : slope * v;", "return v >= (REAL)0 ? v : (REAL)0;"),
+    "heads: no LeakyReLU after linear1": ("h1[n] = NAME(leaky)(acc, s);", "h1[n] = acc;"),
+    "heads: linear1 weight transposed": ("acc += h0[k] * (REAL)w1[(size_t)k * mid1 + n];",
+                                         "acc += h0[k] * (REAL)w1[(size_t)n * mid0 + k];"),
+    "heads: dropped classifier bias": ("REAL acc = (REAL)b2[c];", "REAL acc = (REAL)0;"),
+    "heads: softmax instead of log-softmax": ("out[(size_t)m * classes + c] = z[c] - lse;",
+                                              "out[(size_t)m * classes + c] = EXPR(z[c] - lse);"),
 }
 
 
@@ -40,6 +47,9 @@ def _pins_all_pass(lib_fixture) -> bool:
         lambda: pins.test_zero_recurrent_weights_scan_closed_form(lib_fixture),
         lambda: pins.test_time_reversal_symmetry(lib_fixture, 5, 3, 1, 11),
         lambda: pins.test_projection_matches_numpy_matmul(lib_fixture),
+        lambda: pins.test_heads_one_unit_closed_form(lib_fixture),
+        lambda: pins.test_heads_match_torch_float64(lib_fixture, 64, (16, 8, 12, 7)),
+        lambda: pins.test_heads_log_softmax_normalised_and_shift_invariant(lib_fixture),
     ]
     for check in checks:
         try:

@@ -264,3 +264,56 @@ def test_batch_windows_are_independent(oracle_lib):
     ya = oracle_lib.stack(xs, layers, threads=4)
     yb = oracle_lib.stack(xs, layers, windows=[5, 2])
     np.testing.assert_array_equal(ya[[5, 2]], yb)
+
+
+# ---- segmentation heads (the `segdense.rs` page: linear0, linear1, classifier) -------------
+
+def _head_case():
+    with open(os.path.join(GOLDEN, "heads_one_unit_case.json")) as f:
+        case = json.load(f)
+    head = {k: np.array(case[k], np.float32) for k in ("w0", "b0", "w1", "b1", "w2", "b2")}
+    head["slope"] = case["slope"]
+    return head, np.array(case["y"], np.float32).reshape(1, 1)
+
+
+def test_heads_one_unit_closed_form(oracle_lib):
+    """y = -2 falls on LeakyReLU's negative branch (h0 = 0.01 * -2 = -0.02), then
+    h1 = 3 * -0.02 + 0.5 = 0.44 and z = (0.44, -0.44), whose log-softmax is
+    z - log(e^0.44 + e^-0.44) = z - log(2 cosh 0.44)."""
+    head, y = _head_case()
+    out = oracle_lib.heads(y, head)
+    lse = math.log(2.0 * math.cosh(0.44))
+    np.testing.assert_allclose(out[0], [0.44 - lse, -0.44 - lse], rtol=0, atol=1e-7)
+
+
+def torch_heads(y: np.ndarray, head: dict) -> np.ndarray:
+    """torch.nn.functional linear / leaky_relu / log_softmax in float64 with the same weights."""
+    import torch.nn.functional as F
+    t = torch.from_numpy(y.astype(np.float64))
+    for i in range(3):
+        w = torch.from_numpy(head[f"w{i}"].astype(np.float64))  # [k, n]
+        b = torch.from_numpy(head[f"b{i}"].astype(np.float64))
+        t = F.linear(t, w.T.contiguous(), b)
+        if i < 2:
+            t = F.leaky_relu(t, negative_slope=head["slope"])
+    return F.log_softmax(t, dim=-1).numpy()
+
+
+@pytest.mark.parametrize("rows,sizes", [(5, (3, 4, 5, 2)), (64, (16, 8, 12, 7)), (600, workloads.HEAD_SIZES)])
+def test_heads_match_torch_float64(oracle_lib, rows, sizes):
+    head = workloads.make_heads(77 + rows, sizes=sizes)
+    y = np.random.default_rng(rows).uniform(-1, 1, size=(rows, sizes[0])).astype(np.float32)
+    np.testing.assert_allclose(oracle_lib.heads(y, head), torch_heads(y, head), rtol=0, atol=1e-12)
+
+
+def test_heads_log_softmax_normalised_and_shift_invariant(oracle_lib):
+    head = workloads.make_heads(5)
+    # classifier bias on a 2^-12 grid, so adding 3 to it is exact in float32
+    head["b2"] = (np.round(head["b2"] * 4096.0) / 4096.0).astype(np.float32)
+    y = np.random.default_rng(6).uniform(-1, 1, size=(300, 256)).astype(np.float32)
+    out = oracle_lib.heads(y, head)
+    assert np.all(out <= 0.0)
+    np.testing.assert_allclose(np.exp(out).sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    shifted = dict(head, b2=(head["b2"] + np.float32(3.0)).astype(np.float32))
+    assert np.array_equal(shifted["b2"].astype(np.float64) - 3.0, head["b2"].astype(np.float64))
+    np.testing.assert_allclose(oracle_lib.heads(y, shifted), out, rtol=0, atol=1e-12)

@@ -18,6 +18,11 @@ Weights follow PyTorch's `nn.LSTM` layout and default initialisation, U(-1/sqrt(
 
 Per layer the draws are taken in the order W, R, Wb, Rb (each covering both directions),
 then the input. No data set is involved: every workload here is synthetic.
+
+The segmentation heads that follow the stack (the `segdense.rs` page, `Site` doc: 256 to 128,
+128 to 128 and 128 to 7, weights row-major ``[k, n]``) draw from their own stream: ``w0``,
+``b0``, ``w1``, ``b1``, ``w2``, ``b2``, each ~ U(-1/sqrt(k), 1/sqrt(k)) (PyTorch's `nn.Linear`
+default), with LeakyReLU slope 0.01 (PyTorch's default; the page gives none).
 """
 
 from __future__ import annotations
@@ -124,4 +129,20 @@ def random_layers(seed: int, hidden: int, features: int, layers: int,
             "r": rng.uniform(-bound, bound, size=(2, gates, hidden)).astype(np.float32),
             "b": rng.uniform(-bound, bound, size=(2, 2, gates)).astype(np.float32),
         })
+    return out
+
+
+HEAD_SIZES = (256, 128, 128, 7)   # stack output, linear0, linear1, classes
+LEAKY_SLOPE = 0.01
+
+
+def make_heads(seed: int, sizes: tuple = HEAD_SIZES, slope: float = LEAKY_SLOPE) -> dict:
+    """Draw the heads' weights ``[k, n]`` and biases from ``seed + 2`` (own stream)."""
+    rng = np.random.default_rng(seed + 2)
+    out: dict = {"slope": slope}
+    for i in range(3):
+        k, n = sizes[i], sizes[i + 1]
+        bound = 1.0 / math.sqrt(k)
+        out[f"w{i}"] = np.ascontiguousarray(rng.uniform(-bound, bound, size=(k, n)).astype(np.float32))
+        out[f"b{i}"] = np.ascontiguousarray(rng.uniform(-bound, bound, size=(n,)).astype(np.float32))
     return out
