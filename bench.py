@@ -34,6 +34,9 @@ CLOCK_GHZ = 2.4
 FMA_PER_CLK_PER_CU = 128
 
 RECUR_FMA_PER_FRAME_DIR = 512 * 128                   # R·h per step per direction
+HEAD_FLOP_PER_FRAME = 2 * (256 * 128 + 128 * 128 + 128 * 7)   # segmentation heads
+HEAD_BYTES_PER_FRAME = 256 * 4 + 7 * 4                          # stack output read, log-probs written
+PEAK_HBM_GBS = 8000.0
 
 
 def projection_flops(frames: int) -> float:
@@ -190,6 +193,21 @@ def main() -> int:
     rec_med = [statistics.median(v) for v in rec_ms]
     plan.close()
 
+    # the fused segmentation heads after the stack, alone, on this workload's stack output
+    heads = bl.Heads(workloads.make_heads(wl.seed))
+    logp = torch.empty((wl.batch, wl.steps, 7), dtype=torch.float32, device="cuda")
+    heads_ms = []
+    for _ in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        heads.forward(yd, logp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        heads_ms.append(e0.elapsed_time(e1))
+    heads.close()
+    heads_med = statistics.median(heads_ms[1:])
+    heads_tflops = HEAD_FLOP_PER_FRAME * frames / (heads_med / 1e3) / 1e12
+
     # recurrence: the dominant kernel. Its achieved rate is the algorithmic FLOPs of one launch
     # over that launch's duration in the timed region (events on the stream it runs on).
     rec_tflops = flop_per_launch / (launch_dur_ms / 1e3) / 1e12
@@ -245,6 +263,11 @@ def main() -> int:
         "projection": {"ms_total": proj_total_ms, "ms_per_layer": proj_med, "achieved_tflops": proj_tflops,
                        "tflops_per_layer": proj_layer_tflops,
                        "peak_tflops": PEAK_FP32_MFMA_TFLOPS, "frac": proj_tflops / PEAK_FP32_MFMA_TFLOPS},
+        "heads": {"ms": heads_med, "achieved_tflops": heads_tflops, "peak_tflops": PEAK_FP32_MFMA_TFLOPS,
+                  "frac": heads_tflops / PEAK_FP32_MFMA_TFLOPS,
+                  "hbm_gbs": HEAD_BYTES_PER_FRAME * frames / (heads_med / 1e3) / 1e9,
+                  "note": "linear0 + LeakyReLU, linear1 + LeakyReLU, classifier + log-softmax, fused; "
+                          "not part of the timed step"},
         "kernels_alone_ms": {"projection": proj_med, "recurrence": rec_med},
         "phases_ms_first_slice": {"projection": timed_phases["projection_ms"],
                                   "recurrence": timed_phases["recurrence_ms"]},

@@ -31,7 +31,9 @@ STATUS = {0: "BILSTM_OK", 1: "BILSTM_INVALID_ARGUMENT", 2: "BILSTM_BUFFER_LENGTH
 EXPORTS = ["bilstm_plan_create", "bilstm_plan_create_ex", "bilstm_forward", "bilstm_project",
            "bilstm_recur", "bilstm_plan_get_info", "bilstm_check", "bilstm_set_phase_events",
            "bilstm_phase_times", "bilstm_destroy", "bilstm_last_error", "bilstm_pack_layer",
-           "bilstm_schedule", "bilstm_probe_exchange"]
+           "bilstm_schedule", "bilstm_probe_exchange", "bilstm_heads_create", "bilstm_heads_forward",
+           "bilstm_heads_destroy"]
+HEAD_IN, HEAD_MID, HEAD_CLASSES = 256, 128, 7
 
 
 class LibraryMissing(RuntimeError):
@@ -55,6 +57,16 @@ class Options(ctypes.Structure):
     _fields_ = [("recur_groups", ctypes.c_int32), ("recur_tile", ctypes.c_int32),
                 ("concurrent", ctypes.c_int32), ("watchdog_us", ctypes.c_int32),
                 ("slices", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+
+
+class HeadWeights(ctypes.Structure):
+    _fields_ = [("w0", ctypes.POINTER(ctypes.c_float)), ("w0_len", ctypes.c_size_t),
+                ("b0", ctypes.POINTER(ctypes.c_float)), ("b0_len", ctypes.c_size_t),
+                ("w1", ctypes.POINTER(ctypes.c_float)), ("w1_len", ctypes.c_size_t),
+                ("b1", ctypes.POINTER(ctypes.c_float)), ("b1_len", ctypes.c_size_t),
+                ("w2", ctypes.POINTER(ctypes.c_float)), ("w2_len", ctypes.c_size_t),
+                ("b2", ctypes.POINTER(ctypes.c_float)), ("b2_len", ctypes.c_size_t),
+                ("slope", ctypes.c_float)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -106,6 +118,9 @@ def library():
         "bilstm_probe_exchange": ([ctypes.c_int, ctypes.c_int, ctypes.c_int32,
                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32),
                                    ctypes.POINTER(ctypes.c_int32)], st),
+        "bilstm_heads_create": ([ctypes.c_int, ctypes.POINTER(HeadWeights), ctypes.POINTER(P)], st),
+        "bilstm_heads_forward": ([P, P, ctypes.c_size_t, P, ctypes.c_size_t, P], st),
+        "bilstm_heads_destroy": ([P], None),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -303,3 +318,47 @@ class Plan:
 def gate_column(direction: int, unit: int, gate: int) -> int:
     """Column of (direction, hidden unit, gate) in the packed gate buffer: d·512 + 4j + g."""
     return direction * GATES + 4 * unit + gate
+
+
+class Heads:
+    """The segmentation heads after the stack (linear0, linear1, classifier with LeakyReLU and
+    log-softmax), fused on the GPU.
+
+    ``head`` holds float32 ``w0 [256, 128]``, ``b0``, ``w1 [128, 128]``, ``b1``, ``w2 [128, 7]``,
+    ``b2`` (row-major ``[k, n]``) and ``slope``.
+    """
+
+    def __init__(self, head: dict, device: int = 0):
+        lib = library()
+        keep = [_f32(head[k]) for k in ("w0", "b0", "w1", "b1", "w2", "b2")]
+        hw = HeadWeights(*[v for a in keep for v in (_fptr(a), a.size)], ctypes.c_float(head["slope"]))
+        handle = ctypes.c_void_p()
+        _check(lib.bilstm_heads_create(device, ctypes.byref(hw), ctypes.byref(handle)))
+        self._lib = lib
+        self._h = handle
+        self.device = device
+
+    def forward(self, y, out=None, stream=None):
+        """y: [..., 256] float32 CUDA tensor (e.g. the stack's [B, T, 256]); returns [..., 7]."""
+        import torch
+        rows = y.numel() // HEAD_IN
+        if out is None:
+            out = torch.empty(tuple(y.shape[:-1]) + (HEAD_CLASSES,), dtype=torch.float32, device=y.device)
+        yp = _dev_ptr(y, "y", tuple(y.shape[:-1]) + (HEAD_IN,))
+        op = _dev_ptr(out, "out", tuple(y.shape[:-1]) + (HEAD_CLASSES,))
+        if rows == 0:
+            return out
+        _check(self._lib.bilstm_heads_forward(self._h, yp, rows * HEAD_IN, op, rows * HEAD_CLASSES,
+                                              _stream_handle(stream)))
+        return out
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.bilstm_heads_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

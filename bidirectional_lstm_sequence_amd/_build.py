@@ -13,8 +13,8 @@ LIB_NAME = "libbilstm_amd.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 OBJ_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["host_plan.cpp", "host_pack_schedule.cpp", "kernels_projection.hip",
-           "kernels_recurrence.hip"]
+SOURCES = ["host_plan.cpp", "host_pack_schedule.cpp", "host_heads.cpp", "kernels_projection.hip",
+           "kernels_recurrence.hip", "kernels_heads.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -73,7 +73,29 @@ struct RecurArgs {
     unsigned long long timeout_ticks;  // watchdog, in wall-clock ticks
 };
 
+// Segmentation heads after the stack: 256 -> 128 -> 128 -> 7 (class slots padded to 8).
+constexpr int kHeadIn = 256;
+constexpr int kHeadMid = 128;
+constexpr int kHeadClasses = 7;
+constexpr int kHeadClassSlots = 8;
+constexpr int kHeadTileRows = 64;
+constexpr int kHeadThreads = 256;
+
+struct HeadArgs {
+    const float *y;    // [rows][256]
+    float *out;        // [rows][7]
+    const float *w0t;  // [128][256]  linear0 weight transposed ([n][k])
+    const float *b0;   // [128]
+    const float *w1t;  // [128][128]
+    const float *b1;   // [128]
+    const float *w2t;  // [8][128]    classifier weight transposed, slot 7 zero
+    const float *b2;   // [7]
+    float slope;       // LeakyReLU negative slope
+    long rows;
+};
+
 // Launchers (kernels_*.hip). They return the launch's hipError_t.
+hipError_t launch_heads(const HeadArgs &args, hipStream_t stream);
 // The projection on `workgroups` persistent workgroups (one per CU; rounded to a multiple of 8).
 hipError_t launch_projection(const ProjArgs &args, int workgroups, hipStream_t stream);
 hipError_t launch_recurrence(int groups, int tile, const RecurArgs &args, int directions,

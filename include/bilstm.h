@@ -196,6 +196,52 @@ void bilstm_destroy(bilstm_plan *plan);
 /* Text of the last error recorded on the calling thread ("" if none). */
 const char *bilstm_last_error(void);
 
+/* ---- segmentation heads after the stack ------------------------------------------- */
+
+/*
+ * The segmentation model's dense heads that consume the stack's output (speakrs 0.6.0, page
+ * `segdense.rs`, `Site` doc and `dimensions()`), fused into one kernel:
+ *   h0  = LeakyReLU(y · W0 + b0)      W0 [256][128]  row-major [k][n], as the page's layout
+ *   h1  = LeakyReLU(h0 · W1 + b1)     W1 [128][128]
+ *   out = log_softmax(h1 · W2 + b2)   W2 [128][7], over each row's 7 classes
+ * The page gives no LeakyReLU slope; the caller passes it (PyTorch's default is 0.01).
+ * All pointers HOST, float32; the library copies and repacks them.
+ */
+typedef struct bilstm_heads bilstm_heads; /* opaque; created and owned by the library */
+
+typedef struct {
+    const float *w0;
+    size_t w0_len; /* 256·128 */
+    const float *b0;
+    size_t b0_len; /* 128 */
+    const float *w1;
+    size_t w1_len; /* 128·128 */
+    const float *b1;
+    size_t b1_len; /* 128 */
+    const float *w2;
+    size_t w2_len; /* 128·7 */
+    const float *b2;
+    size_t b2_len; /* 7 */
+    float slope;   /* LeakyReLU negative slope */
+} bilstm_head_weights;
+
+/* Pack the heads' weights onto HIP device `device` (gfx950 only; BILSTM_UNSUPPORTED else). */
+bilstm_status bilstm_heads_create(int device, const bilstm_head_weights *weights, bilstm_heads **out);
+
+/*
+ * The heads over every row of the stack's output:
+ *   y   [rows][256] device, fp32, 16-byte aligned; y_len = rows·256 (any rows >= 0; with
+ *                   rows = 0 the call does nothing and the pointers may be NULL)
+ *   out [rows][7]   device, fp32: log-probabilities; out_len = rows·7
+ * Asynchronous on `stream`; y and out must not overlap. A call may run concurrently with
+ * other calls on the same heads object (it owns no scratch).
+ */
+bilstm_status bilstm_heads_forward(bilstm_heads *heads, const float *y, size_t y_len, float *out,
+                                   size_t out_len, void *stream);
+
+/* Release the heads' device memory (waits for the device first). NULL is a no-op. */
+void bilstm_heads_destroy(bilstm_heads *heads);
+
 /* ---- host-only helpers: no GPU call, usable without a device ---------------------- */
 
 /*

@@ -191,3 +191,21 @@ def _have_gpu():
         return torch.cuda.is_available()
     except Exception:
         return False
+
+
+def test_heads_create_argument_checks_without_gpu(bl):
+    """Length and NULL checks of the heads' constructor come before any device call."""
+    lib = bl.library()
+    head = workloads.make_heads(3)
+    keep = [np.ascontiguousarray(head[k], np.float32) for k in ("w0", "b0", "w1", "b1", "w2", "b2")]
+    fields = []
+    for a in keep:
+        fields += [a.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), a.size]
+    fields[1] -= 1  # W0 one element short
+    hw = bl.HeadWeights(*fields, ctypes.c_float(0.01))
+    h = ctypes.c_void_p()
+    assert lib.bilstm_heads_create(0, ctypes.byref(hw), ctypes.byref(h)) == 2
+    assert "heads_create W0" in bl.last_error() and not h.value
+    assert lib.bilstm_heads_create(0, None, ctypes.byref(h)) == 1
+    assert lib.bilstm_heads_forward(None, None, 0, None, 0, None) == 1
+    lib.bilstm_heads_destroy(None)
