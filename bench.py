@@ -193,6 +193,28 @@ def main() -> int:
     rec_med = [statistics.median(v) for v in rec_ms]
     plan.close()
 
+    # comparator: the same projections through the vendor GEMM (hipBLASLt, FP32, bias epilogue)
+    lib_ms = [[] for _ in range(4)]
+    try:
+        lplan = bl.Plan(layers, wl.batch, wl.steps, projection=1)
+        for _ in range(reps + 1):
+            for l in range(4):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                lplan.project(l, layer_in[l], gates)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                lib_ms[l].append(e0.elapsed_time(e1))
+        lplan.close()
+        lib_med = [statistics.median(v[1:]) for v in lib_ms]
+        lib_tflops = projection_flops(frames) / (sum(lib_med) / 1e3) / 1e12
+        library_projection = {"ms_per_layer": lib_med, "achieved_tflops": lib_tflops,
+                              "frac": lib_tflops / PEAK_FP32_MFMA_TFLOPS,
+                              "tflops_per_layer": [2.0 * frames * 1024 * k / (ms / 1e3) / 1e12
+                                                   for k, ms in zip((60, 256, 256, 256), lib_med)]}
+    except Exception as e:  # measurement only
+        library_projection = {"error": str(e)}
+
     # the fused segmentation heads after the stack, alone, on this workload's stack output
     heads = bl.Heads(workloads.make_heads(wl.seed))
     logp = torch.empty((wl.batch, wl.steps, 7), dtype=torch.float32, device="cuda")
@@ -263,6 +285,7 @@ def main() -> int:
         "projection": {"ms_total": proj_total_ms, "ms_per_layer": proj_med, "achieved_tflops": proj_tflops,
                        "tflops_per_layer": proj_layer_tflops,
                        "peak_tflops": PEAK_FP32_MFMA_TFLOPS, "frac": proj_tflops / PEAK_FP32_MFMA_TFLOPS},
+        "projection_vendor_gemm": library_projection,
         "heads": {"ms": heads_med, "achieved_tflops": heads_tflops, "peak_tflops": PEAK_FP32_MFMA_TFLOPS,
                   "frac": heads_tflops / PEAK_FP32_MFMA_TFLOPS,
                   "hbm_gbs": HEAD_BYTES_PER_FRAME * frames / (heads_med / 1e3) / 1e9,

@@ -13,8 +13,8 @@ LIB_NAME = "libbilstm_amd.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 OBJ_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["host_plan.cpp", "host_pack_schedule.cpp", "host_heads.cpp", "kernels_projection.hip",
-           "kernels_recurrence.hip", "kernels_heads.hip"]
+SOURCES = ["host_plan.cpp", "host_pack_schedule.cpp", "host_heads.cpp", "host_library_projection.cpp",
+           "kernels_projection.hip", "kernels_recurrence.hip", "kernels_heads.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -44,7 +44,9 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as pool:
         objs = list(pool.map(compile_one, SOURCES))
     tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    # hipBLASLt: the vendor-GEMM projection offered as a comparator (bilstm_options.projection)
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
+           "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")

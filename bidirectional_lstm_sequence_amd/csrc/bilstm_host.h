@@ -26,4 +26,12 @@ bilstm_status pack_layer(const bilstm_layer &layer, int in, float *w_out, float 
 bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
                        const bilstm_options *opt, bilstm_plan_info *info);
 
+// The projection through hipBLASLt (comparator for the hand-written kernel), full batch only.
+struct LibraryProjection;
+bilstm_status library_projection_create(long rows, const int in[kLayers], const int kpad[kLayers],
+                                        float *const bias[kLayers], LibraryProjection **out);
+bilstm_status library_projection_run(LibraryProjection *lp, int layer, const float *x, const float *w,
+                                     float *gates, hipStream_t stream);
+void library_projection_destroy(LibraryProjection *lp);
+
 }  // namespace bl

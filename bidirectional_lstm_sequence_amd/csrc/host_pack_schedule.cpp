@@ -46,8 +46,11 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
                     cu_count, per_cu);
     }
     if (opt != nullptr) {
-        for (int i = 0; i < 3; ++i) {
+        for (int i = 0; i < 2; ++i) {
             if (opt->reserved[i] != 0) return fail(BILSTM_INVALID_ARGUMENT, "options: reserved[%d] must be 0", i);
+        }
+        if (opt->projection != 0 && opt->projection != 1) {
+            return fail(BILSTM_INVALID_ARGUMENT, "options: projection %d is not 0 or 1", opt->projection);
         }
         if (opt->slices < 0 || opt->slices > kMaxSlices) {
             return fail(BILSTM_INVALID_ARGUMENT, "options: slices %d is not in 0..%d", opt->slices, kMaxSlices);
@@ -121,14 +124,16 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
     // tile's workgroups wait for each other, and two slices' launches partly resident at once
     // could then wait on each other for good.
     const int want_slices = (opt != nullptr) ? opt->slices : 0;
+    const int projection = (opt != nullptr) ? opt->projection : 0;
     int slices = 1;
     if (want_slices > 1) {
-        if (groups != 1 || concurrent == 1) {
-            return fail(BILSTM_UNSUPPORTED, "schedule: %d slices need recur_groups = 1 and concurrent != 1",
-                        want_slices);
+        if (groups != 1 || concurrent == 1 || projection != 0) {
+            return fail(BILSTM_UNSUPPORTED,
+                        "schedule: %d slices need recur_groups = 1, concurrent != 1 and the library's own "
+                        "projection", want_slices);
         }
         slices = want_slices;
-    } else if (want_slices == 0 && groups == 1 && concurrent != 1) {
+    } else if (want_slices == 0 && groups == 1 && concurrent != 1 && projection == 0) {
         // auto: slice when the recurrence leaves at least half of the CUs idle
         if (2 * grid * 2 <= cu_count && static_cast<long long>(batch) >= 2LL * tile) slices = kAutoSlices;
     }
@@ -141,6 +146,7 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
     info->steps = steps;
     info->slices = slices;
     info->slice_windows = slice_windows;
+    info->projection = projection;
     info->recur_groups = groups;
     info->recur_tile = tile;
     info->recur_tiles = tiles;

@@ -73,6 +73,7 @@ struct bilstm_plan {
     hipEvent_t slice_first[kMaxSlices] = {};  // after the slice's first projection
     hipEvent_t slice_join[kMaxSlices] = {};
     size_t reserve_lds = 0;  // dynamic LDS of a recurrence workgroup (keeps its CU to itself)
+    LibraryProjection *library = nullptr;  // vendor-GEMM projection (comparator), if chosen
     int proj_workgroups = 0;         // persistent projection workgroups on an idle GPU
     int proj_workgroups_sliced = 0;  // ... beside the other slices' recurrences
     uint32_t epoch = 0;  // flags of the next pass start above this value
@@ -147,6 +148,7 @@ void release(bilstm_plan *p) {
         if (p->slice_join[i]) (void)hipEventDestroy(p->slice_join[i]);
     }
     if (p->slice_fork) (void)hipEventDestroy(p->slice_fork);
+    if (p->library) library_projection_destroy(p->library);
     if (p->gates) (void)hipFree(p->gates);
     if (p->exchange) (void)hipFree(p->exchange);
     if (p->error) (void)hipFree(p->error);
@@ -189,6 +191,13 @@ bilstm_status reserve_flags(bilstm_plan *p, uint32_t count, hipStream_t stream, 
 // The projection of rows [row_first, row_first + rows) of x into the same rows of gates.
 bilstm_status enqueue_projection(bilstm_plan *p, int layer, const float *x, float *gates,
                                  hipStream_t stream, size_t row_first, size_t rows, int workgroups) {
+    if (p->library != nullptr) {
+        // the vendor GEMM was planned for the whole batch, which it always runs unsliced
+        if (row_first != 0 || rows != p->rows) {
+            return fail(BILSTM_UNSUPPORTED, "projection: the vendor GEMM runs the whole batch only");
+        }
+        return library_projection_run(p->library, layer, x, p->w[layer], gates, stream);
+    }
     ProjArgs args{};
     args.x = x + row_first * p->in[layer];
     args.w = p->w[layer];
@@ -397,6 +406,12 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
     }
 
     if ((st = device_alloc(p, &p->gates, rows * kGateCols, "gates")) != BILSTM_OK) return fail_release(st);
+    if (info.projection == 1) {
+        if ((st = library_projection_create(static_cast<long>(rows), p->in, p->kpad, p->bias, &p->library)) !=
+            BILSTM_OK) {
+            return fail_release(st);
+        }
+    }
     if ((st = device_alloc(p, &p->error, 1, "error word")) != BILSTM_OK) return fail_release(st);
     e = hipMemset(p->error, 0, sizeof(unsigned int));
     if (info.recur_groups > 1) {

@@ -100,8 +100,12 @@ typedef struct {
                              0 = auto (2 when the recurrence leaves at least half of the CUs
                              idle, else 1), 1 = off, at most 8 (beyond the process's hardware
                              queues, 4 by default, streams share queues and run one after
-                             another); needs recur_groups = 1 and concurrent != 1 */
-    int32_t reserved[3];  /* must be zero */
+                             another); needs recur_groups = 1, concurrent != 1 and
+                             projection = 0 */
+    int32_t projection;   /* input projection: 0 the library's own FP32-MFMA kernel (default),
+                             1 the vendor GEMM (hipBLASLt, FP32 compute, bias epilogue) as a
+                             comparator; 1 runs the batch unsliced */
+    int32_t reserved[2];  /* must be zero */
 } bilstm_options;
 
 /* What a plan chose; filled by bilstm_plan_get_info. */
@@ -121,6 +125,7 @@ typedef struct {
     uint64_t device_bytes;   /* device memory the plan owns */
     int32_t slices;          /* batch slices bilstm_forward runs as concurrent chains */
     int32_t slice_windows;   /* windows per slice (the last slice may hold fewer) */
+    int32_t projection;      /* 0 own FP32-MFMA kernel, 1 vendor GEMM */
 } bilstm_plan_info;
 
 /*

@@ -68,15 +68,18 @@ def projection_bound(x, layer):
     return to_packed((k + 2) * 2.0 ** -24 * mag * 1.01 + 1e-30)
 
 
-@pytest.mark.parametrize("layer_index,rows", [(0, 200), (0, 589), (1, 333), (1, 4712)])
-def test_projection_matches_oracle(bl, orc, layer_index, rows):
+@pytest.mark.parametrize("layer_index,rows,projection", [(0, 200, 0), (0, 589, 0), (1, 333, 0), (1, 4712, 0),
+                                                         (1, 18848, 0), (0, 589, 1), (1, 4712, 1)])
+def test_projection_matches_oracle(bl, orc, layer_index, rows, projection):
+    """The projection alone (projection = 1: the vendor-GEMM comparator) against the oracle,
+    within the summation-order-free fp32 bound."""
     layers = workloads.make_layers(31)
     width = 60 if layer_index == 0 else 256
     x = np.random.default_rng(rows).standard_normal((rows, width)).astype(np.float32)
     if layer_index > 0:
         x = np.tanh(x).astype(np.float32)  # later layers see hidden states in (-1, 1)
-    note(f"projection layer={layer_index} rows={rows}")
-    plan = bl.Plan(layers, rows, 1)
+    note(f"projection layer={layer_index} rows={rows} projection={projection}")
+    plan = bl.Plan(layers, rows, 1, projection=projection)
     gates = plan.project(layer_index, torch.from_numpy(x).cuda())
     torch.cuda.synchronize()
     ref = to_packed(orc.projection(x, layers[layer_index]["w"], layers[layer_index]["b"]))
@@ -181,6 +184,17 @@ def test_stack_bit_stable_and_batch_invariant(bl):
     y8, _ = run_stack(bl, np.ascontiguousarray(x[:8]), layers)
     assert np.array_equal(y1[0].view(np.uint32), runs[0][5].view(np.uint32))
     assert np.array_equal(y8.view(np.uint32), runs[0][:8].view(np.uint32))
+
+
+def test_stack_with_library_projection_matches_oracle(bl, orc):
+    """The whole stack with the vendor-GEMM projection (comparator) against the oracle."""
+    x, layers = workloads.make_workload("b8")
+    note("stack b8 projection=1")
+    got, info = run_stack(bl, x, layers, projection=1)
+    assert info["projection"] == 1 and info["slices"] == 1
+    ref = orc.stack(x, layers, threads=min(16, os.cpu_count() or 1))
+    err = assert_close(got, ref, "b8 library projection")
+    note(f"stack b8 projection=1 max abs err {err:.3e}")
 
 
 @pytest.mark.parametrize("name,steps,slices", [("b8", 200, 2), ("b8", 200, 3), ("b32", 150, 4), ("b32", 150, 8)])
