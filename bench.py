@@ -100,6 +100,8 @@ def main() -> int:
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--concurrent", type=int, default=-1)
     ap.add_argument("--slices", type=int, default=0)
+    ap.add_argument("--projection", type=int, default=0, choices=(0, 1, 2),
+                    help="0 own FP32-MFMA kernel (default), 1 vendor GEMM, 2 own split-precision kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -131,7 +133,7 @@ def main() -> int:
     x, layers = workloads.make_workload(wl)
     frames = wl.batch * wl.steps
     plan = bl.Plan(layers, wl.batch, wl.steps, groups=args.groups, tile=args.tile,
-                   concurrent=args.concurrent, slices=args.slices)
+                   concurrent=args.concurrent, slices=args.slices, projection=args.projection)
     info = plan.info()
     xd = torch.from_numpy(x).cuda()
     yd = torch.empty((wl.batch, wl.steps, 256), dtype=torch.float32, device="cuda")
@@ -193,27 +195,30 @@ def main() -> int:
     rec_med = [statistics.median(v) for v in rec_ms]
     plan.close()
 
-    # comparator: the same projections through the vendor GEMM (hipBLASLt, FP32, bias epilogue)
-    lib_ms = [[] for _ in range(4)]
-    try:
-        lplan = bl.Plan(layers, wl.batch, wl.steps, projection=1)
-        for _ in range(reps + 1):
-            for l in range(4):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                lplan.project(l, layer_in[l], gates)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                lib_ms[l].append(e0.elapsed_time(e1))
-        lplan.close()
-        lib_med = [statistics.median(v[1:]) for v in lib_ms]
-        lib_tflops = projection_flops(frames) / (sum(lib_med) / 1e3) / 1e12
-        library_projection = {"ms_per_layer": lib_med, "achieved_tflops": lib_tflops,
-                              "frac": lib_tflops / PEAK_FP32_MFMA_TFLOPS,
-                              "tflops_per_layer": [2.0 * frames * 1024 * k / (ms / 1e3) / 1e12
-                                                   for k, ms in zip((60, 256, 256, 256), lib_med)]}
-    except Exception as e:  # measurement only
-        library_projection = {"error": str(e)}
+    # the other projection modes, each alone on the whole batch: the vendor GEMM (hipBLASLt,
+    # FP32, bias epilogue) and the own kernel in split precision (bf16 x 3)
+    def other_projection(mode):
+        ms = [[] for _ in range(4)]
+        try:
+            oplan = bl.Plan(layers, wl.batch, wl.steps, projection=mode)
+            for _ in range(reps + 1):
+                for l in range(4):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    oplan.project(l, layer_in[l], gates)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    ms[l].append(e0.elapsed_time(e1))
+            oplan.close()
+        except Exception as e:  # measurement only
+            return {"error": str(e)}
+        med = [statistics.median(v[1:]) for v in ms]
+        tf = projection_flops(frames) / (sum(med) / 1e3) / 1e12
+        return {"ms_per_layer": med, "achieved_tflops": tf, "frac": tf / PEAK_FP32_MFMA_TFLOPS,
+                "tflops_per_layer": [2.0 * frames * 1024 * k / (v / 1e3) / 1e12
+                                     for k, v in zip((60, 256, 256, 256), med)]}
+    library_projection = other_projection(1)
+    split_projection = other_projection(2)
 
     # the fused segmentation heads after the stack, alone, on this workload's stack output
     heads = bl.Heads(workloads.make_heads(wl.seed))
@@ -263,7 +268,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32" if args.projection != 2 else "f32 (projection: bf16x3 split)",
         "data": "synthetic: seeded U(-1/sqrt(128), 1/sqrt(128)) weights, N(0,1) input windows",
         "config": {"workload": f"{wl.name}: {wl.batch} windows x {wl.steps} frames, 4-layer BiLSTM "
                                f"H=128, input 60", "batch": wl.batch, "seq_len": wl.steps,
@@ -286,6 +291,8 @@ def main() -> int:
                        "tflops_per_layer": proj_layer_tflops,
                        "peak_tflops": PEAK_FP32_MFMA_TFLOPS, "frac": proj_tflops / PEAK_FP32_MFMA_TFLOPS},
         "projection_vendor_gemm": library_projection,
+        "projection_split_bf16x3": dict(split_projection, note="FP32-equivalent flops over time; "
+                                        "the matrix pipes run 3 bf16 products per FP32 one"),
         "heads": {"ms": heads_med, "achieved_tflops": heads_tflops, "peak_tflops": PEAK_FP32_MFMA_TFLOPS,
                   "frac": heads_tflops / PEAK_FP32_MFMA_TFLOPS,
                   "hbm_gbs": HEAD_BYTES_PER_FRAME * frames / (heads_med / 1e3) / 1e9,

@@ -46,6 +46,8 @@ inline size_t exchange_words_per_direction(int tiles, int tile) {
 struct ProjArgs {
     const float *x;      // [rows][in]
     const float *w;      // [1024][kpad]
+    const __bf16 *w_hi;  // split-precision mode: [1024][kpad] bf16(w), else nullptr
+    const __bf16 *w_lo;  //                       [1024][kpad] bf16(w - bf16(w))
     const float *bias;   // [1024]
     float *gates;        // [rows][1024]
     int rows;

@@ -49,8 +49,8 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
         for (int i = 0; i < 2; ++i) {
             if (opt->reserved[i] != 0) return fail(BILSTM_INVALID_ARGUMENT, "options: reserved[%d] must be 0", i);
         }
-        if (opt->projection != 0 && opt->projection != 1) {
-            return fail(BILSTM_INVALID_ARGUMENT, "options: projection %d is not 0 or 1", opt->projection);
+        if (opt->projection < 0 || opt->projection > 2) {
+            return fail(BILSTM_INVALID_ARGUMENT, "options: projection %d is not 0, 1 or 2", opt->projection);
         }
         if (opt->slices < 0 || opt->slices > kMaxSlices) {
             return fail(BILSTM_INVALID_ARGUMENT, "options: slices %d is not in 0..%d", opt->slices, kMaxSlices);
@@ -127,13 +127,13 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
     const int projection = (opt != nullptr) ? opt->projection : 0;
     int slices = 1;
     if (want_slices > 1) {
-        if (groups != 1 || concurrent == 1 || projection != 0) {
+        if (groups != 1 || concurrent == 1 || projection == 1) {
             return fail(BILSTM_UNSUPPORTED,
                         "schedule: %d slices need recur_groups = 1, concurrent != 1 and the library's own "
                         "projection", want_slices);
         }
         slices = want_slices;
-    } else if (want_slices == 0 && groups == 1 && concurrent != 1 && projection == 0) {
+    } else if (want_slices == 0 && groups == 1 && concurrent != 1 && projection != 1) {
         // auto: slice when the recurrence leaves at least half of the CUs idle
         if (2 * grid * 2 <= cu_count && static_cast<long long>(batch) >= 2LL * tile) slices = kAutoSlices;
     }

@@ -53,6 +53,8 @@ struct bilstm_plan {
     float *w[kLayers] = {nullptr, nullptr, nullptr, nullptr};
     float *r[kLayers] = {nullptr, nullptr, nullptr, nullptr};
     float *bias[kLayers] = {nullptr, nullptr, nullptr, nullptr};
+    uint16_t *w_hi[kLayers] = {nullptr, nullptr, nullptr, nullptr};  // split precision: bf16(w)
+    uint16_t *w_lo[kLayers] = {nullptr, nullptr, nullptr, nullptr};  //   bf16(w - bf16(w))
     float *gates = nullptr;
     unsigned long long *exchange = nullptr;
     size_t exchange_words = 0;
@@ -84,6 +86,21 @@ struct bilstm_plan {
 };
 
 namespace {
+
+// float -> bf16 bits, round to nearest even (the weights are finite)
+uint16_t bf16_rne(float f) {
+    uint32_t u;
+    std::memcpy(&u, &f, sizeof(u));
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+float bf16_value(uint16_t h) {
+    const uint32_t u = static_cast<uint32_t>(h) << 16;
+    float f;
+    std::memcpy(&f, &u, sizeof(f));
+    return f;
+}
 
 // Make `device` current for the scope and restore the caller's device afterwards.
 class DeviceScope {
@@ -134,6 +151,8 @@ void release(bilstm_plan *p) {
         if (p->w[l]) (void)hipFree(p->w[l]);
         if (p->r[l]) (void)hipFree(p->r[l]);
         if (p->bias[l]) (void)hipFree(p->bias[l]);
+        if (p->w_hi[l]) (void)hipFree(p->w_hi[l]);
+        if (p->w_lo[l]) (void)hipFree(p->w_lo[l]);
         if (p->fork[l]) (void)hipEventDestroy(p->fork[l]);
         if (p->join[l]) (void)hipEventDestroy(p->join[l]);
         if (p->ev_proj[l]) (void)hipEventDestroy(p->ev_proj[l]);
@@ -201,6 +220,8 @@ bilstm_status enqueue_projection(bilstm_plan *p, int layer, const float *x, floa
     ProjArgs args{};
     args.x = x + row_first * p->in[layer];
     args.w = p->w[layer];
+    args.w_hi = reinterpret_cast<const __bf16 *>(p->w_hi[layer]);
+    args.w_lo = reinterpret_cast<const __bf16 *>(p->w_lo[layer]);
     args.bias = p->bias[layer];
     args.gates = gates + row_first * kGateCols;
     args.rows = static_cast<int>(rows);
@@ -402,6 +423,21 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
         if (e == hipSuccess) e = hipMemcpy(p->bias[l], b.data(), b.size() * sizeof(float), hipMemcpyHostToDevice);
         if (e != hipSuccess) {
             return fail_release(fail(BILSTM_HIP_ERROR, "plan_create: weight upload: %s", hipGetErrorString(e)));
+        }
+        if (info.projection == 2) {
+            // split precision: w = hi + lo (+ a residual below 2^-16·|w|), both bf16
+            std::vector<uint16_t> hi(w.size()), lo(w.size());
+            for (size_t i = 0; i < w.size(); ++i) {
+                hi[i] = bf16_rne(w[i]);
+                lo[i] = bf16_rne(w[i] - bf16_value(hi[i]));
+            }
+            if ((st = device_alloc(p, &p->w_hi[l], hi.size(), "W hi")) != BILSTM_OK) return fail_release(st);
+            if ((st = device_alloc(p, &p->w_lo[l], lo.size(), "W lo")) != BILSTM_OK) return fail_release(st);
+            e = hipMemcpy(p->w_hi[l], hi.data(), hi.size() * sizeof(uint16_t), hipMemcpyHostToDevice);
+            if (e == hipSuccess) e = hipMemcpy(p->w_lo[l], lo.data(), lo.size() * sizeof(uint16_t), hipMemcpyHostToDevice);
+            if (e != hipSuccess) {
+                return fail_release(fail(BILSTM_HIP_ERROR, "plan_create: weight upload: %s", hipGetErrorString(e)));
+            }
         }
     }
 

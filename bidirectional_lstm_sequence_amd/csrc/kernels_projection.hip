@@ -199,6 +199,188 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a)
     }
 }
 
+
+// ---- split-precision variant ---------------------------------------------------------------
+//
+// The same projection with every FP32 operand split into two bf16 parts, a = a_hi + a_lo
+// (a_hi = bf16(a), a_lo = bf16(a - a_hi), both round-to-nearest-even), and three bf16 MFMA
+// products per K chunk, hi·hi + hi·lo + lo·hi, accumulated in FP32 (a bf16 x bf16 product is
+// exact in FP32). The dropped lo·lo term and the two parts' residuals stay below
+// 3·2^-16·|x·w| per product, so
+//   |gates - exact| <= (3·2^-16·(1 + 2^-7) + (3K + 2)·2^-24) · sum_k |x_k w_k| (+ bias rounding).
+// W arrives already split (two [1024][kpad] bf16 planes, packed at plan creation); x is split
+// while staging into LDS. v_mfma_f32_32x32x16_bf16: lane l supplies row (or column) l % 32 and
+// eight consecutive k of half l / 32 of each 16-wide K chunk, for A and B alike.
+constexpr int kSplitStride = BK + 8;  // LDS row stride, bf16 elements (80 bytes: conflict-free)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int KSTEPS>
+__global__ __launch_bounds__(kProjThreads, 1) void projection_split_kernel(ProjArgs a) {
+    // [stage][hi, lo][row][k]
+    __shared__ __attribute__((aligned(16))) __bf16 lds_a[2][2][BM * kSplitStride];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_b[2][2][BN * kSplitStride];
+
+    const int nwg = gridDim.x;  // a multiple of 8
+    const int per_xcd = nwg >> 3;
+    const int first = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    constexpr int kColTiles = kGateCols / BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+
+    // x: 4 float4 per thread per K step (row f / 8, k 4·(f % 8)); W: per plane 2 x 16 bytes
+    // (8 bf16) per thread (row f / 4, k 8·(f % 4))
+    v4f ra[kLoadsPerThread];
+    u32x4 rb[2][2];  // [plane][i]
+    auto load = [&](int m0, int n0, int k0) {
+#pragma unroll
+        for (int j = 0; j < kLoadsPerThread; ++j) {
+            const int f = tid + kProjThreads * j;
+            const int m = m0 + f / kThreadsPerRow;
+            const int k = k0 + (f % kThreadsPerRow) * 4;
+            v4f va = {0.f, 0.f, 0.f, 0.f};
+            if (m < a.rows && k < a.in) {
+                va = *reinterpret_cast<const v4f *>(a.x + static_cast<size_t>(m) * a.in + k);
+            }
+            ra[j] = va;
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int f = tid + kProjThreads * i;
+            const size_t off = static_cast<size_t>(n0 + (f >> 2)) * a.kpad + k0 + (f & 3) * 8;
+            rb[0][i] = *reinterpret_cast<const u32x4 *>(a.w_hi + off);
+            rb[1][i] = *reinterpret_cast<const u32x4 *>(a.w_lo + off);
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < kLoadsPerThread; ++j) {
+            const int f = tid + kProjThreads * j;
+            const int off = (f / kThreadsPerRow) * kSplitStride + (f % kThreadsPerRow) * 4;
+            bf16x4 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hi[e] = static_cast<__bf16>(ra[j][e]);
+                lo[e] = static_cast<__bf16>(ra[j][e] - static_cast<float>(hi[e]));
+            }
+            *reinterpret_cast<bf16x4 *>(&lds_a[buf][0][off]) = hi;
+            *reinterpret_cast<bf16x4 *>(&lds_a[buf][1][off]) = lo;
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int f = tid + kProjThreads * i;
+            const int off = (f >> 2) * kSplitStride + (f & 3) * 8;
+            *reinterpret_cast<u32x4 *>(&lds_b[buf][0][off]) = rb[0][i];
+            *reinterpret_cast<u32x4 *>(&lds_b[buf][1][off]) = rb[1][i];
+        }
+    };
+
+    const int frag_row = lane & 31;
+    const int frag_k = (lane >> 5) * 8;
+    // fragments of K chunk c (16 wide): [plane][block]
+    auto frags = [&](int buf, int c, bf16x8 (&af)[2][2], bf16x8 (&bf)[2][2]) {
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                af[pl][t] = *reinterpret_cast<const bf16x8 *>(
+                    &lds_a[buf][pl][(wm * 64 + t * 32 + frag_row) * kSplitStride + c * 16 + frag_k]);
+                bf[pl][t] = *reinterpret_cast<const bf16x8 *>(
+                    &lds_b[buf][pl][(wn * 64 + t * 32 + frag_row) * kSplitStride + c * 16 + frag_k]);
+            }
+    };
+
+    float pend[2][2][16];
+    int pm0 = 0, pn0 = 0;
+    bool have = false;
+    auto put = [&](int i, int j, int r) {
+        const int m = pm0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int n = pn0 + wn * 64 + j * 32 + (lane & 31);
+        if (m < a.rows) a.gates[static_cast<size_t>(m) * kGateCols + n] = pend[i][j][r];
+    };
+    constexpr int kChunk = 64 / KSTEPS;
+    auto put_chunk = [&](int s) {
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+            const int idx = s * kChunk + c;
+            put(idx >> 5, (idx >> 4) & 1, idx & 15);
+        }
+    };
+
+    int q = first;
+    int base = 0;
+    if (q < a.tiles) {
+        load((q / kColTiles) * BM, (q % kColTiles) * BN, 0);
+        store(0);
+    }
+    __syncthreads();
+
+    for (; q < a.tiles; q += nwg) {
+        const int m0 = (q / kColTiles) * BM;
+        const int n0 = (q % kColTiles) * BN;
+        const int qn = q + nwg;
+        const bool next = qn < a.tiles;
+
+        v16f acc[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+#pragma unroll
+        for (int kt = 0; kt < KSTEPS; ++kt) {
+            const int cur = (base + kt) & 1;
+            const bool more = kt + 1 < KSTEPS;
+            if (more) {
+                load(m0, n0, (kt + 1) * BK);
+            } else if (next) {
+                load((qn / kColTiles) * BM, (qn % kColTiles) * BN, 0);
+            }
+#pragma unroll
+            for (int c = 0; c < BK / 16; ++c) {
+                bf16x8 af[2][2], bf[2][2];
+                frags(cur, c, af, bf);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bf[0][j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bf[1][j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bf[0][j], acc[i][j], 0, 0, 0);
+                    }
+                if (c == 0 && have) put_chunk(kt);
+            }
+            if (more || next) store(cur ^ 1);
+            __syncthreads();
+        }
+
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float bv = a.bias[n0 + wn * 64 + j * 32 + (lane & 31)];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) pend[i][j][r] = acc[i][j][r] + bv;
+        }
+        pm0 = m0;
+        pn0 = n0;
+        have = true;
+        base = (base + KSTEPS) & 1;
+    }
+    if (have) {
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) put_chunk(s);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_projection(const ProjArgs &args, int workgroups, hipStream_t stream) {
@@ -206,6 +388,19 @@ hipError_t launch_projection(const ProjArgs &args, int workgroups, hipStream_t s
     // a multiple of 8 (the XCD-ordered walk), at most one workgroup per tile group of 8
     int nwg = std::min(workgroups, (args.tiles + 7) / 8 * 8);
     nwg = std::max(8, nwg / 8 * 8);
+    if (args.w_hi != nullptr) {
+        switch (args.kpad / kProjTileK) {
+            case 2:
+                hipLaunchKernelGGL(projection_split_kernel<2>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
+                break;
+            case 8:
+                hipLaunchKernelGGL(projection_split_kernel<8>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
+                break;
+            default:
+                return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (args.kpad / kProjTileK) {
         case 2:
             hipLaunchKernelGGL(projection_kernel<2>, dim3(nwg), dim3(kProjThreads), 0, stream, args);

@@ -102,9 +102,12 @@ typedef struct {
                              queues, 4 by default, streams share queues and run one after
                              another); needs recur_groups = 1, concurrent != 1 and
                              projection = 0 */
-    int32_t projection;   /* input projection: 0 the library's own FP32-MFMA kernel (default),
+    int32_t projection;   /* input projection: 0 the library's own FP32-MFMA kernel (default);
                              1 the vendor GEMM (hipBLASLt, FP32 compute, bias epilogue) as a
-                             comparator; 1 runs the batch unsliced */
+                             comparator, run unsliced; 2 the own kernel in split precision:
+                             each FP32 operand split into two bf16 parts, three bf16 MFMA
+                             products per K chunk (hi·hi + hi·lo + lo·hi) accumulated in FP32,
+                             |error| <= (3·2^-16·(1 + 2^-7) + (3K + 2)·2^-24)·sum|x·w| per gate */
     int32_t reserved[2];  /* must be zero */
 } bilstm_options;
 
@@ -125,7 +128,7 @@ typedef struct {
     uint64_t device_bytes;   /* device memory the plan owns */
     int32_t slices;          /* batch slices bilstm_forward runs as concurrent chains */
     int32_t slice_windows;   /* windows per slice (the last slice may hold fewer) */
-    int32_t projection;      /* 0 own FP32-MFMA kernel, 1 vendor GEMM */
+    int32_t projection;      /* 0 own FP32-MFMA kernel, 1 vendor GEMM, 2 own split-precision */
 } bilstm_plan_info;
 
 /*

@@ -60,16 +60,23 @@ def to_packed(oracle_gates):
     return np.ascontiguousarray(g.transpose(0, 1, 3, 2).reshape(rows, 1024))
 
 
-def projection_bound(x, layer):
+def projection_bound(x, layer, split=False):
+    """|gpu - exact| bound of a gate pre-activation. FP32: (K + 2)·u·(sum|w x| + |bias|), any
+    summation order. Split precision (bf16 x 3): the dropped lo·lo term and the parts'
+    residuals add 3·2^-16·(1 + 2^-7)·sum|w x|, the FP32 sum runs over 3K products."""
     w = layer["w"].astype(np.float64)
     b = layer["b"].astype(np.float64)
     k = x.shape[1]
     mag = np.einsum("mk,drk->mdr", np.abs(x.astype(np.float64)), np.abs(w)) + np.abs(b[:, 0] + b[:, 1])[None]
-    return to_packed((k + 2) * 2.0 ** -24 * mag * 1.01 + 1e-30)
+    if not split:
+        return to_packed((k + 2) * 2.0 ** -24 * mag * 1.01 + 1e-30)
+    coeff = 3 * 2.0 ** -16 * (1 + 2.0 ** -7) + (3 * k + 2) * 2.0 ** -24 * 1.01
+    return to_packed(coeff * mag * 1.01 + 1e-30)
 
 
 @pytest.mark.parametrize("layer_index,rows,projection", [(0, 200, 0), (0, 589, 0), (1, 333, 0), (1, 4712, 0),
-                                                         (1, 18848, 0), (0, 589, 1), (1, 4712, 1)])
+                                                         (1, 18848, 0), (0, 589, 1), (1, 4712, 1),
+                                                         (0, 589, 2), (1, 333, 2), (1, 18848, 2)])
 def test_projection_matches_oracle(bl, orc, layer_index, rows, projection):
     """The projection alone (projection = 1: the vendor-GEMM comparator) against the oracle,
     within the summation-order-free fp32 bound."""
@@ -84,8 +91,10 @@ def test_projection_matches_oracle(bl, orc, layer_index, rows, projection):
     torch.cuda.synchronize()
     ref = to_packed(orc.projection(x, layers[layer_index]["w"], layers[layer_index]["b"]))
     err = np.abs(gates.cpu().numpy().astype(np.float64) - ref)
-    bound = projection_bound(x, layers[layer_index])
+    bound = projection_bound(x, layers[layer_index], split=projection == 2)
     assert np.all(err <= bound), f"max err {err.max():.3e}, worst ratio {(err / bound).max():.2f}"
+    note(f"projection layer={layer_index} rows={rows} projection={projection} max err {err.max():.3e} "
+         f"worst ratio to bound {(err / bound).max():.3f}")
     plan.close()
 
 
@@ -184,6 +193,28 @@ def test_stack_bit_stable_and_batch_invariant(bl):
     y8, _ = run_stack(bl, np.ascontiguousarray(x[:8]), layers)
     assert np.array_equal(y1[0].view(np.uint32), runs[0][5].view(np.uint32))
     assert np.array_equal(y8.view(np.uint32), runs[0][:8].view(np.uint32))
+
+
+@pytest.mark.parametrize("name,windows", [("b8", None), ("b32", None), ("b256", [0, 3, 10, 255]),
+                                          ("b64_t4096", [5])])
+def test_stack_with_split_projection_matches_oracle(bl, orc, name, windows):
+    """Split-precision projections (bf16 x 3) keep the whole stack within the output tolerance."""
+    x, layers = workloads.make_workload(name)
+    note(f"stack {name} projection=2 windows={windows}")
+    got, info = run_stack(bl, x, layers, projection=2)
+    assert info["projection"] == 2
+    ref = orc.stack(x, layers, windows=windows, threads=min(16, os.cpu_count() or 1))
+    err = assert_close(got if windows is None else got[windows], ref, f"{name} split projection")
+    note(f"stack {name} projection=2 max abs err {err:.3e}")
+
+
+def test_split_projection_batch_invariant(bl):
+    """A window's split-precision output is bitwise the same at B = 1 and inside B = 32."""
+    x, layers = workloads.make_workload("b32")
+    xs = np.ascontiguousarray(x[:, :120])
+    y32, _ = run_stack(bl, xs, layers, projection=2)
+    y1, _ = run_stack(bl, np.ascontiguousarray(xs[9:10]), layers, projection=2)
+    assert np.array_equal(y1[0].view(np.uint32), y32[9].view(np.uint32))
 
 
 def test_stack_with_library_projection_matches_oracle(bl, orc):

@@ -150,6 +150,8 @@ def test_schedule_library_projection_runs_unsliced(bl):
     s = bl.schedule(32, 589, 256, 1, projection=1)
     assert s["projection"] == 1 and s["slices"] == 1
     assert bl.schedule(32, 589, 256, 1)["projection"] == 0
+    s = bl.schedule(32, 589, 256, 1, projection=2)  # own split-precision kernel: sliced like FP32
+    assert s["projection"] == 2 and s["slices"] == 2
     with pytest.raises(bl.BilstmError) as e:
         bl.schedule(32, 589, 256, 1, projection=1, slices=2)
     assert e.value.name == "BILSTM_UNSUPPORTED"
@@ -158,7 +160,8 @@ def test_schedule_library_projection_runs_unsliced(bl):
 @pytest.mark.parametrize("kwargs,status", [
     (dict(groups=3), "BILSTM_UNSUPPORTED"), (dict(tile=3), "BILSTM_UNSUPPORTED"),
     (dict(concurrent=5), "BILSTM_INVALID_ARGUMENT"), (dict(slices=9), "BILSTM_INVALID_ARGUMENT"),
-    (dict(slices=-1), "BILSTM_INVALID_ARGUMENT"), (dict(projection=2), "BILSTM_INVALID_ARGUMENT")])
+    (dict(slices=-1), "BILSTM_INVALID_ARGUMENT"), (dict(projection=3), "BILSTM_INVALID_ARGUMENT"),
+    (dict(projection=-1), "BILSTM_INVALID_ARGUMENT")])
 def test_schedule_rejects_bad_options(bl, kwargs, status):
     with pytest.raises(bl.BilstmError) as e:
         bl.schedule(8, 589, 256, 1, **kwargs)
