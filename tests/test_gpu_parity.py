@@ -317,3 +317,36 @@ def test_exchange_probe(bl):
     cross = bl.probe_exchange(0, False, 2000)
     note(f"exchange one-way: same-xcd {same} cross-xcd {cross}")
     assert 0 < same["one_way_ns"] < 100000 and 0 < cross["one_way_ns"] < 100000
+
+
+@pytest.mark.parametrize("steps", [1, 2, 3, 5, 7])
+@pytest.mark.parametrize("groups,tile", [(1, 1), (1, 2), (1, 4), (2, 2), (4, 1)])
+def test_recurrence_short_sequences(bl, orc, steps, groups, tile):
+    """Sequences shorter than the 4-step prefetch ring and its straight-line groups, with a
+    ragged last tile (3 windows), for single- and multi-workgroup splits."""
+    batch = 3
+    layers = workloads.make_layers(35)
+    rng = np.random.default_rng(100 + steps)
+    gates_src = (rng.standard_normal((batch * steps, 2, 512)) * 1.5).astype(np.float32)
+    note(f"short recurrence steps={steps} groups={groups} tile={tile}")
+    plan = bl.Plan(layers, batch, steps, groups=groups, tile=tile)
+    y = plan.recur(3, torch.from_numpy(to_packed(gates_src)).cuda())
+    plan.check()
+    got = y.cpu().numpy()
+    plan.close()
+    per_window = gates_src.reshape(batch, steps, 2, 512)
+    for b in range(batch):
+        assert_close(got[b], orc.recurrence(per_window[b].astype(np.float64), layers[3]["r"]), f"window {b}")
+
+
+@pytest.mark.parametrize("batch,steps,slices,projection", [(1, 1, 0, 0), (3, 2, 0, 0), (3, 5, 2, 0), (5, 3, 3, 2),
+                                                            (2, 130, 0, 1)])
+def test_stack_degenerate_shapes(bl, orc, batch, steps, slices, projection):
+    """One frame, a handful of frames (projection rows far below one 128-row tile), sliced
+    batches of odd sizes, and every projection mode."""
+    layers = workloads.make_layers(36)
+    x = workloads.make_input(36, batch, steps)
+    note(f"degenerate stack batch={batch} steps={steps} slices={slices} projection={projection}")
+    got, info = run_stack(bl, x, layers, slices=slices, projection=projection)
+    ref = orc.stack(x, layers)
+    assert_close(got, ref, f"b{batch} t{steps}")
