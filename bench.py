@@ -69,7 +69,8 @@ def recorded_traffic(workload: str, info: dict):
         return None
     if (rec.get("source_sha256") != kernel_source_digest() or rec.get("workload") != workload
             or rec.get("concurrent") != info["concurrent"] or rec.get("groups") != info["recur_groups"]
-            or rec.get("tile") != info["recur_tile"] or rec.get("slices") != info["slices"]):
+            or rec.get("tile") != info["recur_tile"] or rec.get("slices") != info["slices"]
+            or rec.get("pipeline", 0) != info["pipeline"]):
         return None
     return {"bytes_per_launch": rec["fetch_bytes"] + rec["write_bytes"], "fetch_bytes": rec["fetch_bytes"],
             "write_bytes": rec["write_bytes"], "source": "profiles/recurrence_traffic.json"}
@@ -102,6 +103,8 @@ def main() -> int:
     ap.add_argument("--slices", type=int, default=0)
     ap.add_argument("--projection", type=int, default=0, choices=(0, 1, 2),
                     help="0 own FP32-MFMA kernel (default), 1 vendor GEMM, 2 own split-precision kernel")
+    ap.add_argument("--pipeline", type=int, default=0, choices=(0, 1, 2),
+                    help="streamed gates: 0 auto, 1 off, 2 on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -133,7 +136,8 @@ def main() -> int:
     x, layers = workloads.make_workload(wl)
     frames = wl.batch * wl.steps
     plan = bl.Plan(layers, wl.batch, wl.steps, groups=args.groups, tile=args.tile,
-                   concurrent=args.concurrent, slices=args.slices, projection=args.projection)
+                   concurrent=args.concurrent, slices=args.slices, projection=args.projection,
+                   pipeline=args.pipeline)
     info = plan.info()
     xd = torch.from_numpy(x).cuda()
     yd = torch.empty((wl.batch, wl.steps, 256), dtype=torch.float32, device="cuda")
@@ -274,8 +278,11 @@ def main() -> int:
                                f"H=128, input 60", "batch": wl.batch, "seq_len": wl.steps,
                    "recurrence_split": {"groups": groups, "tile": tile, "tiles": info["recur_tiles"],
                                         "concurrent": info["concurrent"]},
-                   "slices": info["slices"], "slice_windows": info["slice_windows"]},
-        "roofline": {"kernel": f"recurrence_kernel<{groups}, {tile}> ({launch_dirs} direction(s) per launch)",
+                   "slices": info["slices"], "slice_windows": info["slice_windows"],
+                   "streamed_gates": {"on": bool(info["pipeline"]), "chunk_steps": info["stream_chunk"]}},
+        "roofline": {"kernel": f"recurrence_kernel<{groups}, {tile}, {'true' if info['pipeline'] else 'false'}> "
+                               f"({launch_dirs} direction(s) per launch"
+                               f"{', streamed gates' if info['pipeline'] else ''})",
                      "bound": "alu", "achieved": rec_tflops, "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
                      "frac": rec_tflops / PEAK_FP32_VECTOR_TFLOPS,
                      "traffic": traffic["bytes_per_launch"] if traffic else None,

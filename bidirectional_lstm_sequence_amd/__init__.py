@@ -56,7 +56,8 @@ class Layer(ctypes.Structure):
 class Options(ctypes.Structure):
     _fields_ = [("recur_groups", ctypes.c_int32), ("recur_tile", ctypes.c_int32),
                 ("concurrent", ctypes.c_int32), ("watchdog_us", ctypes.c_int32),
-                ("slices", ctypes.c_int32), ("projection", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
+                ("slices", ctypes.c_int32), ("projection", ctypes.c_int32), ("pipeline", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 1)]
 
 
 class HeadWeights(ctypes.Structure):
@@ -77,7 +78,8 @@ class PlanInfo(ctypes.Structure):
                 ("proj_tile_m", ctypes.c_int32), ("proj_tile_n", ctypes.c_int32),
                 ("cu_count", ctypes.c_int32), ("recur_capacity", ctypes.c_int32),
                 ("device_bytes", ctypes.c_uint64), ("slices", ctypes.c_int32),
-                ("slice_windows", ctypes.c_int32), ("projection", ctypes.c_int32)]
+                ("slice_windows", ctypes.c_int32), ("projection", ctypes.c_int32),
+                ("pipeline", ctypes.c_int32), ("stream_chunk", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -154,9 +156,10 @@ def _layer_struct(layer: dict, keep: list) -> Layer:
 
 
 def _options(groups: int, tile: int, concurrent: int, watchdog_us: int = 0, slices: int = 0,
-             projection: int = 0) -> Options:
+             projection: int = 0, pipeline: int = 0) -> Options:
     o = Options()
     o.projection = projection
+    o.pipeline = pipeline
     o.recur_groups = groups
     o.recur_tile = tile
     o.concurrent = concurrent
@@ -180,11 +183,11 @@ def pack_layer(layer: dict, width: int) -> tuple[np.ndarray, np.ndarray, np.ndar
 
 
 def schedule(batch: int, steps: int, cu_count: int, per_cu: int, groups: int = 0, tile: int = 0,
-             concurrent: int = -1, slices: int = 0, projection: int = 0) -> dict:
+             concurrent: int = -1, slices: int = 0, projection: int = 0, pipeline: int = 0) -> dict:
     """Host-side recurrence schedule (no GPU)."""
     lib = library()
     info = PlanInfo()
-    opt = _options(groups, tile, concurrent, slices=slices, projection=projection)
+    opt = _options(groups, tile, concurrent, slices=slices, projection=projection, pipeline=pipeline)
     _check(lib.bilstm_schedule(batch, steps, cu_count, per_cu, ctypes.byref(opt), ctypes.byref(info)))
     return info.as_dict()
 
@@ -225,18 +228,20 @@ class Plan:
     ``groups``, ``tile`` and ``concurrent`` override the plan's recurrence split;
     ``watchdog_us`` bounds each recurrence wait (0 = 2 s); ``slices`` sets how many batch
     slices the forward runs as concurrent chains (0 = auto, 1 = off); ``projection`` = 1 runs
-    the input projection through the vendor GEMM (hipBLASLt) instead of the library's kernel.
+    the input projection through the vendor GEMM (hipBLASLt) instead of the library's kernel,
+    2 through the library's split-precision kernel; ``pipeline`` streams each layer's gates
+    from its projection into its recurrence while both run (0 = auto, 1 = off, 2 = on).
     """
 
     def __init__(self, layers, batch: int, steps: int, device: int = 0, groups: int = 0,
                  tile: int = 0, concurrent: int = -1, watchdog_us: int = 0, slices: int = 0,
-                 projection: int = 0):
+                 projection: int = 0, pipeline: int = 0):
         if len(layers) != LAYERS:
             raise ValueError(f"expected {LAYERS} layers, got {len(layers)}")
         lib = library()
         keep: list = []
         arr = (Layer * LAYERS)(*[_layer_struct(l, keep) for l in layers])
-        opt = _options(groups, tile, concurrent, watchdog_us, slices, projection)
+        opt = _options(groups, tile, concurrent, watchdog_us, slices, projection, pipeline)
         handle = ctypes.c_void_p()
         _check(lib.bilstm_plan_create_ex(device, batch, steps, arr, ctypes.byref(opt), ctypes.byref(handle)))
         self._lib = lib

@@ -55,6 +55,14 @@ struct ProjArgs {
     int kpad;
     int row_tiles;       // ceil(rows / kProjTileM)
     int tiles;           // row_tiles * (1024 / kProjTileN)
+    // Streamed order (chunk > 0): tiles follow the recurrence's consumption order and each
+    // finished tile is published on `ready` (layout below). chunk = 0: plain row-major tiles.
+    int chunk;           // recurrence steps per tile row block (128 / group_windows)
+    int group_windows;   // windows per tile row block
+    int groups;          // ceil(batch / group_windows)
+    int batch;
+    int steps;
+    unsigned int *ready;  // [chunks][2][groups] publication counters
 };
 
 struct RecurArgs {
@@ -73,6 +81,13 @@ struct RecurArgs {
     unsigned int flag_skew;        // added to the flag a wait expects: 0, or a value no
                                    // producer writes (forced-timeout tests)
     unsigned long long timeout_ticks;  // watchdog, in wall-clock ticks
+    // Streamed gates (chunk > 0): before reading the gates of steps [c·chunk, (c+1)·chunk) of
+    // window group g, wait until ready[(c·2 + dir)·groups + g] reaches ready_target.
+    const unsigned int *ready;
+    int chunk;
+    int group_windows;
+    int groups;
+    unsigned int ready_target;
 };
 
 // Segmentation heads after the stack: 256 -> 128 -> 128 -> 7 (class slots padded to 8).
@@ -96,10 +111,29 @@ struct HeadArgs {
     long rows;
 };
 
+// Streamed projection: each layer's projection runs beside that layer's recurrence and
+// publishes its gates chunk by chunk in the order the recurrence reads them. A tile row
+// block holds `group_windows` windows × `chunk` steps (128 rows): row r is window
+// g·group_windows + r / chunk at step s = c·chunk + r % chunk of direction d, i.e. time s
+// (forward) or steps - 1 - s (reverse); rows past the batch or past the last step are
+// skipped. Tile q = ((c·2 + d)·groups + g)·4 + column tile, columns d·512 + 128·(column tile).
+// Each of a tile's 4 waves adds 1 to ready[(c·2 + d)·groups + g] once its gates are stored and
+// made visible at agent scope, so a pass adds kReadyPerPass to every counter.
+constexpr int kReadyPerPass = 4 * (kProjThreads / 64);
+// Dynamic LDS a streamed projection workgroup claims on top of its tiles, so that two of them
+// never share a CU (2 · (72 + 16) KB > 160 KB): its persistent grid then spreads one per CU.
+constexpr size_t kProjStreamLds = 16 * 1024;
+// Streamed gates are chosen automatically from this many windows on.
+constexpr int kStreamMinBatch = 16;
+inline int stream_chunks(int steps, int chunk) { return (steps + chunk - 1) / chunk; }
+
 // Launchers (kernels_*.hip). They return the launch's hipError_t.
 hipError_t launch_heads(const HeadArgs &args, hipStream_t stream);
-// The projection on `workgroups` persistent workgroups (one per CU; rounded to a multiple of 8).
-hipError_t launch_projection(const ProjArgs &args, int workgroups, hipStream_t stream);
+// The projection on `workgroups` persistent workgroups (one per CU; rounded to a multiple of 8),
+// each with `dynamic_lds` bytes of dynamic LDS besides its tiles.
+hipError_t launch_projection(const ProjArgs &args, int workgroups, size_t dynamic_lds, hipStream_t stream);
+// Allow `bytes` of dynamic LDS per streamed projection workgroup.
+hipError_t projection_allow_lds(size_t bytes);
 hipError_t launch_recurrence(int groups, int tile, const RecurArgs &args, int directions,
                              size_t dynamic_lds, hipStream_t stream);
 // Allow `bytes` of dynamic LDS per recurrence workgroup of this split.

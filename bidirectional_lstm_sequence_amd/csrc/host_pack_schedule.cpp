@@ -46,8 +46,9 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
                     cu_count, per_cu);
     }
     if (opt != nullptr) {
-        for (int i = 0; i < 2; ++i) {
-            if (opt->reserved[i] != 0) return fail(BILSTM_INVALID_ARGUMENT, "options: reserved[%d] must be 0", i);
+        if (opt->reserved[0] != 0) return fail(BILSTM_INVALID_ARGUMENT, "options: reserved[0] must be 0");
+        if (opt->pipeline < 0 || opt->pipeline > 2) {
+            return fail(BILSTM_INVALID_ARGUMENT, "options: pipeline %d is not 0, 1 or 2", opt->pipeline);
         }
         if (opt->projection < 0 || opt->projection > 2) {
             return fail(BILSTM_INVALID_ARGUMENT, "options: projection %d is not 0, 1 or 2", opt->projection);
@@ -119,14 +120,49 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
         }
     }
 
+    const int want_slices = (opt != nullptr) ? opt->slices : 0;
+    const int projection = (opt != nullptr) ? opt->projection : 0;
+
+    // Streamed gates: each layer's projection runs beside its own recurrence, on the CUs the
+    // recurrence leaves free (every recurrence workgroup keeps a CU to itself), and never waits
+    // for it; only the recurrence waits, for chunks the projection publishes. The projection
+    // needs CUs of its own (8 at least), single-workgroup tiles (no cross-workgroup waits in
+    // the recurrence besides the counters) and the library's own FP32 kernel.
+    const int want_pipe = (opt != nullptr) ? opt->pipeline : 0;
+    const long long rec_wgs = 2 * grid;
+    const bool pipe_possible = groups == 1 && projection == 0 && want_slices <= 1 && rec_wgs + 8 <= cu_count;
+    bool pipeline = false;
+    if (want_pipe == 2) {
+        if (!pipe_possible) {
+            return fail(BILSTM_UNSUPPORTED,
+                        "schedule: streamed gates need recur_groups = 1, projection = 0, slices <= 1 and at "
+                        "least 8 CUs beside the recurrence's %lld workgroups (%d CUs)", rec_wgs, cu_count);
+        }
+        pipeline = true;
+    } else if (want_pipe == 0) {
+        // auto: when the recurrence leaves at least a quarter of the CUs to the projection and
+        // the batch has at least 16 windows. Below that the whole projection of a layer takes
+        // about as long as the first published chunk (one tile of every direction, measured
+        // ~35 us at K = 256), so streaming gains nothing.
+        pipeline = pipe_possible && concurrent == 2 && 4 * rec_wgs <= 3LL * cu_count &&
+                   batch >= static_cast<uint32_t>(kStreamMinBatch);
+    }
+    // windows per projection row block: up to 4, a multiple of the recurrence tile, so a
+    // recurrence tile never spans two row blocks; chunk = 128 / that many steps
+    int group_windows = 1;
+    if (pipeline) {
+        while (group_windows < 4 && group_windows < static_cast<long long>(batch)) group_windows *= 2;
+        group_windows = std::max(group_windows, tile);
+    }
+
     // Batch slices: while one slice's recurrence runs (on 2·tiles/slices of the CUs), another
     // slice's projection uses the CUs it leaves idle. Only single-workgroup tiles: a split
     // tile's workgroups wait for each other, and two slices' launches partly resident at once
     // could then wait on each other for good.
-    const int want_slices = (opt != nullptr) ? opt->slices : 0;
-    const int projection = (opt != nullptr) ? opt->projection : 0;
     int slices = 1;
-    if (want_slices > 1) {
+    if (pipeline) {
+        // the streamed projection already runs beside the recurrence
+    } else if (want_slices > 1) {
         if (groups != 1 || concurrent == 1 || projection == 1) {
             return fail(BILSTM_UNSUPPORTED,
                         "schedule: %d slices need recur_groups = 1, concurrent != 1 and the library's own "
@@ -147,6 +183,8 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
     info->slices = slices;
     info->slice_windows = slice_windows;
     info->projection = projection;
+    info->pipeline = pipeline ? 1 : 0;
+    info->stream_chunk = pipeline ? kProjTileM / group_windows : 0;
     info->recur_groups = groups;
     info->recur_tile = tile;
     info->recur_tiles = tiles;

@@ -69,11 +69,24 @@ struct bilstm_plan {
     hipEvent_t ev_launch0[kLayers] = {nullptr, nullptr, nullptr, nullptr};
     hipEvent_t ev_launch1[kLayers] = {nullptr, nullptr, nullptr, nullptr};
     bool phases_recorded = false;
+    bool phases_streamed = false;  // the recorded forward streamed its gates
     // batch slices: each runs its own chain of layers on its own stream
     hipStream_t slice_stream[kMaxSlices] = {};
     hipEvent_t slice_fork = nullptr;
     hipEvent_t slice_first[kMaxSlices] = {};  // after the slice's first projection
     hipEvent_t slice_join[kMaxSlices] = {};
+    // streamed gates: the projection's stream, the second layer buffer, the chunk counters
+    hipStream_t proj_stream = nullptr;
+    hipEvent_t proj_fork = nullptr;
+    hipEvent_t proj_join = nullptr;
+    hipEvent_t layer_done[kLayers] = {nullptr, nullptr, nullptr, nullptr};
+    float *ybuf = nullptr;                 // [rows][256]: output of layers 0 and 2
+    unsigned long long *ready = nullptr;   // counters, two per word
+    size_t ready_words = 0;
+    int stream_groups = 0;
+    uint32_t ready_passes = 0;   // streamed layer passes since the counters were zeroed
+    bool ready_dirty = false;    // a streamed pass failed to enqueue: zero the counters first
+    int proj_workgroups_streamed = 0;
     size_t reserve_lds = 0;  // dynamic LDS of a recurrence workgroup (keeps its CU to itself)
     LibraryProjection *library = nullptr;  // vendor-GEMM projection (comparator), if chosen
     int proj_workgroups = 0;         // persistent projection workgroups on an idle GPU
@@ -167,6 +180,14 @@ void release(bilstm_plan *p) {
         if (p->slice_join[i]) (void)hipEventDestroy(p->slice_join[i]);
     }
     if (p->slice_fork) (void)hipEventDestroy(p->slice_fork);
+    for (int l = 0; l < kLayers; ++l) {
+        if (p->layer_done[l]) (void)hipEventDestroy(p->layer_done[l]);
+    }
+    if (p->proj_fork) (void)hipEventDestroy(p->proj_fork);
+    if (p->proj_join) (void)hipEventDestroy(p->proj_join);
+    if (p->proj_stream) (void)hipStreamDestroy(p->proj_stream);
+    if (p->ybuf) (void)hipFree(p->ybuf);
+    if (p->ready) (void)hipFree(p->ready);
     if (p->library) library_projection_destroy(p->library);
     if (p->gates) (void)hipFree(p->gates);
     if (p->exchange) (void)hipFree(p->exchange);
@@ -208,8 +229,10 @@ bilstm_status reserve_flags(bilstm_plan *p, uint32_t count, hipStream_t stream, 
 }
 
 // The projection of rows [row_first, row_first + rows) of x into the same rows of gates.
+// streamed: the whole batch in the recurrence's order, published on the plan's counters.
 bilstm_status enqueue_projection(bilstm_plan *p, int layer, const float *x, float *gates,
-                                 hipStream_t stream, size_t row_first, size_t rows, int workgroups) {
+                                 hipStream_t stream, size_t row_first, size_t rows, int workgroups,
+                                 bool streamed = false) {
     if (p->library != nullptr) {
         // the vendor GEMM was planned for the whole batch, which it always runs unsliced
         if (row_first != 0 || rows != p->rows) {
@@ -229,7 +252,17 @@ bilstm_status enqueue_projection(bilstm_plan *p, int layer, const float *x, floa
     args.kpad = p->kpad[layer];
     args.row_tiles = static_cast<int>((rows + kProjTileM - 1) / kProjTileM);
     args.tiles = args.row_tiles * (kGateCols / kProjTileN);
-    BL_HIP(launch_projection(args, workgroups, stream), "projection launch");
+    if (streamed) {
+        const int chunk = p->info.stream_chunk;
+        args.chunk = chunk;
+        args.group_windows = kProjTileM / chunk;
+        args.groups = p->stream_groups;
+        args.batch = static_cast<int>(p->batch);
+        args.steps = static_cast<int>(p->steps);
+        args.ready = reinterpret_cast<unsigned int *>(p->ready);
+        args.tiles = stream_chunks(args.steps, chunk) * 2 * args.groups * (kGates / kProjTileN);
+    }
+    BL_HIP(launch_projection(args, workgroups, streamed ? kProjStreamLds : 0, stream), "projection launch");
     return BILSTM_OK;
 }
 
@@ -238,7 +271,7 @@ bilstm_status enqueue_projection(bilstm_plan *p, int layer, const float *x, floa
 // the schedule allows it, joined back before the next layer).
 bilstm_status enqueue_recurrence(bilstm_plan *p, int layer, const float *gates, float *y,
                                  uint32_t flag_base, hipStream_t stream, bool layer_events,
-                                 int tile_lo, int tile_hi) {
+                                 int tile_lo, int tile_hi, bool streamed = false) {
     const bilstm_plan_info &s = p->info;
     RecurArgs base{};
     base.gates = gates;
@@ -252,6 +285,14 @@ bilstm_status enqueue_recurrence(bilstm_plan *p, int layer, const float *gates, 
     base.flag_base = flag_base;
     base.timeout_ticks = p->timeout_ticks;
     base.flag_skew = p->flag_skew;
+    if (streamed) {
+        base.ready = reinterpret_cast<const unsigned int *>(p->ready);
+        base.chunk = s.stream_chunk;
+        base.group_windows = kProjTileM / s.stream_chunk;
+        base.groups = p->stream_groups;
+        // a forced timeout expects a count no pass reaches
+        base.ready_target = p->ready_passes * static_cast<unsigned int>(kReadyPerPass) + p->flag_skew;
+    }
 
     const int per_launch = (s.recur_tiles + s.recur_launches - 1) / s.recur_launches;
     const size_t lds = p->reserve_lds;
@@ -287,6 +328,47 @@ bilstm_status enqueue_recurrence(bilstm_plan *p, int layer, const float *gates, 
     }
     if ((st = launch_direction(0, 1, stream)) != BILSTM_OK) return st;
     return launch_direction(1, 1, stream);
+}
+
+// The stack with streamed gates: per layer, the projection on the plan's projection stream
+// and the recurrence on the caller's stream run at the same time; the recurrence waits for
+// chunks the projection publishes. The next layer's projection waits for this layer's
+// recurrence (it reads its output and overwrites the gates). Layers 0 and 2 write the plan's
+// layer buffer, 1 and 3 write y, so a layer never writes rows its own projection may still
+// read.
+bilstm_status forward_streamed(bilstm_plan *p, const float *x, float *y, hipStream_t stream, uint32_t base) {
+    bilstm_status st;
+    if (p->ready_dirty || p->ready_passes > 0x0FFFFFFFu) {
+        // counters out of step with the pass count (a failed enqueue), or close to wrapping
+        BL_HIP(launch_exchange_clear(p->ready, p->ready_words, stream), "counter clear");
+        p->ready_passes = 0;
+        p->ready_dirty = false;
+    }
+    BL_HIP(hipEventRecord(p->proj_fork, stream), "projection fork");
+    BL_HIP(hipStreamWaitEvent(p->proj_stream, p->proj_fork, 0), "projection fork wait");
+    if (p->phase_events) BL_HIP(hipEventRecord(p->ev_start, stream), "phase event");
+    for (int l = 0; l < kLayers; ++l) {
+        const float *in = l == 0 ? x : (l % 2 == 1 ? p->ybuf : y);
+        float *out = l % 2 == 0 ? p->ybuf : y;
+        if (l > 0) BL_HIP(hipStreamWaitEvent(p->proj_stream, p->layer_done[l - 1], 0), "layer wait");
+        ++p->ready_passes;
+        if ((st = enqueue_projection(p, l, in, p->gates, p->proj_stream, 0, p->rows, p->proj_workgroups_streamed,
+                                     true)) != BILSTM_OK) {
+            return st;
+        }
+        if (p->phase_events) BL_HIP(hipEventRecord(p->ev_proj[l], p->proj_stream), "phase event");
+        if ((st = enqueue_recurrence(p, l, p->gates, out, base + l * p->steps, stream, true, 0, p->info.recur_tiles,
+                                     true)) != BILSTM_OK) {
+            return st;
+        }
+        BL_HIP(hipEventRecord(p->layer_done[l], stream), "layer event");
+        if (p->phase_events) BL_HIP(hipEventRecord(p->ev_recur[l], stream), "phase event");
+    }
+    BL_HIP(hipEventRecord(p->proj_join, p->proj_stream), "projection join");
+    BL_HIP(hipStreamWaitEvent(stream, p->proj_join, 0), "projection join wait");
+    p->phases_recorded = p->phase_events;
+    p->phases_streamed = true;
+    return BILSTM_OK;
 }
 
 bilstm_status check_plan_buffers(const char *context, const bilstm_plan *p, const void *a,
@@ -483,6 +565,34 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
             e = recurrence_allow_lds(info.recur_groups, info.recur_tile, p->reserve_lds);
         }
     }
+    if (e == hipSuccess && info.pipeline) {
+        // streamed gates: the second layer buffer, the chunk counters (zeroed), the projection's
+        // stream and the events that order it against the recurrence
+        const int group_windows = kProjTileM / info.stream_chunk;
+        p->stream_groups = static_cast<int>((batch + group_windows - 1) / group_windows);
+        const size_t counters = static_cast<size_t>(stream_chunks(static_cast<int>(steps), info.stream_chunk)) * 2 *
+                                p->stream_groups;
+        p->ready_words = (counters + 1) / 2;
+        if ((st = device_alloc(p, &p->ybuf, rows * kWidth, "layer buffer")) != BILSTM_OK) return fail_release(st);
+        if ((st = device_alloc(p, &p->ready, p->ready_words, "chunk counters")) != BILSTM_OK) return fail_release(st);
+        e = hipMemset(p->ready, 0, p->ready_words * sizeof(unsigned long long));
+        if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->proj_stream, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->proj_fork, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->proj_join, hipEventDisableTiming);
+        for (int l = 0; l < kLayers && e == hipSuccess; ++l) {
+            e = hipEventCreateWithFlags(&p->layer_done[l], hipEventDisableTiming);
+        }
+        // Each recurrence workgroup claims enough LDS that no projection workgroup fits beside
+        // it, and each streamed projection workgroup enough that no second one shares its CU:
+        // the projection's persistent grid then takes exactly the CUs the recurrence leaves.
+        if (e == hipSuccess) {
+            p->reserve_lds = kCuLdsBytes - kProjLdsBytes + 4096;
+            e = recurrence_allow_lds(info.recur_groups, info.recur_tile, p->reserve_lds);
+        }
+        if (e == hipSuccess) e = projection_allow_lds(kProjStreamLds);
+        p->proj_workgroups_streamed =
+            std::max(8, (cu_count - 2 * info.recur_tiles * info.recur_groups) / 8 * 8);
+    }
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         return fail_release(fail(BILSTM_HIP_ERROR, "plan_create: scratch setup: %s", hipGetErrorString(e)));
@@ -513,6 +623,11 @@ bilstm_status bilstm_forward(bilstm_plan *plan, const float *x, size_t x_len, fl
     uint32_t base = 0;
     if ((st = reserve_flags(plan, kLayers * plan->steps, stream, &base)) != BILSTM_OK) return st;
     const bilstm_plan_info &info = plan->info;
+    if (info.pipeline) {
+        st = forward_streamed(plan, x, y, stream, base);
+        if (st != BILSTM_OK) plan->ready_dirty = true;
+        return st;
+    }
     const int slices = info.slices;
     if (slices > 1) {
         // fork: every slice stream starts after the caller's prior work
@@ -560,6 +675,7 @@ bilstm_status bilstm_forward(bilstm_plan *plan, const float *x, size_t x_len, fl
         }
     }
     plan->phases_recorded = plan->phase_events;
+    plan->phases_streamed = false;
     return BILSTM_OK;
 }
 
@@ -631,7 +747,10 @@ bilstm_status bilstm_phase_times(bilstm_plan *plan, float *ms, size_t n) {
     for (int l = 0; l < kLayers; ++l) {
         hipEvent_t before = l == 0 ? plan->ev_start : plan->ev_recur[l - 1];
         BL_HIP(hipEventElapsedTime(&ms[l], before, plan->ev_proj[l]), "phase_times");
-        BL_HIP(hipEventElapsedTime(&ms[kLayers + l], plan->ev_proj[l], plan->ev_recur[l]), "phase_times");
+        // streamed: both phases from the layer's start; else the recurrence after the projection
+        BL_HIP(hipEventElapsedTime(&ms[kLayers + l], plan->phases_streamed ? before : plan->ev_proj[l],
+                                   plan->ev_recur[l]),
+               "phase_times");
         BL_HIP(hipEventElapsedTime(&ms[2 * kLayers + l], plan->ev_launch0[l], plan->ev_launch1[l]), "phase_times");
     }
     return BILSTM_OK;

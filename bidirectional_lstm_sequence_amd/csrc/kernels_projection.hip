@@ -27,7 +27,14 @@
 //    the matrix pipe idle while every tile of a round drains at once. In the 32x32 output
 //    layout one store instruction writes two full 128-byte row segments.
 //  * Every row's K order is fixed and independent of the row's position and of the grid, so a
-//    row's gates are bitwise the same whatever the batch or the number of workgroups.
+//    row's gates are bitwise the same whatever the batch, the number of workgroups or the
+//    tile order.
+//  * Streamed order (STREAM): the layer's recurrence runs at the same time on other CUs and
+//    reads the gates step by step. Tiles then cover `group_windows` windows × `chunk`
+//    consecutive recurrence steps of one direction and are walked chunk by chunk, so the
+//    gates arrive in the order they are read. A finished tile is stored at once (no overlap
+//    with the next tile: the recurrence, not this kernel, sets the pace) with agent-scope
+//    stores, and once they have completed, published by one counter increment per wave.
 #include <algorithm>
 
 #include "bilstm_internal.h"
@@ -50,7 +57,35 @@ static_assert(BM == 128 && BN == 128 && BK == 32 && kProjThreads == 256, "tile s
 static_assert(kLoadsPerThread == 4, "loads per thread");
 static_assert(2 * 2 * BM * kStride * sizeof(float) == kProjLdsBytes, "LDS size");
 
-template <int KSTEPS>
+// Row block of streamed tile q (the streamed layout of the internal header): its first window,
+// first step, direction, first gate column and publication counter.
+struct StreamTile {
+    int w0, s0, dir, n0, counter;
+};
+
+__device__ __forceinline__ StreamTile stream_tile(const ProjArgs &a, int q) {
+    const int ct = q & 3;
+    const int rest = q >> 2;
+    const int g = rest % a.groups;
+    const int cd = rest / a.groups;
+    StreamTile t;
+    t.dir = cd & 1;
+    t.w0 = g * a.group_windows;
+    t.s0 = (cd >> 1) * a.chunk;
+    t.n0 = t.dir * kGates + ct * BN;
+    t.counter = rest;  // (c·2 + d)·groups + g
+    return t;
+}
+
+// Gate row of local row r of a streamed tile, or -1 when r falls past the batch or the steps.
+__device__ __forceinline__ int stream_row(const ProjArgs &a, const StreamTile &t, int r) {
+    const int w = t.w0 + r / a.chunk;
+    const int s = t.s0 + r % a.chunk;
+    if (w >= a.batch || s >= a.steps) return -1;
+    return w * a.steps + (t.dir == 0 ? s : a.steps - 1 - s);
+}
+
+template <int KSTEPS, bool STREAM>
 __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a) {
     __shared__ __attribute__((aligned(16))) float lds_a[2][BM * kStride];
     __shared__ __attribute__((aligned(16))) float lds_b[2][BN * kStride];
@@ -68,16 +103,29 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a)
 
     // ---- global -> registers -> LDS staging of one K step -----------------------------------
     v4f ra[kLoadsPerThread], rb[kLoadsPerThread];
+    // STREAM: gate rows of this thread's staging rows tid / 8 + 32 j of the tile being loaded
+    int srow[kLoadsPerThread];
+    auto stream_rows = [&](int q) {
+        const StreamTile t = stream_tile(a, q);
+#pragma unroll
+        for (int j = 0; j < kLoadsPerThread; ++j) srow[j] = stream_row(a, t, (tid + kProjThreads * j) / kThreadsPerRow);
+    };
     auto load = [&](int m0, int n0, int k0) {
 #pragma unroll
         for (int j = 0; j < kLoadsPerThread; ++j) {
             const int f = tid + kProjThreads * j;
             const int row = f / kThreadsPerRow;
             const int k = k0 + (f % kThreadsPerRow) * 4;
-            const int m = m0 + row;
             v4f va = {0.f, 0.f, 0.f, 0.f};
-            if (m < a.rows && k < a.in) {
-                va = *reinterpret_cast<const v4f *>(a.x + static_cast<size_t>(m) * a.in + k);
+            if constexpr (STREAM) {
+                if (srow[j] >= 0 && k < a.in) {
+                    va = *reinterpret_cast<const v4f *>(a.x + static_cast<size_t>(srow[j]) * a.in + k);
+                }
+            } else {
+                const int m = m0 + row;
+                if (m < a.rows && k < a.in) {
+                    va = *reinterpret_cast<const v4f *>(a.x + static_cast<size_t>(m) * a.in + k);
+                }
             }
             ra[j] = va;
             rb[j] = *reinterpret_cast<const v4f *>(a.w + static_cast<size_t>(n0 + row) * a.kpad + k);
@@ -126,10 +174,15 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a)
         }
     };
 
+    // tile q's output columns and (plain order) first row
+    auto tile_n0 = [&](int q) { return STREAM ? stream_tile(a, q).n0 : (q % kColTiles) * BN; };
+    auto tile_m0 = [&](int q) { return STREAM ? 0 : (q / kColTiles) * BM; };
+
     int q = first;
     int base = 0;  // LDS buffer of the tile's first K step
     if (q < a.tiles) {
-        load((q / kColTiles) * BM, (q % kColTiles) * BN, 0);
+        if constexpr (STREAM) stream_rows(q);
+        load(tile_m0(q), tile_n0(q), 0);
         store(0);
     }
     __syncthreads();
@@ -137,10 +190,16 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a)
     frags(0, 0, af[0], bf[0]);
 
     for (; q < a.tiles; q += nwg) {
-        const int m0 = (q / kColTiles) * BM;
-        const int n0 = (q % kColTiles) * BN;
+        const int m0 = tile_m0(q);
+        const int n0 = tile_n0(q);
         const int qn = q + nwg;
         const bool next = qn < a.tiles;
+        // STREAM: the tile's bias, loaded now so that it has arrived long before the stores
+        float sbias[2] = {0.0f, 0.0f};
+        if constexpr (STREAM) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) sbias[j] = a.bias[n0 + wn * 64 + j * 32 + (lane & 31)];
+        }
 
         v16f acc[2][2];
 #pragma unroll
@@ -158,7 +217,8 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a)
             if (more) {
                 load(m0, n0, (kt + 1) * BK);
             } else if (next) {
-                load((qn / kColTiles) * BM, (qn % kColTiles) * BN, 0);
+                if constexpr (STREAM) stream_rows(qn);
+                load(tile_m0(qn), tile_n0(qn), 0);
             }
 #pragma unroll
             for (int g = 0; g < kGroups; ++g) {
@@ -172,28 +232,65 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a)
                         for (int j = 0; j < 2; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[p][i][e], bf[p][j][e],
                                                                              acc[i][j], 0, 0, 0);
-                if (g == kGroups / 2 && have) put_chunk(kt);
+                if (!STREAM && g == kGroups / 2 && have) put_chunk(kt);
             }
             if (more || next) store(cur ^ 1);
             __syncthreads();
             if (more || next) frags(cur ^ 1, 0, af[0], bf[0]);
         }
 
-        // this tile's sums plus bias become the pending output of the next tile
+        if constexpr (STREAM) {
+            // store now with agent-scope stores, wait for them to complete, then publish (one
+            // counter increment per wave)
+            const StreamTile t = stream_tile(a, q);
+            float *const gcol = a.gates + n0 + wn * 64 + (lane & 31);
+            auto put_row = [&](int i, int r, int m) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const float bv = a.bias[n0 + wn * 64 + j * 32 + (lane & 31)];
+                for (int j = 0; j < 2; ++j) {
+                    __hip_atomic_store(gcol + static_cast<size_t>(m) * kGateCols + j * 32, acc[i][j][r] + sbias[j],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            };
+            if (t.w0 + a.group_windows <= a.batch && t.s0 + a.chunk <= a.steps) {
+                // every row of the tile exists (all but the ragged last chunk and group)
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) pend[i][j][r] = acc[i][j][r] + bv;
+                    for (int r = 0; r < 16; ++r) {
+                        const int lr = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                        const int sr = t.s0 + lr % a.chunk;
+                        put_row(i, r, (t.w0 + lr / a.chunk) * a.steps + (t.dir == 0 ? sr : a.steps - 1 - sr));
+                    }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = stream_row(a, t, wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3));
+                        if (m >= 0) put_row(i, r, m);
+                    }
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            if (lane == 0) {
+                __hip_atomic_fetch_add(a.ready + t.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        } else {
+            // this tile's sums plus bias become the pending output of the next tile
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float bv = a.bias[n0 + wn * 64 + j * 32 + (lane & 31)];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) pend[i][j][r] = acc[i][j][r] + bv;
+            }
+            pm0 = m0;
+            pn0 = n0;
+            have = true;
         }
-        pm0 = m0;
-        pn0 = n0;
-        have = true;
         base = (base + KSTEPS) & 1;
     }
-    if (have) {
+    if (!STREAM && have) {
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) put_chunk(s);
     }
@@ -383,12 +480,21 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_split_kernel(ProjA
 
 }  // namespace
 
-hipError_t launch_projection(const ProjArgs &args, int workgroups, hipStream_t stream) {
+hipError_t projection_allow_lds(size_t bytes) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&projection_kernel<2, true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&projection_kernel<8, true>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+}
+
+hipError_t launch_projection(const ProjArgs &args, int workgroups, size_t dynamic_lds, hipStream_t stream) {
     if (args.tiles <= 0) return hipSuccess;
     // a multiple of 8 (the XCD-ordered walk), at most one workgroup per tile group of 8
     int nwg = std::min(workgroups, (args.tiles + 7) / 8 * 8);
     nwg = std::max(8, nwg / 8 * 8);
     if (args.w_hi != nullptr) {
+        if (args.chunk > 0) return hipErrorInvalidValue;  // streamed order: FP32 kernel only
         switch (args.kpad / kProjTileK) {
             case 2:
                 hipLaunchKernelGGL(projection_split_kernel<2>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
@@ -401,12 +507,22 @@ hipError_t launch_projection(const ProjArgs &args, int workgroups, hipStream_t s
         }
         return hipGetLastError();
     }
+    const bool streamed = args.chunk > 0;
+    if (streamed && (args.ready == nullptr || args.chunk * args.group_windows != BM)) return hipErrorInvalidValue;
     switch (args.kpad / kProjTileK) {
         case 2:
-            hipLaunchKernelGGL(projection_kernel<2>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
+            if (streamed) {
+                hipLaunchKernelGGL((projection_kernel<2, true>), dim3(nwg), dim3(kProjThreads), dynamic_lds, stream, args);
+            } else {
+                hipLaunchKernelGGL((projection_kernel<2, false>), dim3(nwg), dim3(kProjThreads), 0, stream, args);
+            }
             break;
         case 8:
-            hipLaunchKernelGGL(projection_kernel<8>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
+            if (streamed) {
+                hipLaunchKernelGGL((projection_kernel<8, true>), dim3(nwg), dim3(kProjThreads), dynamic_lds, stream, args);
+            } else {
+                hipLaunchKernelGGL((projection_kernel<8, false>), dim3(nwg), dim3(kProjThreads), 0, stream, args);
+            }
             break;
         default:
             return hipErrorInvalidValue;

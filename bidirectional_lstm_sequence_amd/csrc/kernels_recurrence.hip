@@ -30,6 +30,13 @@
 // would drain them), so wave 0 prefetches the workgroup's gates into an LDS ring and does not
 // poll; waves 1.. poll.
 //
+// Streamed gates (STREAM, KG = 1): the layer's projection runs at the same time on other CUs
+// and publishes the gates chunk by chunk. Before the gate loads of a group of kRing steps are
+// issued, the chunk counter read one group earlier must show the chunk published (else the
+// wave polls until it does); the counter of the group after next is read at the same point,
+// so in the steady state no wave ever waits for a counter. Gate loads are then agent-scope
+// loads, which see the projection's stores once its release and counter are observed.
+//
 // Waits are bounded: a poll that sees no progress for `timeout_ticks` wall-clock ticks
 // sets the error word and stops waiting, so the grid always drains.
 #include "bilstm_internal.h"
@@ -39,7 +46,10 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kRing = 4;  // prefetch depth in steps
+// Prefetch depth in steps: gate loads of step s are issued at step s - depth. Streamed gates
+// are read with agent-scope loads, which go past the L2, so they are issued further ahead.
+constexpr int kRingPlain = 4;
+constexpr int kRingStream = 8;
 
 // Padded h index: 4 floats of padding after every 32, so the four K quarters of h start on
 // different LDS banks.
@@ -87,11 +97,22 @@ struct Slot {
     static constexpr int value = N;
 };
 
-template <int KG, int BT>
+// f(Slot<P>{}) for P = FIRST .. LAST - 1, as straight-line code.
+template <int FIRST, int LAST, typename F>
+__device__ __forceinline__ void for_slots(F &&f) {
+    if constexpr (FIRST < LAST) {
+        f(Slot<FIRST>{});
+        for_slots<FIRST + 1, LAST>(f);
+    }
+}
+
+template <int KG, int BT, bool STREAM>
 __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArgs a) {
     constexpr int U = kHidden / KG;  // units per workgroup
     constexpr int NT = 4 * U;        // threads
     static_assert(KG == 1 || NT >= 128, "a polling wave besides the staging wave");
+    static_assert(!STREAM || KG == 1, "streamed gates: single-workgroup tiles only");
+    constexpr int kRing = STREAM ? kRingStream : kRingPlain;
 
     // ---- which tile, member and direction ------------------------------------------------
     int tile, member;
@@ -152,8 +173,42 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
     auto gate_in = [&](int b, int s) -> float {
         const int w = (win0 + b < a.batch) ? win0 + b : win0;
         const int sc = s < steps ? s : steps - 1;
-        return a.gates[(static_cast<size_t>(w) * steps + time_of(sc)) * kGateCols + gate_col];
+        const float *p = a.gates + (static_cast<size_t>(w) * steps + time_of(sc)) * kGateCols + gate_col;
+        if constexpr (STREAM) {
+            return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            return *p;
+        }
     };
+
+    // STREAM: publication counter of the chunk holding step s (clamped to the last step) for
+    // this tile's window group and direction
+    bool timed_out = false;
+    const unsigned int *ready_tile =
+        STREAM ? a.ready + static_cast<size_t>(dir) * a.groups + win0 / a.group_windows : nullptr;
+    auto ready_ptr = [&](int s) {
+        const int sc = s < steps ? s : steps - 1;
+        return ready_tile + static_cast<size_t>(sc / a.chunk) * 2 * a.groups;
+    };
+    auto read_ready = [&](int s) -> unsigned int {
+        return __hip_atomic_load(ready_ptr(s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto published = [&](unsigned int v) { return static_cast<int>(v - a.ready_target) >= 0; };
+    // Wait until the chunk of step s is published; `seen` is a counter value read earlier.
+    auto wait_ready = [&](unsigned int seen, int s) {
+        if (__builtin_expect(published(seen) || timed_out, 1)) return;
+        const unsigned long long t0 = wall_clock64();
+        while (true) {
+            __builtin_amdgcn_s_sleep(1);
+            if (published(read_ready(s))) break;
+            if (wall_clock64() - t0 > a.timeout_ticks) {
+                atomicOr(a.error, 2u);
+                timed_out = true;
+                break;
+            }
+        }
+    };
+    unsigned int ready_seen = 0;  // counter of the chunk of the group after the current one
     float *const ycol = a.y + static_cast<size_t>(win0 + qe) * steps * kWidth + dir * kHidden + ug;
 
     // KG == 1: per-lane register ring of gate inputs.
@@ -172,6 +227,10 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
     };
 
     if constexpr (KG == 1) {
+        if constexpr (STREAM) {
+            wait_ready(read_ready(0), 0);
+            ready_seen = read_ready(kRing);
+        }
 #pragma unroll
         for (int p = 0; p < kRing; ++p)
 #pragma unroll
@@ -202,7 +261,6 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
     }
     const bool is_g = q == 2;
     float cst = 0.0f;  // cell state of (unit ug, window qe)
-    bool timed_out = false;
 
     // One step s; P is the step's slot in the prefetch ring (s mod kRing), a compile-time
     // constant so the ring stays in registers.
@@ -210,6 +268,13 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
         constexpr int P = decltype(slot)::value;
         const int cur = s & 1;
         const int nxt = cur ^ 1;
+
+        if constexpr (STREAM && P == 0) {
+            // this group refills the ring with steps s + kRing .. s + 2·kRing - 1 (one chunk):
+            // check the counter read a group ago, and read the one for the next group
+            wait_ready(ready_seen, s + kRing);
+            ready_seen = read_ready(s + 2 * kRing);
+        }
 
         // (1) partial dot products over this lane's K quarter
         float acc[4][BT];
@@ -328,15 +393,11 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
     // the compiler's memory-wait counting exact; the last partial group is guarded.
     int s0 = 0;
     for (; s0 + kRing <= steps; s0 += kRing) {
-        step(s0 + 0, Slot<0>{});
-        step(s0 + 1, Slot<1>{});
-        step(s0 + 2, Slot<2>{});
-        step(s0 + 3, Slot<3>{});
+        for_slots<0, kRing>([&](auto slot) { step(s0 + decltype(slot)::value, slot); });
     }
-    static_assert(kRing == 4, "the unrolled groups assume a ring of 4");
-    if (s0 + 0 < steps) step(s0 + 0, Slot<0>{});
-    if (s0 + 1 < steps) step(s0 + 1, Slot<1>{});
-    if (s0 + 2 < steps) step(s0 + 2, Slot<2>{});
+    for_slots<0, kRing - 1>([&](auto slot) {
+        if (s0 + decltype(slot)::value < steps) step(s0 + decltype(slot)::value, slot);
+    });
 }
 
 __global__ void exchange_clear_kernel(unsigned long long *words, size_t count) {
@@ -390,20 +451,33 @@ __global__ void exchange_probe_kernel(unsigned long long *words, int partner, in
 template <int KG, int BT>
 hipError_t launch_typed(const RecurArgs &args, int directions, size_t lds, hipStream_t stream) {
     const int nwg = KG == 1 ? args.tile_count : (args.tile_count + 7) / 8 * 8 * KG;
-    hipLaunchKernelGGL((recurrence_kernel<KG, BT>), dim3(nwg, directions), dim3(recur_threads(KG)), lds,
+    if constexpr (KG == 1) {
+        if (args.chunk > 0) {
+            hipLaunchKernelGGL((recurrence_kernel<KG, BT, true>), dim3(nwg, directions), dim3(recur_threads(KG)),
+                               lds, stream, args);
+            return hipGetLastError();
+        }
+    } else {
+        if (args.chunk > 0) return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL((recurrence_kernel<KG, BT, false>), dim3(nwg, directions), dim3(recur_threads(KG)), lds,
                        stream, args);
     return hipGetLastError();
 }
 
 template <int KG, int BT>
 hipError_t allow_lds_typed(size_t bytes) {
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&recurrence_kernel<KG, BT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&recurrence_kernel<KG, BT, false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+    if (e != hipSuccess || KG != 1) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&recurrence_kernel<KG, BT, KG == 1>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
 }
 
 template <int KG, int BT>
 hipError_t occupancy_typed(int *per_cu) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, recurrence_kernel<KG, BT>, recur_threads(KG), 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, recurrence_kernel<KG, BT, false>, recur_threads(KG),
+                                                        0);
 }
 
 #define BL_FOR_EACH_SPLIT(X) X(1, 1) X(1, 2) X(1, 4) X(2, 1) X(2, 2) X(2, 4) X(4, 1) X(4, 2) X(4, 4)

@@ -108,7 +108,22 @@ typedef struct {
                              each FP32 operand split into two bf16 parts, three bf16 MFMA
                              products per K chunk (hi·hi + hi·lo + lo·hi) accumulated in FP32,
                              |error| <= (3·2^-16·(1 + 2^-7) + (3K + 2)·2^-24)·sum|x·w| per gate */
-    int32_t reserved[2];  /* must be zero */
+    int32_t pipeline;     /* streamed gates for bilstm_forward: each layer's projection runs beside
+                             that layer's recurrence on the CUs the recurrence leaves free, computes
+                             the gates in the order the recurrence reads them (chunks of steps,
+                             per direction) and publishes each chunk through a counter the
+                             recurrence polls; layers alternate between y and a plan-owned
+                             buffer, so no layer overwrites rows its projection still reads.
+                             The output is bitwise the same as without it.
+                             0 = auto (on from 16 windows when recur_groups = 1, the
+                             recurrence's grid leaves at least a quarter of the CUs free and
+                             projection = 0), 1 = off,
+                             2 = on (BILSTM_UNSUPPORTED unless recur_groups = 1, projection = 0,
+                             slices <= 1 and at least 8 CUs stay free). The recurrence's waits
+                             on the counters are bounded by the watchdog like every other wait:
+                             if the GPU is shared with other work that keeps the projection from
+                             running, bilstm_check reports BILSTM_TIMEOUT instead of hanging */
+    int32_t reserved[1];  /* must be zero */
 } bilstm_options;
 
 /* What a plan chose; filled by bilstm_plan_get_info. */
@@ -129,6 +144,9 @@ typedef struct {
     int32_t slices;          /* batch slices bilstm_forward runs as concurrent chains */
     int32_t slice_windows;   /* windows per slice (the last slice may hold fewer) */
     int32_t projection;      /* 0 own FP32-MFMA kernel, 1 vendor GEMM, 2 own split-precision */
+    int32_t pipeline;        /* 1 when bilstm_forward streams the gates (see bilstm_options) */
+    int32_t stream_chunk;    /* streamed gates: recurrence steps per published chunk (128 /
+                                windows per projection row block); 0 when not streamed */
 } bilstm_plan_info;
 
 /*
@@ -150,9 +168,11 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
  * The whole stack (page `lstmproj.rs`, `Oxide::enqueue`).
  *   x [batch][steps][60]  device, fp32, 16-byte aligned; read only; x_len = batch·steps·60
  *   y [batch][steps][256] device, fp32, 16-byte aligned; y_len = batch·steps·256
- * y doubles as the inter-layer buffer, updated in place layer by layer: a layer's
- * projection has consumed all of the previous layer's output by the time its recurrence
- * starts writing (page `lstmproj.rs`, module doc).
+ * y doubles as the inter-layer buffer. Without streamed gates it is updated in place layer by
+ * layer: a layer's projection has consumed all of the previous layer's output by the time its
+ * recurrence starts writing (page `lstmproj.rs`, module doc). With streamed gates
+ * (bilstm_options.pipeline) a layer's projection still reads while its recurrence writes, so
+ * layers 0 and 2 write a plan-owned buffer and layers 1 and 3 write y.
  * x and y must not overlap. Asynchronous on `stream`.
  */
 bilstm_status bilstm_forward(bilstm_plan *plan, const float *x, size_t x_len, float *y,
@@ -193,7 +213,9 @@ bilstm_status bilstm_check(bilstm_plan *plan);
  * writes 12 values in milliseconds: projection of layers 0..3; recurrence phase of layers
  * 0..3 (both directions, including any join); duration of the first recurrence launch on the
  * caller's stream of layers 0..3 (the launch running both directions when they share one
- * launch, else the forward direction's). n must be >= 12.
+ * launch, else the forward direction's). n must be >= 12. With streamed gates the two phases
+ * of a layer overlap: both are then measured from the layer's start (the end of the previous
+ * layer's recurrence), the projection to its end and the recurrence to its end.
  */
 bilstm_status bilstm_set_phase_events(bilstm_plan *plan, int enable);
 bilstm_status bilstm_phase_times(bilstm_plan *plan, float *ms, size_t n);

@@ -1,0 +1,129 @@
+"""GPU: streamed gates (each layer's projection beside its own recurrence, published chunk by
+chunk through counters the recurrence polls).
+
+The projection's per-row sum and the recurrence do not depend on the order tiles run in, so a
+streamed forward must equal the unstreamed one bit for bit, for every batch and sequence
+shape (ragged row blocks, sequences shorter than one chunk or than the prefetch ring), over
+repeated forwards on one plan (the counters' targets advance per pass), and the oracle bounds
+it as it does the default path.
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-5
+RTOL = 1e-4
+
+
+def note(msg: str) -> None:
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def bl():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bidirectional_lstm_sequence_amd as bl
+    bl.library()  # fails loudly if the HIP library was not built
+    return bl
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    oracle.build(force=False)
+    return oracle
+
+
+def run(bl, x, layers, repeats=1, **kw):
+    plan = bl.Plan(layers, x.shape[0], x.shape[1], **kw)
+    xd = torch.from_numpy(x).cuda()
+    outs = [plan.forward(xd).cpu().numpy() for _ in range(repeats)]
+    plan.check()
+    info = plan.info()
+    plan.close()
+    return outs, info
+
+
+# (batch, steps, tile): one window (chunks of 128 steps), two (64), three and more (32); steps
+# below one chunk, below the 8 steps the counters are read ahead, not a multiple of the chunk
+SHAPES = [(1, 589, 0), (1, 1, 0), (2, 130, 0), (3, 150, 0), (3, 3, 0), (5, 7, 0), (4, 33, 0), (8, 200, 0),
+          (8, 97, 2), (8, 64, 4), (32, 150, 0)]
+
+
+@pytest.mark.parametrize("batch,steps,tile", SHAPES)
+def test_streamed_equals_unstreamed_bitwise(bl, batch, steps, tile):
+    x = workloads.make_input(40 + batch, batch, steps)
+    layers = workloads.make_layers(41)
+    note(f"streamed vs unstreamed batch={batch} steps={steps} tile={tile}")
+    got, info = run(bl, x, layers, pipeline=2, tile=tile)
+    base, binfo = run(bl, x, layers, pipeline=1, slices=1, tile=tile)
+    assert info["pipeline"] == 1 and binfo["pipeline"] == 0
+    assert np.array_equal(got[0].view(np.uint32), base[0].view(np.uint32))
+
+
+def test_streamed_repeated_forwards_are_bit_stable(bl):
+    """Five forwards on one plan: each pass's counters reach the next target exactly once."""
+    x, layers = workloads.make_workload("b8")
+    xs = np.ascontiguousarray(x[:, :150])
+    note("streamed repeated forwards b8 t150 x5")
+    outs, info = run(bl, xs, layers, repeats=5, pipeline=2)
+    assert info["pipeline"] == 1
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+
+
+def test_streamed_matches_oracle(bl, orc):
+    x, layers = workloads.make_workload("b8")
+    note("streamed b8 against the oracle")
+    outs, info = run(bl, x, layers, pipeline=2)
+    ref = orc.stack(x, layers, threads=min(16, os.cpu_count() or 1))
+    err = np.abs(outs[0].astype(np.float64) - ref)
+    assert np.all(err <= ATOL + RTOL * np.abs(ref)), f"max abs err {err.max():.3e}"
+    note(f"streamed b8 max abs err {err.max():.3e} chunk {info['stream_chunk']}")
+
+
+def test_streamed_phase_times(bl):
+    x, layers = workloads.make_workload("b8")
+    xs = np.ascontiguousarray(x[:, :100])
+    note("streamed phase times")
+    plan = bl.Plan(layers, 8, 100, pipeline=2)
+    xd = torch.from_numpy(xs).cuda()
+    plan.forward(xd)
+    plan.set_phase_events(True)
+    plan.forward(xd)
+    t = plan.phase_times()
+    plan.check()
+    plan.close()
+    for l in range(4):
+        # both measured from the layer's start; the recurrence needs the projection's chunks
+        assert 0 < t["projection_ms"][l] and 0 < t["recurrence_ms"][l]
+        assert 0 < t["recurrence_launch_ms"][l] <= t["recurrence_ms"][l] + 1e-3
+
+
+def test_streamed_watchdog_reports_timeout_and_grid_drains(bl):
+    """Counter waits forced to time out from the host (watchdog_us = -1: every wait expects a
+    count no pass reaches and gives up on its first poll): the kernels finish and the plan
+    reports BILSTM_TIMEOUT; a normal plan afterwards is unaffected."""
+    x, layers = workloads.make_workload("b8")
+    xs = np.ascontiguousarray(x[:, :64])
+    note("streamed watchdog first-miss")
+    plan = bl.Plan(layers, 8, 64, pipeline=2, watchdog_us=-1)
+    plan.forward(torch.from_numpy(xs).cuda())
+    with pytest.raises(bl.BilstmError) as e:
+        plan.check()
+    assert e.value.name == "BILSTM_TIMEOUT"
+    plan.check()
+    plan.close()
+    got, _ = run(bl, xs, layers, pipeline=2)
+    base, _ = run(bl, xs, layers, pipeline=1)
+    assert np.array_equal(got[0].view(np.uint32), base[0].view(np.uint32))

@@ -125,8 +125,9 @@ def test_schedule_refuses_concurrency_that_cannot_be_resident(bl):
 @pytest.mark.parametrize("slices", [0, 1, 2, 3, 4, 8])
 def test_schedule_slices_cover_the_batch(bl, batch, slices):
     """Slices are whole tiles, cover every window once, and the auto choice slices only when
-    the recurrence leaves at least half of the CUs idle."""
-    s = bl.schedule(batch, 589, 256, 1, slices=slices)
+    the recurrence leaves at least half of the CUs idle (streamed gates off: they replace the
+    slices when on)."""
+    s = bl.schedule(batch, 589, 256, 1, slices=slices, pipeline=1)
     n, w, tile = s["slices"], s["slice_windows"], s["recur_tile"]
     assert 1 <= n <= max(1, slices if slices else 2)
     assert w % tile == 0 or w == batch
@@ -142,7 +143,7 @@ def test_schedule_slices_need_single_workgroup_tiles(bl):
             bl.schedule(32, 589, 256, 1, slices=4, **kwargs)
         assert e.value.name == "BILSTM_UNSUPPORTED"
         assert bl.schedule(32, 589, 256, 1, **kwargs)["slices"] == 1
-    assert bl.schedule(32, 589, 256, 1)["slices"] == 2
+    assert bl.schedule(32, 589, 256, 1, pipeline=1)["slices"] == 2
     assert bl.schedule(256, 589, 256, 1)["slices"] == 1
 
 
@@ -150,18 +151,53 @@ def test_schedule_library_projection_runs_unsliced(bl):
     s = bl.schedule(32, 589, 256, 1, projection=1)
     assert s["projection"] == 1 and s["slices"] == 1
     assert bl.schedule(32, 589, 256, 1)["projection"] == 0
-    s = bl.schedule(32, 589, 256, 1, projection=2)  # own split-precision kernel: sliced like FP32
-    assert s["projection"] == 2 and s["slices"] == 2
+    s = bl.schedule(32, 589, 256, 1, projection=2)  # own split-precision kernel: sliced, not streamed
+    assert s["projection"] == 2 and s["slices"] == 2 and s["pipeline"] == 0
     with pytest.raises(bl.BilstmError) as e:
         bl.schedule(32, 589, 256, 1, projection=1, slices=2)
     assert e.value.name == "BILSTM_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("batch,steps,on,chunk", [(1, 589, 0, 0), (8, 589, 0, 0), (15, 589, 0, 0), (16, 589, 1, 32),
+                                                   (32, 589, 1, 32), (64, 4096, 1, 32),
+                                                   (96, 589, 1, 32), (97, 589, 0, 0), (256, 589, 0, 0)])
+def test_schedule_streams_gates_when_the_recurrence_leaves_cus(bl, batch, steps, on, chunk):
+    """Auto: streamed gates from 16 windows on, when the recurrence's grid (one workgroup per
+    window and direction) leaves at least a quarter of the 256 CUs to the projection; they
+    replace the batch slices."""
+    s = bl.schedule(batch, steps, 256, 1)
+    assert s["pipeline"] == on and s["stream_chunk"] == chunk
+    if on:
+        assert s["slices"] == 1 and s["recur_groups"] == 1 and s["concurrent"] == 2
+        assert 4 * 2 * s["recur_tiles"] <= 3 * 256
+        # a chunk's row block of 128 rows holds whole windows, a whole number of recurrence tiles
+        assert 128 % chunk == 0 and (128 // chunk) % s["recur_tile"] == 0 and chunk % 4 == 0
+
+
+def test_schedule_forced_streaming_checks_its_conditions(bl):
+    s = bl.schedule(8, 589, 256, 1, pipeline=2, tile=4)
+    assert s["pipeline"] == 1 and s["stream_chunk"] == 32 and s["recur_tile"] == 4
+    for batch, chunk in ((1, 128), (2, 64), (3, 32)):  # row blocks of 1, 2 and 4 windows
+        assert bl.schedule(batch, 589, 256, 1, pipeline=2)["stream_chunk"] == chunk
+    s = bl.schedule(120, 589, 256, 1, pipeline=2)  # 240 + 8 <= 256: allowed when asked for
+    assert s["pipeline"] == 1
+    for kwargs in (dict(groups=2), dict(projection=1), dict(projection=2), dict(slices=2)):
+        with pytest.raises(bl.BilstmError) as e:
+            bl.schedule(32, 589, 256, 1, pipeline=2, **kwargs)
+        assert e.value.name == "BILSTM_UNSUPPORTED"
+        assert bl.schedule(32, 589, 256, 1, **kwargs)["pipeline"] == 0
+    with pytest.raises(bl.BilstmError) as e:
+        bl.schedule(256, 589, 256, 1, pipeline=2)  # the recurrence takes every CU
+    assert e.value.name == "BILSTM_UNSUPPORTED"
+    assert bl.schedule(32, 589, 256, 1, pipeline=1)["pipeline"] == 0
 
 
 @pytest.mark.parametrize("kwargs,status", [
     (dict(groups=3), "BILSTM_UNSUPPORTED"), (dict(tile=3), "BILSTM_UNSUPPORTED"),
     (dict(concurrent=5), "BILSTM_INVALID_ARGUMENT"), (dict(slices=9), "BILSTM_INVALID_ARGUMENT"),
     (dict(slices=-1), "BILSTM_INVALID_ARGUMENT"), (dict(projection=3), "BILSTM_INVALID_ARGUMENT"),
-    (dict(projection=-1), "BILSTM_INVALID_ARGUMENT")])
+    (dict(projection=-1), "BILSTM_INVALID_ARGUMENT"), (dict(pipeline=3), "BILSTM_INVALID_ARGUMENT"),
+    (dict(pipeline=-1), "BILSTM_INVALID_ARGUMENT")])
 def test_schedule_rejects_bad_options(bl, kwargs, status):
     with pytest.raises(bl.BilstmError) as e:
         bl.schedule(8, 589, 256, 1, **kwargs)
