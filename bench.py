@@ -103,8 +103,8 @@ def main() -> int:
     ap.add_argument("--slices", type=int, default=0)
     ap.add_argument("--projection", type=int, default=0, choices=(0, 1, 2),
                     help="0 own FP32-MFMA kernel (default), 1 vendor GEMM, 2 own split-precision kernel")
-    ap.add_argument("--pipeline", type=int, default=0, choices=(0, 1, 2),
-                    help="streamed gates: 0 auto, 1 off, 2 on")
+    ap.add_argument("--pipeline", type=int, default=0, choices=(0, 1, 2, 3, 4),
+                    help="streamed gates: 0 auto, 1 off, 2 on, 3 on without and 4 on with layer overlap")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -279,7 +279,8 @@ def main() -> int:
                    "recurrence_split": {"groups": groups, "tile": tile, "tiles": info["recur_tiles"],
                                         "concurrent": info["concurrent"]},
                    "slices": info["slices"], "slice_windows": info["slice_windows"],
-                   "streamed_gates": {"on": bool(info["pipeline"]), "chunk_steps": info["stream_chunk"]}},
+                   "streamed_gates": {"on": bool(info["pipeline"]), "chunk_steps": info["stream_chunk"],
+                                      "layers_overlap": bool(info["stream_overlap"])}},
         "roofline": {"kernel": f"recurrence_kernel<{groups}, {tile}, {'true' if info['pipeline'] else 'false'}> "
                                f"({launch_dirs} direction(s) per launch"
                                f"{', streamed gates' if info['pipeline'] else ''})",

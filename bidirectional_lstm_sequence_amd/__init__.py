@@ -79,7 +79,8 @@ class PlanInfo(ctypes.Structure):
                 ("cu_count", ctypes.c_int32), ("recur_capacity", ctypes.c_int32),
                 ("device_bytes", ctypes.c_uint64), ("slices", ctypes.c_int32),
                 ("slice_windows", ctypes.c_int32), ("projection", ctypes.c_int32),
-                ("pipeline", ctypes.c_int32), ("stream_chunk", ctypes.c_int32)]
+                ("pipeline", ctypes.c_int32), ("stream_chunk", ctypes.c_int32),
+                ("stream_overlap", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -230,7 +231,9 @@ class Plan:
     slices the forward runs as concurrent chains (0 = auto, 1 = off); ``projection`` = 1 runs
     the input projection through the vendor GEMM (hipBLASLt) instead of the library's kernel,
     2 through the library's split-precision kernel; ``pipeline`` streams each layer's gates
-    from its projection into its recurrence while both run (0 = auto, 1 = off, 2 = on).
+    from its projection into its recurrence while both run (0 = auto, 1 = off, 2 = on, 3 = on with
+    each projection after the previous layer's recurrence, 4 = on with the next layer's projection
+    during this layer's recurrence).
     """
 
     def __init__(self, layers, batch: int, steps: int, device: int = 0, groups: int = 0,

@@ -58,11 +58,21 @@ struct ProjArgs {
     // Streamed order (chunk > 0): tiles follow the recurrence's consumption order and each
     // finished tile is published on `ready` (layout below). chunk = 0: plain row-major tiles.
     int chunk;           // recurrence steps per tile row block (128 / group_windows)
+    int chunk_shift;     // log2(chunk)
     int group_windows;   // windows per tile row block
     int groups;          // ceil(batch / group_windows)
     int batch;
     int steps;
-    unsigned int *ready;  // [chunks][2][groups] publication counters
+    unsigned int *ready;      // [chunks][2][groups] publication counters
+    const int *chunk_order;   // [chunks]: the walk takes chunk chunk_order[i] i-th
+    // Inputs written by the previous layer's recurrence while this projection runs
+    // (progress != nullptr): before a tile's rows are read, each of its windows' progress word
+    // in both directions must reach progress_pass | steps the rows need (see StreamLayout);
+    // the rows are then read with agent-scope loads.
+    const unsigned long long *progress;  // [batch][2]
+    unsigned long long progress_pass;    // (previous layer's pass number) << 32
+    unsigned int *error;                 // watchdog flag word
+    unsigned long long timeout_ticks;
 };
 
 struct RecurArgs {
@@ -88,6 +98,10 @@ struct RecurArgs {
     int group_windows;
     int groups;
     unsigned int ready_target;
+    // Streamed gates: the output is written with agent-scope stores and, every few steps, each
+    // window's progress[window][dir] = progress_pass | (steps whose output has completed).
+    unsigned long long *progress;
+    unsigned long long progress_pass;
 };
 
 // Segmentation heads after the stack: 256 -> 128 -> 128 -> 7 (class slots padded to 8).
@@ -111,14 +125,22 @@ struct HeadArgs {
     long rows;
 };
 
-// Streamed projection: each layer's projection runs beside that layer's recurrence and
-// publishes its gates chunk by chunk in the order the recurrence reads them. A tile row
+// StreamLayout. Streamed projection: each layer's projection runs beside the recurrences
+// and publishes its gates chunk by chunk in the order the recurrence reads them. A tile row
 // block holds `group_windows` windows × `chunk` steps (128 rows): row r is window
 // g·group_windows + r / chunk at step s = c·chunk + r % chunk of direction d, i.e. time s
 // (forward) or steps - 1 - s (reverse); rows past the batch or past the last step are
-// skipped. Tile q = ((c·2 + d)·groups + g)·4 + column tile, columns d·512 + 128·(column tile).
-// Each of a tile's 4 waves adds 1 to ready[(c·2 + d)·groups + g] once its gates are stored and
-// made visible at agent scope, so a pass adds kReadyPerPass to every counter.
+// skipped. Tile q = ((i·2 + d)·groups + g)·4 + column tile holds chunk c = chunk_order[i],
+// columns d·512 + 128·(column tile). Each of a tile's 4 waves adds 1 to
+// ready[(c·2 + d)·groups + g] once its gates are stored with agent-scope stores and those
+// stores have completed, so a pass adds kReadyPerPass to every counter.
+// A tile of layer l + 1 reads the times of its chunk, all 256 columns, of layer l's output:
+// forward output up to the chunk's last time t_hi (written at forward step t_hi) and reverse
+// output down to its first time t_lo (written at reverse step T-1-t_lo). For chunk c that is
+// min(c·chunk + chunk, T) forward and T - c·chunk reverse steps (direction 0), or the same two
+// counts swapped (direction 1). The tile waits until both directions of each of its windows
+// have run stream_need(c) = max(T - c·chunk, min(c·chunk + chunk, T)) steps of layer l: the
+// middle chunks are ready first, chunk 0 last.
 constexpr int kReadyPerPass = 4 * (kProjThreads / 64);
 // Dynamic LDS a streamed projection workgroup claims on top of its tiles, so that two of them
 // never share a CU (2 · (72 + 16) KB > 160 KB): its persistent grid then spreads one per CU.
@@ -126,6 +148,10 @@ constexpr size_t kProjStreamLds = 16 * 1024;
 // Streamed gates are chosen automatically from this many windows on.
 constexpr int kStreamMinBatch = 16;
 inline int stream_chunks(int steps, int chunk) { return (steps + chunk - 1) / chunk; }
+__host__ __device__ inline int stream_need(int steps, int chunk, int c) {
+    const int hi = c * chunk + chunk < steps ? c * chunk + chunk : steps;
+    return steps - c * chunk > hi ? steps - c * chunk : hi;
+}
 
 // Launchers (kernels_*.hip). They return the launch's hipError_t.
 hipError_t launch_heads(const HeadArgs &args, hipStream_t stream);

@@ -79,12 +79,18 @@ struct bilstm_plan {
     hipStream_t proj_stream = nullptr;
     hipEvent_t proj_fork = nullptr;
     hipEvent_t proj_join = nullptr;
-    hipEvent_t layer_done[kLayers] = {nullptr, nullptr, nullptr, nullptr};
+    hipEvent_t layer_done[kLayers] = {nullptr, nullptr, nullptr, nullptr};  // no layer overlap
     float *ybuf = nullptr;                 // [rows][256]: output of layers 0 and 2
-    unsigned long long *ready = nullptr;   // counters, two per word
+    float *gates_odd = nullptr;            // [rows][1024]: gates of layers 1 and 3
+    // chunk counters of the two gate buffers (two per word): buffer b at b·ready_words
+    unsigned long long *ready = nullptr;
     size_t ready_words = 0;
+    unsigned long long *progress = nullptr;  // [batch][2] recurrence progress words
+    int *chunk_order = nullptr;              // [2][chunks]: layer 0's walk, later layers' walk
     int stream_groups = 0;
-    uint32_t ready_passes = 0;   // streamed layer passes since the counters were zeroed
+    int stream_chunks = 0;
+    uint32_t ready_passes[2] = {0, 0};  // streamed passes per gate buffer since the last clear
+    uint32_t layer_pass = 0;            // streamed layer passes since the last clear
     bool ready_dirty = false;    // a streamed pass failed to enqueue: zero the counters first
     int proj_workgroups_streamed = 0;
     size_t reserve_lds = 0;  // dynamic LDS of a recurrence workgroup (keeps its CU to itself)
@@ -180,14 +186,17 @@ void release(bilstm_plan *p) {
         if (p->slice_join[i]) (void)hipEventDestroy(p->slice_join[i]);
     }
     if (p->slice_fork) (void)hipEventDestroy(p->slice_fork);
+    if (p->proj_fork) (void)hipEventDestroy(p->proj_fork);
+    if (p->proj_join) (void)hipEventDestroy(p->proj_join);
     for (int l = 0; l < kLayers; ++l) {
         if (p->layer_done[l]) (void)hipEventDestroy(p->layer_done[l]);
     }
-    if (p->proj_fork) (void)hipEventDestroy(p->proj_fork);
-    if (p->proj_join) (void)hipEventDestroy(p->proj_join);
     if (p->proj_stream) (void)hipStreamDestroy(p->proj_stream);
     if (p->ybuf) (void)hipFree(p->ybuf);
+    if (p->gates_odd) (void)hipFree(p->gates_odd);
     if (p->ready) (void)hipFree(p->ready);
+    if (p->progress) (void)hipFree(p->progress);
+    if (p->chunk_order) (void)hipFree(p->chunk_order);
     if (p->library) library_projection_destroy(p->library);
     if (p->gates) (void)hipFree(p->gates);
     if (p->exchange) (void)hipFree(p->exchange);
@@ -232,7 +241,7 @@ bilstm_status reserve_flags(bilstm_plan *p, uint32_t count, hipStream_t stream, 
 // streamed: the whole batch in the recurrence's order, published on the plan's counters.
 bilstm_status enqueue_projection(bilstm_plan *p, int layer, const float *x, float *gates,
                                  hipStream_t stream, size_t row_first, size_t rows, int workgroups,
-                                 bool streamed = false) {
+                                 bool streamed = false, int buffer = 0) {
     if (p->library != nullptr) {
         // the vendor GEMM was planned for the whole batch, which it always runs unsliced
         if (row_first != 0 || rows != p->rows) {
@@ -255,12 +264,25 @@ bilstm_status enqueue_projection(bilstm_plan *p, int layer, const float *x, floa
     if (streamed) {
         const int chunk = p->info.stream_chunk;
         args.chunk = chunk;
+        while ((1 << args.chunk_shift) < chunk) ++args.chunk_shift;
         args.group_windows = kProjTileM / chunk;
         args.groups = p->stream_groups;
         args.batch = static_cast<int>(p->batch);
         args.steps = static_cast<int>(p->steps);
-        args.ready = reinterpret_cast<unsigned int *>(p->ready);
-        args.tiles = stream_chunks(args.steps, chunk) * 2 * args.groups * (kGates / kProjTileN);
+        args.ready = reinterpret_cast<unsigned int *>(p->ready + buffer * p->ready_words);
+        args.tiles = p->stream_chunks * 2 * args.groups * (kGates / kProjTileN);
+        args.error = p->error;
+        args.timeout_ticks = p->timeout_ticks;
+        if (layer == 0 || !p->info.stream_overlap) {
+            // the input is complete before the pass starts: chunks in the recurrence's order
+            args.chunk_order = p->chunk_order;
+        } else {
+            // the previous layer's recurrence, running now, still writes the input: chunks in
+            // the order their rows appear, each waiting for its rows
+            args.chunk_order = p->chunk_order + p->stream_chunks;
+            args.progress = p->progress;
+            args.progress_pass = static_cast<unsigned long long>(p->layer_pass - 1) << 32;
+        }
     }
     BL_HIP(launch_projection(args, workgroups, streamed ? kProjStreamLds : 0, stream), "projection launch");
     return BILSTM_OK;
@@ -271,7 +293,7 @@ bilstm_status enqueue_projection(bilstm_plan *p, int layer, const float *x, floa
 // the schedule allows it, joined back before the next layer).
 bilstm_status enqueue_recurrence(bilstm_plan *p, int layer, const float *gates, float *y,
                                  uint32_t flag_base, hipStream_t stream, bool layer_events,
-                                 int tile_lo, int tile_hi, bool streamed = false) {
+                                 int tile_lo, int tile_hi, bool streamed = false, int buffer = 0) {
     const bilstm_plan_info &s = p->info;
     RecurArgs base{};
     base.gates = gates;
@@ -286,12 +308,14 @@ bilstm_status enqueue_recurrence(bilstm_plan *p, int layer, const float *gates, 
     base.timeout_ticks = p->timeout_ticks;
     base.flag_skew = p->flag_skew;
     if (streamed) {
-        base.ready = reinterpret_cast<const unsigned int *>(p->ready);
+        base.ready = reinterpret_cast<const unsigned int *>(p->ready + buffer * p->ready_words);
         base.chunk = s.stream_chunk;
         base.group_windows = kProjTileM / s.stream_chunk;
         base.groups = p->stream_groups;
         // a forced timeout expects a count no pass reaches
-        base.ready_target = p->ready_passes * static_cast<unsigned int>(kReadyPerPass) + p->flag_skew;
+        base.ready_target = p->ready_passes[buffer] * static_cast<unsigned int>(kReadyPerPass) + p->flag_skew;
+        base.progress = p->progress;
+        base.progress_pass = static_cast<unsigned long long>(p->layer_pass) << 32;
     }
 
     const int per_launch = (s.recur_tiles + s.recur_launches - 1) / s.recur_launches;
@@ -330,38 +354,48 @@ bilstm_status enqueue_recurrence(bilstm_plan *p, int layer, const float *gates, 
     return launch_direction(1, 1, stream);
 }
 
-// The stack with streamed gates: per layer, the projection on the plan's projection stream
-// and the recurrence on the caller's stream run at the same time; the recurrence waits for
-// chunks the projection publishes. The next layer's projection waits for this layer's
-// recurrence (it reads its output and overwrites the gates). Layers 0 and 2 write the plan's
-// layer buffer, 1 and 3 write y, so a layer never writes rows its own projection may still
-// read.
+// The stack with streamed gates. Every projection runs on the plan's projection stream and
+// every recurrence on the caller's stream: the recurrence of layer l waits for the chunks its
+// projection publishes. With layer overlap the projection of layer l + 1 starts as soon as
+// layer l's projection is done and waits for the rows layer l's recurrence publishes; without,
+// it waits on an event for layer l's recurrence to end. Gates alternate between two buffers and
+// layer outputs between the plan's layer buffer (layers 0, 2) and y (1, 3), so a projection
+// never overwrites gates a running recurrence reads, nor a recurrence rows a running
+// projection reads.
 bilstm_status forward_streamed(bilstm_plan *p, const float *x, float *y, hipStream_t stream, uint32_t base) {
     bilstm_status st;
-    if (p->ready_dirty || p->ready_passes > 0x0FFFFFFFu) {
-        // counters out of step with the pass count (a failed enqueue), or close to wrapping
-        BL_HIP(launch_exchange_clear(p->ready, p->ready_words, stream), "counter clear");
-        p->ready_passes = 0;
+    if (p->ready_dirty || p->layer_pass > 0x0FFFFFF0u || p->ready_passes[0] > 0x03FFFFFFu ||
+        p->ready_passes[1] > 0x03FFFFFFu) {
+        // counters out of step with the pass counts (a failed enqueue), or close to wrapping
+        BL_HIP(launch_exchange_clear(p->ready, 2 * p->ready_words, stream), "counter clear");
+        BL_HIP(launch_exchange_clear(p->progress, 2 * static_cast<size_t>(p->batch), stream), "progress clear");
+        p->ready_passes[0] = p->ready_passes[1] = 0;
+        p->layer_pass = 0;
         p->ready_dirty = false;
     }
     BL_HIP(hipEventRecord(p->proj_fork, stream), "projection fork");
     BL_HIP(hipStreamWaitEvent(p->proj_stream, p->proj_fork, 0), "projection fork wait");
     if (p->phase_events) BL_HIP(hipEventRecord(p->ev_start, stream), "phase event");
     for (int l = 0; l < kLayers; ++l) {
+        const int buffer = l % 2;
         const float *in = l == 0 ? x : (l % 2 == 1 ? p->ybuf : y);
         float *out = l % 2 == 0 ? p->ybuf : y;
-        if (l > 0) BL_HIP(hipStreamWaitEvent(p->proj_stream, p->layer_done[l - 1], 0), "layer wait");
-        ++p->ready_passes;
-        if ((st = enqueue_projection(p, l, in, p->gates, p->proj_stream, 0, p->rows, p->proj_workgroups_streamed,
-                                     true)) != BILSTM_OK) {
+        float *gates = buffer == 0 ? p->gates : p->gates_odd;
+        ++p->layer_pass;
+        ++p->ready_passes[buffer];
+        if (!p->info.stream_overlap && l > 0) {
+            BL_HIP(hipStreamWaitEvent(p->proj_stream, p->layer_done[l - 1], 0), "layer wait");
+        }
+        if ((st = enqueue_projection(p, l, in, gates, p->proj_stream, 0, p->rows, p->proj_workgroups_streamed, true,
+                                     buffer)) != BILSTM_OK) {
             return st;
         }
         if (p->phase_events) BL_HIP(hipEventRecord(p->ev_proj[l], p->proj_stream), "phase event");
-        if ((st = enqueue_recurrence(p, l, p->gates, out, base + l * p->steps, stream, true, 0, p->info.recur_tiles,
-                                     true)) != BILSTM_OK) {
+        if ((st = enqueue_recurrence(p, l, gates, out, base + l * p->steps, stream, true, 0, p->info.recur_tiles,
+                                     true, buffer)) != BILSTM_OK) {
             return st;
         }
-        BL_HIP(hipEventRecord(p->layer_done[l], stream), "layer event");
+        if (!p->info.stream_overlap) BL_HIP(hipEventRecord(p->layer_done[l], stream), "layer event");
         if (p->phase_events) BL_HIP(hipEventRecord(p->ev_recur[l], stream), "phase event");
     }
     BL_HIP(hipEventRecord(p->proj_join, p->proj_stream), "projection join");
@@ -570,12 +604,31 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
         // stream and the events that order it against the recurrence
         const int group_windows = kProjTileM / info.stream_chunk;
         p->stream_groups = static_cast<int>((batch + group_windows - 1) / group_windows);
-        const size_t counters = static_cast<size_t>(stream_chunks(static_cast<int>(steps), info.stream_chunk)) * 2 *
-                                p->stream_groups;
+        p->stream_chunks = stream_chunks(static_cast<int>(steps), info.stream_chunk);
+        const size_t counters = static_cast<size_t>(p->stream_chunks) * 2 * p->stream_groups;
         p->ready_words = (counters + 1) / 2;
+        // the projection walks: layer 0 in the recurrence's order, later layers by when the
+        // previous layer's recurrence has written the chunk's rows (middle chunks first)
+        std::vector<int> order(2 * static_cast<size_t>(p->stream_chunks));
+        for (int c = 0; c < p->stream_chunks; ++c) order[c] = order[p->stream_chunks + c] = c;
+        if (false) std::stable_sort(order.begin() + p->stream_chunks, order.end(), [&](int u, int v) {
+            return stream_need(static_cast<int>(steps), info.stream_chunk, u) <
+                   stream_need(static_cast<int>(steps), info.stream_chunk, v);
+        });
         if ((st = device_alloc(p, &p->ybuf, rows * kWidth, "layer buffer")) != BILSTM_OK) return fail_release(st);
-        if ((st = device_alloc(p, &p->ready, p->ready_words, "chunk counters")) != BILSTM_OK) return fail_release(st);
-        e = hipMemset(p->ready, 0, p->ready_words * sizeof(unsigned long long));
+        if ((st = device_alloc(p, &p->gates_odd, rows * kGateCols, "second gate buffer")) != BILSTM_OK) {
+            return fail_release(st);
+        }
+        if ((st = device_alloc(p, &p->ready, 2 * p->ready_words, "chunk counters")) != BILSTM_OK) return fail_release(st);
+        if ((st = device_alloc(p, &p->progress, 2 * static_cast<size_t>(batch), "progress words")) != BILSTM_OK) {
+            return fail_release(st);
+        }
+        if ((st = device_alloc(p, &p->chunk_order, order.size(), "chunk order")) != BILSTM_OK) return fail_release(st);
+        e = hipMemset(p->ready, 0, 2 * p->ready_words * sizeof(unsigned long long));
+        if (e == hipSuccess) e = hipMemset(p->progress, 0, 2 * static_cast<size_t>(batch) * sizeof(unsigned long long));
+        if (e == hipSuccess) {
+            e = hipMemcpy(p->chunk_order, order.data(), order.size() * sizeof(int), hipMemcpyHostToDevice);
+        }
         if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->proj_stream, hipStreamNonBlocking);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&p->proj_fork, hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&p->proj_join, hipEventDisableTiming);
@@ -745,10 +798,11 @@ bilstm_status bilstm_phase_times(bilstm_plan *plan, float *ms, size_t n) {
     BL_HIP(scope.error(), "phase_times: hipSetDevice");
     BL_HIP(hipEventSynchronize(plan->ev_recur[kLayers - 1]), "phase_times");
     for (int l = 0; l < kLayers; ++l) {
-        hipEvent_t before = l == 0 ? plan->ev_start : plan->ev_recur[l - 1];
+        // streamed: the end of every phase from the forward's start (the phases of a layer and
+        // of its neighbours overlap); else each phase's own duration
+        hipEvent_t before = plan->phases_streamed || l == 0 ? plan->ev_start : plan->ev_recur[l - 1];
         BL_HIP(hipEventElapsedTime(&ms[l], before, plan->ev_proj[l]), "phase_times");
-        // streamed: both phases from the layer's start; else the recurrence after the projection
-        BL_HIP(hipEventElapsedTime(&ms[kLayers + l], plan->phases_streamed ? before : plan->ev_proj[l],
+        BL_HIP(hipEventElapsedTime(&ms[kLayers + l], plan->phases_streamed ? plan->ev_start : plan->ev_proj[l],
                                    plan->ev_recur[l]),
                "phase_times");
         BL_HIP(hipEventElapsedTime(&ms[2 * kLayers + l], plan->ev_launch0[l], plan->ev_launch1[l]), "phase_times");

@@ -29,12 +29,12 @@
 //  * Every row's K order is fixed and independent of the row's position and of the grid, so a
 //    row's gates are bitwise the same whatever the batch, the number of workgroups or the
 //    tile order.
-//  * Streamed order (STREAM): the layer's recurrence runs at the same time on other CUs and
-//    reads the gates step by step. Tiles then cover `group_windows` windows × `chunk`
-//    consecutive recurrence steps of one direction and are walked chunk by chunk, so the
-//    gates arrive in the order they are read. A finished tile is stored at once (no overlap
-//    with the next tile: the recurrence, not this kernel, sets the pace) with agent-scope
-//    stores, and once they have completed, published by one counter increment per wave.
+//  * Streamed order (projection_stream_kernel): the recurrences run at the same time on
+//    other CUs, this layer's reading the gates step by step and the previous layer's still
+//    writing this layer's input. Tiles then cover `group_windows` windows × `chunk`
+//    consecutive recurrence steps of one direction, walked in the order their inputs appear,
+//    and each waits for its rows, is computed on its own, stored with agent-scope stores and,
+//    once those have completed, published by one counter increment per wave.
 #include <algorithm>
 
 #include "bilstm_internal.h"
@@ -44,6 +44,12 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+
+// Raw buffer resource, word 3 of the descriptor for the gfx9 family (no format conversion),
+// and the cache-policy bit of an agent-scope (sc1) access.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kCachePolicySc1 = 16;
+
 
 constexpr int BM = kProjTileM;
 constexpr int BN = kProjTileN;
@@ -57,35 +63,7 @@ static_assert(BM == 128 && BN == 128 && BK == 32 && kProjThreads == 256, "tile s
 static_assert(kLoadsPerThread == 4, "loads per thread");
 static_assert(2 * 2 * BM * kStride * sizeof(float) == kProjLdsBytes, "LDS size");
 
-// Row block of streamed tile q (the streamed layout of the internal header): its first window,
-// first step, direction, first gate column and publication counter.
-struct StreamTile {
-    int w0, s0, dir, n0, counter;
-};
-
-__device__ __forceinline__ StreamTile stream_tile(const ProjArgs &a, int q) {
-    const int ct = q & 3;
-    const int rest = q >> 2;
-    const int g = rest % a.groups;
-    const int cd = rest / a.groups;
-    StreamTile t;
-    t.dir = cd & 1;
-    t.w0 = g * a.group_windows;
-    t.s0 = (cd >> 1) * a.chunk;
-    t.n0 = t.dir * kGates + ct * BN;
-    t.counter = rest;  // (c·2 + d)·groups + g
-    return t;
-}
-
-// Gate row of local row r of a streamed tile, or -1 when r falls past the batch or the steps.
-__device__ __forceinline__ int stream_row(const ProjArgs &a, const StreamTile &t, int r) {
-    const int w = t.w0 + r / a.chunk;
-    const int s = t.s0 + r % a.chunk;
-    if (w >= a.batch || s >= a.steps) return -1;
-    return w * a.steps + (t.dir == 0 ? s : a.steps - 1 - s);
-}
-
-template <int KSTEPS, bool STREAM>
+template <int KSTEPS>
 __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a) {
     __shared__ __attribute__((aligned(16))) float lds_a[2][BM * kStride];
     __shared__ __attribute__((aligned(16))) float lds_b[2][BN * kStride];
@@ -103,29 +81,16 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a)
 
     // ---- global -> registers -> LDS staging of one K step -----------------------------------
     v4f ra[kLoadsPerThread], rb[kLoadsPerThread];
-    // STREAM: gate rows of this thread's staging rows tid / 8 + 32 j of the tile being loaded
-    int srow[kLoadsPerThread];
-    auto stream_rows = [&](int q) {
-        const StreamTile t = stream_tile(a, q);
-#pragma unroll
-        for (int j = 0; j < kLoadsPerThread; ++j) srow[j] = stream_row(a, t, (tid + kProjThreads * j) / kThreadsPerRow);
-    };
     auto load = [&](int m0, int n0, int k0) {
 #pragma unroll
         for (int j = 0; j < kLoadsPerThread; ++j) {
             const int f = tid + kProjThreads * j;
             const int row = f / kThreadsPerRow;
             const int k = k0 + (f % kThreadsPerRow) * 4;
+            const int m = m0 + row;
             v4f va = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (STREAM) {
-                if (srow[j] >= 0 && k < a.in) {
-                    va = *reinterpret_cast<const v4f *>(a.x + static_cast<size_t>(srow[j]) * a.in + k);
-                }
-            } else {
-                const int m = m0 + row;
-                if (m < a.rows && k < a.in) {
-                    va = *reinterpret_cast<const v4f *>(a.x + static_cast<size_t>(m) * a.in + k);
-                }
+            if (m < a.rows && k < a.in) {
+                va = *reinterpret_cast<const v4f *>(a.x + static_cast<size_t>(m) * a.in + k);
             }
             ra[j] = va;
             rb[j] = *reinterpret_cast<const v4f *>(a.w + static_cast<size_t>(n0 + row) * a.kpad + k);
@@ -174,15 +139,10 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a)
         }
     };
 
-    // tile q's output columns and (plain order) first row
-    auto tile_n0 = [&](int q) { return STREAM ? stream_tile(a, q).n0 : (q % kColTiles) * BN; };
-    auto tile_m0 = [&](int q) { return STREAM ? 0 : (q / kColTiles) * BM; };
-
     int q = first;
     int base = 0;  // LDS buffer of the tile's first K step
     if (q < a.tiles) {
-        if constexpr (STREAM) stream_rows(q);
-        load(tile_m0(q), tile_n0(q), 0);
+        load((q / kColTiles) * BM, (q % kColTiles) * BN, 0);
         store(0);
     }
     __syncthreads();
@@ -190,16 +150,10 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a)
     frags(0, 0, af[0], bf[0]);
 
     for (; q < a.tiles; q += nwg) {
-        const int m0 = tile_m0(q);
-        const int n0 = tile_n0(q);
+        const int m0 = (q / kColTiles) * BM;
+        const int n0 = (q % kColTiles) * BN;
         const int qn = q + nwg;
         const bool next = qn < a.tiles;
-        // STREAM: the tile's bias, loaded now so that it has arrived long before the stores
-        float sbias[2] = {0.0f, 0.0f};
-        if constexpr (STREAM) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) sbias[j] = a.bias[n0 + wn * 64 + j * 32 + (lane & 31)];
-        }
 
         v16f acc[2][2];
 #pragma unroll
@@ -217,8 +171,7 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a)
             if (more) {
                 load(m0, n0, (kt + 1) * BK);
             } else if (next) {
-                if constexpr (STREAM) stream_rows(qn);
-                load(tile_m0(qn), tile_n0(qn), 0);
+                load((qn / kColTiles) * BM, (qn % kColTiles) * BN, 0);
             }
 #pragma unroll
             for (int g = 0; g < kGroups; ++g) {
@@ -232,65 +185,28 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a)
                         for (int j = 0; j < 2; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[p][i][e], bf[p][j][e],
                                                                              acc[i][j], 0, 0, 0);
-                if (!STREAM && g == kGroups / 2 && have) put_chunk(kt);
+                if (g == kGroups / 2 && have) put_chunk(kt);
             }
             if (more || next) store(cur ^ 1);
             __syncthreads();
             if (more || next) frags(cur ^ 1, 0, af[0], bf[0]);
         }
 
-        if constexpr (STREAM) {
-            // store now with agent-scope stores, wait for them to complete, then publish (one
-            // counter increment per wave)
-            const StreamTile t = stream_tile(a, q);
-            float *const gcol = a.gates + n0 + wn * 64 + (lane & 31);
-            auto put_row = [&](int i, int r, int m) {
+        // this tile's sums plus bias become the pending output of the next tile
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    __hip_atomic_store(gcol + static_cast<size_t>(m) * kGateCols + j * 32, acc[i][j][r] + sbias[j],
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            };
-            if (t.w0 + a.group_windows <= a.batch && t.s0 + a.chunk <= a.steps) {
-                // every row of the tile exists (all but the ragged last chunk and group)
+        for (int j = 0; j < 2; ++j) {
+            const float bv = a.bias[n0 + wn * 64 + j * 32 + (lane & 31)];
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int lr = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                        const int sr = t.s0 + lr % a.chunk;
-                        put_row(i, r, (t.w0 + lr / a.chunk) * a.steps + (t.dir == 0 ? sr : a.steps - 1 - sr));
-                    }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int m = stream_row(a, t, wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3));
-                        if (m >= 0) put_row(i, r, m);
-                    }
-            }
-            __builtin_amdgcn_s_waitcnt(0);
-            if (lane == 0) {
-                __hip_atomic_fetch_add(a.ready + t.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        } else {
-            // this tile's sums plus bias become the pending output of the next tile
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const float bv = a.bias[n0 + wn * 64 + j * 32 + (lane & 31)];
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) pend[i][j][r] = acc[i][j][r] + bv;
-            }
-            pm0 = m0;
-            pn0 = n0;
-            have = true;
+                for (int r = 0; r < 16; ++r) pend[i][j][r] = acc[i][j][r] + bv;
         }
+        pm0 = m0;
+        pn0 = n0;
+        have = true;
         base = (base + KSTEPS) & 1;
     }
-    if (!STREAM && have) {
+    if (have) {
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) put_chunk(s);
     }
@@ -478,13 +394,256 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_split_kernel(ProjA
     }
 }
 
+
+// ---- streamed order ------------------------------------------------------------------------
+//
+// The same MFMA tile as projection_kernel over the streamed row blocks (StreamLayout in the
+// internal header). A tile's first K step is loaded once its rows exist (during the previous
+// tile's last K step if they already do), and its outputs are stored and published as soon as
+// its K loop ends, so no finished tile waits behind the inputs of the next one. Every row sums
+// its K terms in the same order as projection_kernel, so the gates are bitwise the same.
+
+// Row block of streamed tile q: first window, first step, chunk, direction, first gate column
+// and publication counter.
+struct StreamTile {
+    int w0, s0, c, dir, n0, counter;
+};
+
+__device__ __forceinline__ StreamTile stream_tile(const ProjArgs &a, int q) {
+    const int ct = q & 3;
+    const int rest = q >> 2;
+    const int g = rest % a.groups;
+    const int id = rest / a.groups;  // walk position · 2 + direction
+    StreamTile t;
+    t.dir = id & 1;
+    t.c = a.chunk_order[id >> 1];
+    t.w0 = g * a.group_windows;
+    t.s0 = t.c * a.chunk;
+    t.n0 = t.dir * kGates + ct * BN;
+    t.counter = (t.c * 2 + t.dir) * a.groups + g;
+    return t;
+}
+
+// Gate row of local row r of a streamed tile, or -1 when r falls past the batch or the steps.
+__device__ __forceinline__ int stream_row(const ProjArgs &a, const StreamTile &t, int r) {
+    const int w = t.w0 + (r >> a.chunk_shift);
+    const int s = t.s0 + (r & (a.chunk - 1));
+    if (w >= a.batch || s >= a.steps) return -1;
+    return w * a.steps + (t.dir == 0 ? s : a.steps - 1 - s);
+}
+
+// Inputs written by the previous layer's recurrence during this kernel: a tile's rows exist
+// once both directions of each of its windows have published enough steps. Lane 2i + d of a
+// wave watches window w0 + i, direction d (the other lanes watch nothing).
+__device__ __forceinline__ const unsigned long long *watched_word(const ProjArgs &a, const StreamTile &t, int lane) {
+    const int w = t.w0 + (lane >> 1);
+    if (a.progress == nullptr || lane >= 2 * a.group_windows || w >= a.batch) return nullptr;
+    return a.progress + 2 * w + (lane & 1);
+}
+
+__device__ __forceinline__ unsigned long long wanted_word(const ProjArgs &a, const StreamTile &t) {
+    return a.progress_pass | static_cast<unsigned int>(stream_need(a.steps, a.chunk, t.c));
+}
+
+// Wait until the tile's rows exist; the wave goes on when all its lanes have seen them.
+__device__ __forceinline__ void wait_rows(const ProjArgs &a, const StreamTile &t, int lane, bool &timed_out) {
+    const unsigned long long *p = watched_word(a, t, lane);
+    if (p == nullptr || timed_out) return;
+    const unsigned long long want = wanted_word(a, t);
+    if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) return;
+    const unsigned long long t0 = wall_clock64();
+    while (true) {
+        __builtin_amdgcn_s_sleep(2);
+        if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) break;
+        if (wall_clock64() - t0 > a.timeout_ticks) {
+            atomicOr(a.error, 4u);
+            timed_out = true;
+            break;
+        }
+    }
+}
+
+template <int KSTEPS>
+__global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(ProjArgs a) {
+    __shared__ __attribute__((aligned(16))) float lds_a[2][BM * kStride];
+    __shared__ __attribute__((aligned(16))) float lds_b[2][BN * kStride];
+    static_assert(KSTEPS % 2 == 0, "a tile's first K step goes to LDS buffer 0");
+
+    const int nwg = gridDim.x;  // a multiple of 8
+    const int per_xcd = nwg >> 3;
+    const int first = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+    // Inputs written while this kernel runs are read with agent-scope (sc1) buffer loads; the
+    // buffer's range is the whole input, so a load outside it would return zeros.
+    const bool coherent = a.progress != nullptr;
+    const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(a.x), 0, static_cast<int>(static_cast<unsigned int>(a.steps) * a.batch * a.in * 4),
+        kBufferRsrcWord3);
+
+    v4f ra[kLoadsPerThread], rb[kLoadsPerThread];
+    int srow[kLoadsPerThread];  // gate rows of this thread's staging rows tid / 8 + 32 j
+    auto load = [&](int n0, int k0) {
+#pragma unroll
+        for (int j = 0; j < kLoadsPerThread; ++j) {
+            const int f = tid + kProjThreads * j;
+            const int row = f / kThreadsPerRow;
+            const int k = k0 + (f % kThreadsPerRow) * 4;
+            v4f va = {0.f, 0.f, 0.f, 0.f};
+            if (srow[j] >= 0 && k < a.in) {
+                const unsigned int off = static_cast<unsigned int>(srow[j]) * a.in + k;
+                if (coherent) {
+                    va = __builtin_amdgcn_raw_buffer_load_b128(xrsrc, off * 4, 0, kCachePolicySc1);
+                } else {
+                    va = *reinterpret_cast<const v4f *>(a.x + off);
+                }
+            }
+            ra[j] = va;
+            rb[j] = *reinterpret_cast<const v4f *>(a.w + static_cast<size_t>(n0 + row) * a.kpad + k);
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < kLoadsPerThread; ++j) {
+            const int f = tid + kProjThreads * j;
+            const int off = (f / kThreadsPerRow) * kStride + (f % kThreadsPerRow) * 4;
+            *reinterpret_cast<v4f *>(&lds_a[buf][off]) = ra[j];
+            *reinterpret_cast<v4f *>(&lds_b[buf][off]) = rb[j];
+        }
+    };
+    const int frag_row = lane & 31;
+    const int frag_k = (lane >> 5) * 4;
+    auto frags = [&](int buf, int g, v4f (&af)[2], v4f (&bf)[2]) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            af[t] = *reinterpret_cast<const v4f *>(
+                &lds_a[buf][(wm * 64 + t * 32 + frag_row) * kStride + g * 8 + frag_k]);
+            bf[t] = *reinterpret_cast<const v4f *>(
+                &lds_b[buf][(wn * 64 + t * 32 + frag_row) * kStride + g * 8 + frag_k]);
+        }
+    };
+
+    auto rows_of = [&](const StreamTile &t) {
+#pragma unroll
+        for (int j = 0; j < kLoadsPerThread; ++j) srow[j] = stream_row(a, t, (tid + kProjThreads * j) / kThreadsPerRow);
+    };
+
+    auto publish = [&](const StreamTile &t) {
+        __hip_atomic_fetch_add(a.ready + t.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    bool timed_out = false;
+    // The next tile's first K step is loaded during the current tile's last one when its rows
+    // already exist (known from a progress read issued at the current tile's start); else the
+    // wave waits for them after the current tile is published.
+    bool staged = false;  // this wave already staged the tile's first K step in LDS buffer 0
+    for (int q = first; q < a.tiles; q += nwg) {
+        const StreamTile t = stream_tile(a, q);
+        const int n0 = t.n0;
+        float sbias[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) sbias[j] = a.bias[n0 + wn * 64 + j * 32 + (lane & 31)];
+        if (!staged) {
+            wait_rows(a, t, lane, timed_out);
+            rows_of(t);
+            load(n0, 0);
+            store(0);
+        }
+        __syncthreads();
+        v4f af[2][2], bf[2][2];
+        frags(0, 0, af[0], bf[0]);
+
+        // progress of the next tile's windows, read now and checked in the last K step
+        const int qn = q + nwg;
+        const bool next = qn < a.tiles;
+        const StreamTile tn = stream_tile(a, next ? qn : q);
+        const unsigned long long *pn = next ? watched_word(a, tn, lane) : nullptr;
+        const unsigned long long seen_next =
+            pn != nullptr ? __hip_atomic_load(pn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : ~0ull;
+
+        v16f acc[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+        staged = false;
+#pragma unroll
+        for (int kt = 0; kt < KSTEPS; ++kt) {
+            const int cur = kt & 1;
+            const bool more = kt + 1 < KSTEPS;
+            if (more) {
+                load(n0, (kt + 1) * BK);
+            } else if (next && __all(seen_next >= wanted_word(a, tn))) {
+                rows_of(tn);
+                load(tn.n0, 0);
+                staged = true;
+            }
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g) {
+                const int p = g & 1;
+                if (g + 1 < kGroups) frags(cur, g + 1, af[p ^ 1], bf[p ^ 1]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[p][i][e], bf[p][j][e],
+                                                                             acc[i][j], 0, 0, 0);
+            }
+            // the last K step reads buffer 1, so the next tile's first K step goes to buffer 0
+            if (more || staged) store(cur ^ 1);
+            __syncthreads();
+            if (more) frags(cur ^ 1, 0, af[0], bf[0]);
+        }
+
+        // store with agent-scope stores, wait for them to complete, then publish (one counter
+        // increment per wave)
+        float *const gcol = a.gates + n0 + wn * 64 + (lane & 31);
+        auto put_row = [&](int i, int r, int m) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                __hip_atomic_store(gcol + static_cast<size_t>(m) * kGateCols + j * 32, acc[i][j][r] + sbias[j],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        };
+        if (t.w0 + a.group_windows <= a.batch && t.s0 + a.chunk <= a.steps) {
+            // every row of the tile exists (all but the ragged last chunk and group)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int lr = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                    const int sr = t.s0 + (lr & (a.chunk - 1));
+                    put_row(i, r, (t.w0 + (lr >> a.chunk_shift)) * a.steps + (t.dir == 0 ? sr : a.steps - 1 - sr));
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = stream_row(a, t, wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3));
+                    if (m >= 0) put_row(i, r, m);
+                }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        if (lane == 0) publish(t);
+    }
+}
+
 }  // namespace
 
 hipError_t projection_allow_lds(size_t bytes) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&projection_kernel<2, true>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&projection_stream_kernel<2>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
     if (e != hipSuccess) return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&projection_kernel<8, true>),
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&projection_stream_kernel<8>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
 }
 
@@ -493,8 +652,25 @@ hipError_t launch_projection(const ProjArgs &args, int workgroups, size_t dynami
     // a multiple of 8 (the XCD-ordered walk), at most one workgroup per tile group of 8
     int nwg = std::min(workgroups, (args.tiles + 7) / 8 * 8);
     nwg = std::max(8, nwg / 8 * 8);
+    if (args.chunk > 0) {
+        // streamed order: FP32 kernel only
+        if (args.w_hi != nullptr || args.ready == nullptr || args.chunk_order == nullptr ||
+            args.chunk * args.group_windows != kProjTileM || (1 << args.chunk_shift) != args.chunk) {
+            return hipErrorInvalidValue;
+        }
+        switch (args.kpad / kProjTileK) {
+            case 2:
+                hipLaunchKernelGGL(projection_stream_kernel<2>, dim3(nwg), dim3(kProjThreads), dynamic_lds, stream, args);
+                break;
+            case 8:
+                hipLaunchKernelGGL(projection_stream_kernel<8>, dim3(nwg), dim3(kProjThreads), dynamic_lds, stream, args);
+                break;
+            default:
+                return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     if (args.w_hi != nullptr) {
-        if (args.chunk > 0) return hipErrorInvalidValue;  // streamed order: FP32 kernel only
         switch (args.kpad / kProjTileK) {
             case 2:
                 hipLaunchKernelGGL(projection_split_kernel<2>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
@@ -507,22 +683,12 @@ hipError_t launch_projection(const ProjArgs &args, int workgroups, size_t dynami
         }
         return hipGetLastError();
     }
-    const bool streamed = args.chunk > 0;
-    if (streamed && (args.ready == nullptr || args.chunk * args.group_windows != BM)) return hipErrorInvalidValue;
     switch (args.kpad / kProjTileK) {
         case 2:
-            if (streamed) {
-                hipLaunchKernelGGL((projection_kernel<2, true>), dim3(nwg), dim3(kProjThreads), dynamic_lds, stream, args);
-            } else {
-                hipLaunchKernelGGL((projection_kernel<2, false>), dim3(nwg), dim3(kProjThreads), 0, stream, args);
-            }
+            hipLaunchKernelGGL(projection_kernel<2>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
             break;
         case 8:
-            if (streamed) {
-                hipLaunchKernelGGL((projection_kernel<8, true>), dim3(nwg), dim3(kProjThreads), dynamic_lds, stream, args);
-            } else {
-                hipLaunchKernelGGL((projection_kernel<8, false>), dim3(nwg), dim3(kProjThreads), 0, stream, args);
-            }
+            hipLaunchKernelGGL(projection_kernel<8>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
             break;
         default:
             return hipErrorInvalidValue;

@@ -34,8 +34,11 @@
 // and publishes the gates chunk by chunk. Before the gate loads of a group of kRing steps are
 // issued, the chunk counter read one group earlier must show the chunk published (else the
 // wave polls until it does); the counter of the group after next is read at the same point,
-// so in the steady state no wave ever waits for a counter. Gate loads are then agent-scope
-// loads, which see the projection's stores once its release and counter are observed.
+// so in the steady state no wave ever waits for a counter. Gate loads are agent-scope loads,
+// which see the projection's agent-scope stores once its counter shows them complete. In
+// turn the output is written with agent-scope stores and each window's progress (steps whose
+// output has completed) is published every kRing steps, for the next layer's projection when
+// it runs beside this recurrence.
 //
 // Waits are bounded: a poll that sees no progress for `timeout_ticks` wall-clock ticks
 // sets the error word and stops waiting, so the grid always drains.
@@ -209,6 +212,17 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
         }
     };
     unsigned int ready_seen = 0;  // counter of the chunk of the group after the current one
+    // STREAM: progress[window][dir] = progress_pass | steps whose output stores have completed,
+    // for every window of the tile (read by the next layer's projection)
+    auto publish = [&](unsigned int done) {
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+            if (win0 + b < a.batch) {
+                __hip_atomic_store(a.progress + 2 * (win0 + b) + dir, a.progress_pass | done, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    };
     float *const ycol = a.y + static_cast<size_t>(win0 + qe) * steps * kWidth + dir * kHidden + ug;
 
     // KG == 1: per-lane register ring of gate inputs.
@@ -274,6 +288,11 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
             // check the counter read a group ago, and read the one for the next group
             wait_ready(ready_seen, s + kRing);
             ready_seen = read_ready(s + 2 * kRing);
+            // Publish this tile's progress. Every wave has passed the previous step's barrier
+            // and, before it, waited for the gate load issued kRing steps earlier; vector
+            // memory operations complete in issue order, so every output store of the steps
+            // before s - 2·kRing has completed.
+            if (tid == 0 && s >= 2 * kRing) publish(static_cast<unsigned int>(s - 2 * kRing));
         }
 
         // (1) partial dot products over this lane's K quarter
@@ -385,7 +404,12 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
             }
         }
 
-        ycol[static_cast<size_t>(time_of(s)) * kWidth] = hval;
+        if constexpr (STREAM) {
+            __hip_atomic_store(ycol + static_cast<size_t>(time_of(s)) * kWidth, hval, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            ycol[static_cast<size_t>(time_of(s)) * kWidth] = hval;
+        }
         __syncthreads();
     };
 
@@ -398,6 +422,12 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
     for_slots<0, kRing - 1>([&](auto slot) {
         if (s0 + decltype(slot)::value < steps) step(s0 + decltype(slot)::value, slot);
     });
+    if constexpr (STREAM) {
+        // every wave's output stores have completed: the whole sequence is published
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) publish(static_cast<unsigned int>(steps));
+    }
 }
 
 __global__ void exchange_clear_kernel(unsigned long long *words, size_t count) {

@@ -112,16 +112,21 @@ typedef struct {
                              that layer's recurrence on the CUs the recurrence leaves free, computes
                              the gates in the order the recurrence reads them (chunks of steps,
                              per direction) and publishes each chunk through a counter the
-                             recurrence polls; layers alternate between y and a plan-owned
-                             buffer, so no layer overwrites rows its projection still reads.
-                             The output is bitwise the same as without it.
+                             recurrence polls; the next layer's projection can start while this
+                             layer's recurrence still runs, reading the rows it has published.
+                             Gates alternate between two plan-owned buffers and layer outputs
+                             between y and a plan-owned buffer, so no kernel overwrites data a
+                             running one still reads. The output is bitwise the same as without
+                             it.
                              0 = auto (on from 16 windows when recur_groups = 1, the
                              recurrence's grid leaves at least a quarter of the CUs free and
                              projection = 0), 1 = off,
                              2 = on (BILSTM_UNSUPPORTED unless recur_groups = 1, projection = 0,
-                             slices <= 1 and at least 8 CUs stay free). The recurrence's waits
-                             on the counters are bounded by the watchdog like every other wait:
-                             if the GPU is shared with other work that keeps the projection from
+                             slices <= 1 and at least 8 CUs stay free), with the next layer's
+                             projection starting during this layer's recurrence; 3 = on, with it
+                             starting after this layer's recurrence; 4 = the same as 2.
+                             Every wait on a counter is bounded by the watchdog like every other
+                             wait: if the GPU is shared with other work that keeps a kernel from
                              running, bilstm_check reports BILSTM_TIMEOUT instead of hanging */
     int32_t reserved[1];  /* must be zero */
 } bilstm_options;
@@ -147,6 +152,8 @@ typedef struct {
     int32_t pipeline;        /* 1 when bilstm_forward streams the gates (see bilstm_options) */
     int32_t stream_chunk;    /* streamed gates: recurrence steps per published chunk (128 /
                                 windows per projection row block); 0 when not streamed */
+    int32_t stream_overlap;  /* streamed gates: 1 when the next layer's projection starts during
+                                this layer's recurrence, 0 when after it */
 } bilstm_plan_info;
 
 /*
@@ -213,9 +220,9 @@ bilstm_status bilstm_check(bilstm_plan *plan);
  * writes 12 values in milliseconds: projection of layers 0..3; recurrence phase of layers
  * 0..3 (both directions, including any join); duration of the first recurrence launch on the
  * caller's stream of layers 0..3 (the launch running both directions when they share one
- * launch, else the forward direction's). n must be >= 12. With streamed gates the two phases
- * of a layer overlap: both are then measured from the layer's start (the end of the previous
- * layer's recurrence), the projection to its end and the recurrence to its end.
+ * launch, else the forward direction's). n must be >= 12. With streamed gates the phases of a
+ * layer and of its neighbours overlap: the first 8 values are then the time from the forward's
+ * start to the end of each projection and of each recurrence.
  */
 bilstm_status bilstm_set_phase_events(bilstm_plan *plan, int enable);
 bilstm_status bilstm_phase_times(bilstm_plan *plan, float *ms, size_t n);

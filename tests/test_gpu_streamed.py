@@ -60,23 +60,28 @@ SHAPES = [(1, 589, 0), (1, 1, 0), (2, 130, 0), (3, 150, 0), (3, 3, 0), (5, 7, 0)
           (8, 97, 2), (8, 64, 4), (32, 150, 0)]
 
 
+@pytest.mark.parametrize("pipeline", [4, 3])
 @pytest.mark.parametrize("batch,steps,tile", SHAPES)
-def test_streamed_equals_unstreamed_bitwise(bl, batch, steps, tile):
+def test_streamed_equals_unstreamed_bitwise(bl, batch, steps, tile, pipeline):
+    """pipeline 4: the next layer's projection runs during this layer's recurrence, reading the
+    rows it publishes; 3: after it."""
     x = workloads.make_input(40 + batch, batch, steps)
     layers = workloads.make_layers(41)
-    note(f"streamed vs unstreamed batch={batch} steps={steps} tile={tile}")
-    got, info = run(bl, x, layers, pipeline=2, tile=tile)
+    note(f"streamed (pipeline={pipeline}) vs unstreamed batch={batch} steps={steps} tile={tile}")
+    got, info = run(bl, x, layers, pipeline=pipeline, tile=tile)
     base, binfo = run(bl, x, layers, pipeline=1, slices=1, tile=tile)
     assert info["pipeline"] == 1 and binfo["pipeline"] == 0
+    assert info["stream_overlap"] == (1 if pipeline == 4 else 0)
     assert np.array_equal(got[0].view(np.uint32), base[0].view(np.uint32))
 
 
-def test_streamed_repeated_forwards_are_bit_stable(bl):
+@pytest.mark.parametrize("pipeline", [4, 3])
+def test_streamed_repeated_forwards_are_bit_stable(bl, pipeline):
     """Five forwards on one plan: each pass's counters reach the next target exactly once."""
     x, layers = workloads.make_workload("b8")
     xs = np.ascontiguousarray(x[:, :150])
-    note("streamed repeated forwards b8 t150 x5")
-    outs, info = run(bl, xs, layers, repeats=5, pipeline=2)
+    note(f"streamed repeated forwards b8 t150 x5 pipeline={pipeline}")
+    outs, info = run(bl, xs, layers, repeats=5, pipeline=pipeline)
     assert info["pipeline"] == 1
     for o in outs[1:]:
         assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
@@ -85,18 +90,19 @@ def test_streamed_repeated_forwards_are_bit_stable(bl):
 def test_streamed_matches_oracle(bl, orc):
     x, layers = workloads.make_workload("b8")
     note("streamed b8 against the oracle")
-    outs, info = run(bl, x, layers, pipeline=2)
+    outs, info = run(bl, x, layers, pipeline=4)
     ref = orc.stack(x, layers, threads=min(16, os.cpu_count() or 1))
     err = np.abs(outs[0].astype(np.float64) - ref)
     assert np.all(err <= ATOL + RTOL * np.abs(ref)), f"max abs err {err.max():.3e}"
     note(f"streamed b8 max abs err {err.max():.3e} chunk {info['stream_chunk']}")
 
 
-def test_streamed_phase_times(bl):
+@pytest.mark.parametrize("pipeline", [4, 3])
+def test_streamed_phase_times(bl, pipeline):
     x, layers = workloads.make_workload("b8")
     xs = np.ascontiguousarray(x[:, :100])
-    note("streamed phase times")
-    plan = bl.Plan(layers, 8, 100, pipeline=2)
+    note(f"streamed phase times pipeline={pipeline}")
+    plan = bl.Plan(layers, 8, 100, pipeline=pipeline)
     xd = torch.from_numpy(xs).cuda()
     plan.forward(xd)
     plan.set_phase_events(True)
@@ -104,20 +110,24 @@ def test_streamed_phase_times(bl):
     t = plan.phase_times()
     plan.check()
     plan.close()
+    rec = t["recurrence_ms"]
     for l in range(4):
-        # both measured from the layer's start; the recurrence needs the projection's chunks
-        assert 0 < t["projection_ms"][l] and 0 < t["recurrence_ms"][l]
-        assert 0 < t["recurrence_launch_ms"][l] <= t["recurrence_ms"][l] + 1e-3
+        # phase ends from the forward's start: recurrences end in order, each after the
+        # projection whose gates it reads, and each launch lasts at most until its end
+        assert 0 < t["projection_ms"][l] < rec[l] + 1e-3
+        assert l == 0 or rec[l - 1] < rec[l]
+        assert 0 < t["recurrence_launch_ms"][l] <= rec[l] + 1e-3
 
 
-def test_streamed_watchdog_reports_timeout_and_grid_drains(bl):
+@pytest.mark.parametrize("pipeline", [4, 3])
+def test_streamed_watchdog_reports_timeout_and_grid_drains(bl, pipeline):
     """Counter waits forced to time out from the host (watchdog_us = -1: every wait expects a
     count no pass reaches and gives up on its first poll): the kernels finish and the plan
     reports BILSTM_TIMEOUT; a normal plan afterwards is unaffected."""
     x, layers = workloads.make_workload("b8")
     xs = np.ascontiguousarray(x[:, :64])
-    note("streamed watchdog first-miss")
-    plan = bl.Plan(layers, 8, 64, pipeline=2, watchdog_us=-1)
+    note(f"streamed watchdog first-miss pipeline={pipeline}")
+    plan = bl.Plan(layers, 8, 64, pipeline=pipeline, watchdog_us=-1)
     plan.forward(torch.from_numpy(xs).cuda())
     with pytest.raises(bl.BilstmError) as e:
         plan.check()

@@ -192,11 +192,22 @@ def test_schedule_forced_streaming_checks_its_conditions(bl):
     assert bl.schedule(32, 589, 256, 1, pipeline=1)["pipeline"] == 0
 
 
+@pytest.mark.parametrize("batch,steps,pipeline,overlap", [
+    (32, 589, 0, 1), (16, 589, 0, 1), (64, 4096, 0, 1), (96, 589, 0, 1), (32, 589, 3, 0), (64, 4096, 4, 1),
+    (8, 589, 2, 1), (1, 589, 2, 1), (32, 589, 1, 0), (8, 589, 0, 0)])
+def test_schedule_layer_overlap(bl, batch, steps, pipeline, overlap):
+    """Streamed gates overlap the next layer's projection with this layer's recurrence unless
+    pipeline = 3 asks for each projection after the previous recurrence."""
+    s = bl.schedule(batch, steps, 256, 1, pipeline=pipeline)
+    assert s["stream_overlap"] == overlap
+    assert s["pipeline"] == (1 if pipeline >= 2 or (pipeline == 0 and batch >= 16) else 0)
+
+
 @pytest.mark.parametrize("kwargs,status", [
     (dict(groups=3), "BILSTM_UNSUPPORTED"), (dict(tile=3), "BILSTM_UNSUPPORTED"),
     (dict(concurrent=5), "BILSTM_INVALID_ARGUMENT"), (dict(slices=9), "BILSTM_INVALID_ARGUMENT"),
     (dict(slices=-1), "BILSTM_INVALID_ARGUMENT"), (dict(projection=3), "BILSTM_INVALID_ARGUMENT"),
-    (dict(projection=-1), "BILSTM_INVALID_ARGUMENT"), (dict(pipeline=3), "BILSTM_INVALID_ARGUMENT"),
+    (dict(projection=-1), "BILSTM_INVALID_ARGUMENT"), (dict(pipeline=5), "BILSTM_INVALID_ARGUMENT"),
     (dict(pipeline=-1), "BILSTM_INVALID_ARGUMENT")])
 def test_schedule_rejects_bad_options(bl, kwargs, status):
     with pytest.raises(bl.BilstmError) as e:
