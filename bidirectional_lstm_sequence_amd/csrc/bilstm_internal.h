@@ -34,6 +34,15 @@ constexpr int kAutoSlices = 2;
 
 inline int padded_input(int in) { return (in + kProjTileK - 1) / kProjTileK * kProjTileK; }
 
+// Factor of each gate's pre-activation in the exponent of its activation, by gate (i, f, g,
+// o): σ(a) = 1/(1 + 2^(-a·log2 e)) and tanh(a) = 2/(1 + 2^(-2a·log2 e)) - 1. The plan stores the
+// recurrent rows multiplied by these factors (rounded to fp32).
+__host__ __device__ constexpr float gate_exp_scale(int gate) {
+    return gate == 2 ? -2.8853900817779268f : -1.4426950408889634f;
+}
+__device__ constexpr float kGateExpScale[4] = {gate_exp_scale(0), gate_exp_scale(1), gate_exp_scale(2),
+                                               gate_exp_scale(3)};
+
 // Threads per recurrence workgroup for `groups` workgroups per (direction, tile): four lanes
 // per hidden unit.
 inline int recur_threads(int groups) { return 4 * (kHidden / groups); }
@@ -69,7 +78,7 @@ struct ProjArgs {
     // (progress != nullptr): before a tile's rows are read, each of its windows' progress word
     // in both directions must reach progress_pass | steps the rows need (see StreamLayout);
     // the rows are then read with agent-scope loads.
-    const unsigned long long *progress;  // [batch][2]
+    const unsigned long long *progress;  // [batch][2], kProgressStride words apart
     unsigned long long progress_pass;    // (previous layer's pass number) << 32
     unsigned int *error;                 // watchdog flag word
     unsigned long long timeout_ticks;
@@ -146,8 +155,11 @@ constexpr int kReadyPerPass = 4 * (kProjThreads / 64);
 // never share a CU (2 · (72 + 16) KB > 160 KB): its persistent grid then spreads one per CU.
 constexpr size_t kProjStreamLds = 16 * 1024;
 // Streamed gates are chosen automatically from this many windows on.
-constexpr int kStreamMinBatch = 16;
+constexpr int kStreamMinBatch = 8;
 inline int stream_chunks(int steps, int chunk) { return (steps + chunk - 1) / chunk; }
+// Progress words one 128-byte line apart: each window's direction has its own line, so the
+// recurrence's stores and the projection's polls of different windows never share one.
+constexpr int kProgressStride = 16;
 __host__ __device__ inline int stream_need(int steps, int chunk, int c) {
     const int hi = c * chunk + chunk < steps ? c * chunk + chunk : steps;
     return steps - c * chunk > hi ? steps - c * chunk : hi;

@@ -141,9 +141,9 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
         pipeline = true;
     } else if (want_pipe == 0) {
         // auto: when the recurrence leaves at least a quarter of the CUs to the projection and
-        // the batch has at least 16 windows. Below that the whole projection of a layer takes
-        // about as long as the first published chunk (one tile of every direction, measured
-        // ~35 us at K = 256), so streaming gains nothing.
+        // the batch has at least 8 windows (measured on MI355X: 8 windows 1.303 -> 1.277 ms
+        // streamed, one window 1.230 -> 1.245 ms: there the whole projection of a layer takes
+        // about as long as its first published chunk).
         pipeline = pipe_possible && concurrent == 2 && 4 * rec_wgs <= 3LL * cu_count &&
                    batch >= static_cast<uint32_t>(kStreamMinBatch);
     }

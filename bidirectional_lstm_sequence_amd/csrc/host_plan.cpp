@@ -368,7 +368,8 @@ bilstm_status forward_streamed(bilstm_plan *p, const float *x, float *y, hipStre
         p->ready_passes[1] > 0x03FFFFFFu) {
         // counters out of step with the pass counts (a failed enqueue), or close to wrapping
         BL_HIP(launch_exchange_clear(p->ready, 2 * p->ready_words, stream), "counter clear");
-        BL_HIP(launch_exchange_clear(p->progress, 2 * static_cast<size_t>(p->batch), stream), "progress clear");
+        BL_HIP(launch_exchange_clear(p->progress, kProgressStride * 2 * static_cast<size_t>(p->batch), stream),
+               "progress clear");
         p->ready_passes[0] = p->ready_passes[1] = 0;
         p->layer_pass = 0;
         p->ready_dirty = false;
@@ -531,6 +532,11 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
         std::vector<float> r(2ull * kGates * kHidden);
         std::vector<float> b(kGateCols);
         pack_layer(layers[l], p->in[l], w.data(), r.data(), b.data());
+        // recurrent rows scaled into the exponent of their gate's activation (row 4j + g)
+        for (size_t row = 0; row < 2ull * kGates; ++row) {
+            const float scale = gate_exp_scale(static_cast<int>(row % 4));
+            for (int k = 0; k < kHidden; ++k) r[row * kHidden + k] *= scale;
+        }
         if ((st = device_alloc(p, &p->w[l], w.size(), "W")) != BILSTM_OK) return fail_release(st);
         if ((st = device_alloc(p, &p->r[l], r.size(), "R")) != BILSTM_OK) return fail_release(st);
         if ((st = device_alloc(p, &p->bias[l], b.size(), "bias")) != BILSTM_OK) return fail_release(st);
@@ -620,12 +626,15 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
             return fail_release(st);
         }
         if ((st = device_alloc(p, &p->ready, 2 * p->ready_words, "chunk counters")) != BILSTM_OK) return fail_release(st);
-        if ((st = device_alloc(p, &p->progress, 2 * static_cast<size_t>(batch), "progress words")) != BILSTM_OK) {
+        if ((st = device_alloc(p, &p->progress, kProgressStride * 2 * static_cast<size_t>(batch), "progress words")) !=
+            BILSTM_OK) {
             return fail_release(st);
         }
         if ((st = device_alloc(p, &p->chunk_order, order.size(), "chunk order")) != BILSTM_OK) return fail_release(st);
         e = hipMemset(p->ready, 0, 2 * p->ready_words * sizeof(unsigned long long));
-        if (e == hipSuccess) e = hipMemset(p->progress, 0, 2 * static_cast<size_t>(batch) * sizeof(unsigned long long));
+        if (e == hipSuccess) {
+            e = hipMemset(p->progress, 0, kProgressStride * 2 * static_cast<size_t>(batch) * sizeof(unsigned long long));
+        }
         if (e == hipSuccess) {
             e = hipMemcpy(p->chunk_order, order.data(), order.size() * sizeof(int), hipMemcpyHostToDevice);
         }

@@ -438,7 +438,7 @@ __device__ __forceinline__ int stream_row(const ProjArgs &a, const StreamTile &t
 __device__ __forceinline__ const unsigned long long *watched_word(const ProjArgs &a, const StreamTile &t, int lane) {
     const int w = t.w0 + (lane >> 1);
     if (a.progress == nullptr || lane >= 2 * a.group_windows || w >= a.batch) return nullptr;
-    return a.progress + 2 * w + (lane & 1);
+    return a.progress + kProgressStride * (2 * w + (lane & 1));
 }
 
 __device__ __forceinline__ unsigned long long wanted_word(const ProjArgs &a, const StreamTile &t) {

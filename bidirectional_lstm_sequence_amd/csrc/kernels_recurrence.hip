@@ -68,15 +68,14 @@ constexpr int kXor2 = 0x4E;       // quad_perm 2,3,0,1
 template <int L>
 constexpr int kBcast = L * 0x55;  // quad_perm L,L,L,L: every lane reads quad lane L
 
-// σ(z) = 1/(1 + e^{-z}) on the hardware exp2 and reciprocal. For very negative z, e^{-z}
-// overflows to +inf and the reciprocal returns the exact limit 0, so no clamp is needed.
-__device__ __forceinline__ float sigmoid_f(float z) {
-    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
-}
-
-// tanh(z) = 2σ(2z) - 1.
-__device__ __forceinline__ float tanh_f(float z) {
-    return fmaf(2.0f, sigmoid_f(2.0f * z), -1.0f);
+// Activations on the hardware exp2 and reciprocal: σ(a) = 1/(1 + 2^(-a·log2 e)) and
+// tanh(a) = 2σ(2a) - 1. The recurrent rows arrive pre-multiplied by -log2 e (i, f, o) or
+// -2·log2 e (g) (kGateExpScale), and the gate input is scaled the same way, so a gate's sum is
+// already the exponent z and its activation is A·rcp(1 + 2^z) + B with (A, B) = (1, 0) for
+// σ and (2, -1) for tanh. For z -> +inf, 2^z overflows to +inf and the reciprocal returns the
+// exact limit 0, so no clamp is needed.
+__device__ __forceinline__ float rcp_one_plus_exp2(float z) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
 }
 
 template <int BT>
@@ -197,9 +196,16 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
         return __hip_atomic_load(ready_ptr(s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
     auto published = [&](unsigned int v) { return static_cast<int>(v - a.ready_target) >= 0; };
-    // Wait until the chunk of step s is published; `seen` is a counter value read earlier.
+    // The counter read one group ahead: even lanes read the chunk of step s, odd lanes the one
+    // after. The per-lane address keeps the value in a vector register across the group (a
+    // value the compiler sees as uniform would be moved to a scalar register at once, which
+    // waits for the load, and with it for every gate prefetch, right after it is issued).
+    auto read_ready_ahead = [&](int s) -> unsigned int {
+        return __hip_atomic_load(ready_ptr(s + (tid & 1) * a.chunk), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // Wait until the chunk of step s is published; `seen` is what read_ready_ahead(s) returned.
     auto wait_ready = [&](unsigned int seen, int s) {
-        if (__builtin_expect(published(seen) || timed_out, 1)) return;
+        if (__builtin_expect(__all((tid & 1) || published(seen)) || timed_out, 1)) return;
         const unsigned long long t0 = wall_clock64();
         while (true) {
             __builtin_amdgcn_s_sleep(1);
@@ -218,8 +224,8 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
             if (win0 + b < a.batch) {
-                __hip_atomic_store(a.progress + 2 * (win0 + b) + dir, a.progress_pass | done, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(a.progress + kProgressStride * (2 * (win0 + b) + dir), a.progress_pass | done,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     };
@@ -242,8 +248,8 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
 
     if constexpr (KG == 1) {
         if constexpr (STREAM) {
-            wait_ready(read_ready(0), 0);
-            ready_seen = read_ready(kRing);
+            wait_ready(read_ready_ahead(0), 0);
+            ready_seen = read_ready_ahead(kRing);
         }
 #pragma unroll
         for (int p = 0; p < kRing; ++p)
@@ -274,6 +280,9 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
         xdir = a.exchange + (static_cast<size_t>(dir) * a.tiles + tile) * 2 * kHidden * BT;
     }
     const bool is_g = q == 2;
+    const float zscale = is_g ? kGateExpScale[2] : kGateExpScale[0];  // of gate q
+    const float act_a = is_g ? 2.0f : 1.0f;
+    const float act_b = is_g ? -1.0f : 0.0f;
     float cst = 0.0f;  // cell state of (unit ug, window qe)
 
     // One step s; P is the step's slot in the prefetch ring (s mod kRing), a compile-time
@@ -287,15 +296,27 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
             // this group refills the ring with steps s + kRing .. s + 2·kRing - 1 (one chunk):
             // check the counter read a group ago, and read the one for the next group
             wait_ready(ready_seen, s + kRing);
-            ready_seen = read_ready(s + 2 * kRing);
+            ready_seen = read_ready_ahead(s + 2 * kRing);
             // Publish this tile's progress. Every wave has passed the previous step's barrier
             // and, before it, waited for the gate load issued kRing steps earlier; vector
             // memory operations complete in issue order, so every output store of the steps
             // before s - 2·kRing has completed.
-            if (tid == 0 && s >= 2 * kRing) publish(static_cast<unsigned int>(s - 2 * kRing));
+            if (tid == 0) publish(static_cast<unsigned int>(s >= 2 * kRing ? s - 2 * kRing : 0));
         }
 
-        // (1) partial dot products over this lane's K quarter
+        // (1) partial dot products over this lane's K quarter; gate q's scaled input starts
+        // the sum in slot 0, so the reduction below yields the whole exponent
+        float zin[BT];
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+            float gin;
+            if constexpr (KG == 1) {
+                gin = ring[P][b];
+            } else {
+                gin = gs[cur][4 * (b * U + u) + q];
+            }
+            zin[b] = gin * zscale;
+        }
         float acc[4][BT];
         {
             const float *hp = &hs[cur][36 * q * BT];
@@ -309,13 +330,15 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
                     const int b = idx % BT;
 #pragma unroll
                     for (int sl = 0; sl < 4; ++sl) {
-                        acc[sl][b] = kk == 0 ? rr[sl][0] * h4[e] : fmaf(rr[sl][kk], h4[e], acc[sl][b]);
+                        acc[sl][b] = kk != 0   ? fmaf(rr[sl][kk], h4[e], acc[sl][b])
+                                     : sl == 0 ? fmaf(rr[0][0], h4[e], zin[b])
+                                               : rr[sl][0] * h4[e];
                     }
                 }
             }
         }
 
-        // (2) reduce-scatter: lane q keeps gate q, sum ((p0+p1)+(p2+p3))
+        // (2) reduce-scatter: lane q keeps gate q's exponent ((p0+p1)+(p2+p3))
         float sum[BT];
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
@@ -324,20 +347,11 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
             sum[b] = t0 + dpp<kXor2>(t2);
         }
 
-        // (3) activation of gate q for each window (tanh(a) = 2σ(2a) - 1 for gate g), then
-        // every lane updates the cell of window qe
+        // (3) activation of gate q for each window, then every lane updates the cell of
+        // window qe
         float act[BT];
 #pragma unroll
-        for (int b = 0; b < BT; ++b) {
-            float gin;
-            if constexpr (KG == 1) {
-                gin = ring[P][b];
-            } else {
-                gin = gs[cur][4 * (b * U + u) + q];
-            }
-            const float sg = sigmoid_f(is_g ? 2.0f * (gin + sum[b]) : gin + sum[b]);
-            act[b] = is_g ? fmaf(2.0f, sg, -1.0f) : sg;
-        }
+        for (int b = 0; b < BT; ++b) act[b] = fmaf(act_a, rcp_one_plus_exp2(sum[b]), act_b);
         float ig[BT], fg[BT], gg[BT], og[BT];
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
@@ -349,7 +363,8 @@ __global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArg
         const float i_w = pick<BT>(ig, qe), f_w = pick<BT>(fg, qe);
         const float g_w = pick<BT>(gg, qe), o_w = pick<BT>(og, qe);
         cst = fmaf(f_w, cst, i_w * g_w);
-        const float hval = o_w * tanh_f(cst);
+        // h = o·tanh(c) = 2o·rcp(1 + 2^(-2c·log2 e)) - o
+        const float hval = fmaf(o_w + o_w, rcp_one_plus_exp2(cst * kGateExpScale[2]), -o_w);
 
         // h to LDS for the next step (lanes of one window write the same value)
         hs[nxt][hpad(ug) * BT + qe] = hval;

@@ -158,11 +158,11 @@ def test_schedule_library_projection_runs_unsliced(bl):
     assert e.value.name == "BILSTM_UNSUPPORTED"
 
 
-@pytest.mark.parametrize("batch,steps,on,chunk", [(1, 589, 0, 0), (8, 589, 0, 0), (15, 589, 0, 0), (16, 589, 1, 32),
+@pytest.mark.parametrize("batch,steps,on,chunk", [(1, 589, 0, 0), (7, 589, 0, 0), (8, 589, 1, 32), (16, 589, 1, 32),
                                                    (32, 589, 1, 32), (64, 4096, 1, 32),
                                                    (96, 589, 1, 32), (97, 589, 0, 0), (256, 589, 0, 0)])
 def test_schedule_streams_gates_when_the_recurrence_leaves_cus(bl, batch, steps, on, chunk):
-    """Auto: streamed gates from 16 windows on, when the recurrence's grid (one workgroup per
+    """Auto: streamed gates from 8 windows on, when the recurrence's grid (one workgroup per
     window and direction) leaves at least a quarter of the 256 CUs to the projection; they
     replace the batch slices."""
     s = bl.schedule(batch, steps, 256, 1)
@@ -194,13 +194,13 @@ def test_schedule_forced_streaming_checks_its_conditions(bl):
 
 @pytest.mark.parametrize("batch,steps,pipeline,overlap", [
     (32, 589, 0, 1), (16, 589, 0, 1), (64, 4096, 0, 1), (96, 589, 0, 1), (32, 589, 3, 0), (64, 4096, 4, 1),
-    (8, 589, 2, 1), (1, 589, 2, 1), (32, 589, 1, 0), (8, 589, 0, 0)])
+    (8, 589, 2, 1), (1, 589, 2, 1), (32, 589, 1, 0), (8, 589, 0, 1), (4, 589, 0, 0)])
 def test_schedule_layer_overlap(bl, batch, steps, pipeline, overlap):
     """Streamed gates overlap the next layer's projection with this layer's recurrence unless
     pipeline = 3 asks for each projection after the previous recurrence."""
     s = bl.schedule(batch, steps, 256, 1, pipeline=pipeline)
     assert s["stream_overlap"] == overlap
-    assert s["pipeline"] == (1 if pipeline >= 2 or (pipeline == 0 and batch >= 16) else 0)
+    assert s["pipeline"] == (1 if pipeline >= 2 or (pipeline == 0 and batch >= 8) else 0)
 
 
 @pytest.mark.parametrize("kwargs,status", [
