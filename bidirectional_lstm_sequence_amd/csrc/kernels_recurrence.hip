@@ -108,8 +108,12 @@ __device__ __forceinline__ void for_slots(F &&f) {
     }
 }
 
+// A workgroup is 512 / KG threads, i.e. 2 / KG waves per SIMD, and one workgroup runs per CU:
+// telling the compiler so keeps it from trading the step's latency for a higher occupancy
+// (squeezed to fit 3 waves, it serialized the LDS reads of h).
 template <int KG, int BT, bool STREAM>
-__global__ __launch_bounds__(4 * (kHidden / KG)) void recurrence_kernel(RecurArgs a) {
+__global__ __launch_bounds__(4 * (kHidden / KG)) __attribute__((amdgpu_waves_per_eu(KG == 1 ? 2 : 1, KG == 1 ? 2 : 1)))
+void recurrence_kernel(RecurArgs a) {
     constexpr int U = kHidden / KG;  // units per workgroup
     constexpr int NT = 4 * U;        // threads
     static_assert(KG == 1 || NT >= 128, "a polling wave besides the staging wave");
