@@ -73,7 +73,6 @@ struct ProjArgs {
     int batch;
     int steps;
     unsigned int *ready;      // [chunks][2][groups] publication counters
-    const int *chunk_order;   // [chunks]: the walk takes chunk chunk_order[i] i-th
     // Inputs written by the previous layer's recurrence while this projection runs
     // (progress != nullptr): before a tile's rows are read, each of its windows' progress word
     // in both directions must reach progress_pass | steps the rows need (see StreamLayout);
@@ -139,10 +138,10 @@ struct HeadArgs {
 // block holds `group_windows` windows × `chunk` steps (128 rows): row r is window
 // g·group_windows + r / chunk at step s = c·chunk + r % chunk of direction d, i.e. time s
 // (forward) or steps - 1 - s (reverse); rows past the batch or past the last step are
-// skipped. Tile q = ((i·2 + d)·groups + g)·4 + column tile holds chunk c = chunk_order[i],
-// columns d·512 + 128·(column tile). Each of a tile's 4 waves adds 1 to
-// ready[(c·2 + d)·groups + g] once its gates are stored with agent-scope stores and those
-// stores have completed, so a pass adds kReadyPerPass to every counter.
+// skipped. Tile q = ((c·2 + d)·groups + g)·4 + column tile, columns d·512 + 128·(column
+// tile): the walk goes chunk by chunk, the order the recurrence reads them. Each of a tile's
+// 4 waves adds 1 to ready[(c·2 + d)·groups + g] once its gates are stored with agent-scope
+// stores and those stores have completed, so a pass adds kReadyPerPass to every counter.
 // A tile of layer l + 1 reads the times of its chunk, all 256 columns, of layer l's output:
 // forward output up to the chunk's last time t_hi (written at forward step t_hi) and reverse
 // output down to its first time t_lo (written at reverse step T-1-t_lo). For chunk c that is

@@ -86,7 +86,6 @@ struct bilstm_plan {
     unsigned long long *ready = nullptr;
     size_t ready_words = 0;
     unsigned long long *progress = nullptr;  // [batch][2] recurrence progress words
-    int *chunk_order = nullptr;              // [2][chunks]: layer 0's walk, later layers' walk
     int stream_groups = 0;
     int stream_chunks = 0;
     uint32_t ready_passes[2] = {0, 0};  // streamed passes per gate buffer since the last clear
@@ -196,7 +195,6 @@ void release(bilstm_plan *p) {
     if (p->gates_odd) (void)hipFree(p->gates_odd);
     if (p->ready) (void)hipFree(p->ready);
     if (p->progress) (void)hipFree(p->progress);
-    if (p->chunk_order) (void)hipFree(p->chunk_order);
     if (p->library) library_projection_destroy(p->library);
     if (p->gates) (void)hipFree(p->gates);
     if (p->exchange) (void)hipFree(p->exchange);
@@ -273,13 +271,9 @@ bilstm_status enqueue_projection(bilstm_plan *p, int layer, const float *x, floa
         args.tiles = p->stream_chunks * 2 * args.groups * (kGates / kProjTileN);
         args.error = p->error;
         args.timeout_ticks = p->timeout_ticks;
-        if (layer == 0 || !p->info.stream_overlap) {
-            // the input is complete before the pass starts: chunks in the recurrence's order
-            args.chunk_order = p->chunk_order;
-        } else {
-            // the previous layer's recurrence, running now, still writes the input: chunks in
-            // the order their rows appear, each waiting for its rows
-            args.chunk_order = p->chunk_order + p->stream_chunks;
+        if (layer > 0 && p->info.stream_overlap) {
+            // the previous layer's recurrence, running now, still writes the input: each tile
+            // waits for its rows
             args.progress = p->progress;
             args.progress_pass = static_cast<unsigned long long>(p->layer_pass - 1) << 32;
         }
@@ -613,14 +607,6 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
         p->stream_chunks = stream_chunks(static_cast<int>(steps), info.stream_chunk);
         const size_t counters = static_cast<size_t>(p->stream_chunks) * 2 * p->stream_groups;
         p->ready_words = (counters + 1) / 2;
-        // the projection walks: layer 0 in the recurrence's order, later layers by when the
-        // previous layer's recurrence has written the chunk's rows (middle chunks first)
-        std::vector<int> order(2 * static_cast<size_t>(p->stream_chunks));
-        for (int c = 0; c < p->stream_chunks; ++c) order[c] = order[p->stream_chunks + c] = c;
-        if (false) std::stable_sort(order.begin() + p->stream_chunks, order.end(), [&](int u, int v) {
-            return stream_need(static_cast<int>(steps), info.stream_chunk, u) <
-                   stream_need(static_cast<int>(steps), info.stream_chunk, v);
-        });
         if ((st = device_alloc(p, &p->ybuf, rows * kWidth, "layer buffer")) != BILSTM_OK) return fail_release(st);
         if ((st = device_alloc(p, &p->gates_odd, rows * kGateCols, "second gate buffer")) != BILSTM_OK) {
             return fail_release(st);
@@ -630,13 +616,9 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
             BILSTM_OK) {
             return fail_release(st);
         }
-        if ((st = device_alloc(p, &p->chunk_order, order.size(), "chunk order")) != BILSTM_OK) return fail_release(st);
         e = hipMemset(p->ready, 0, 2 * p->ready_words * sizeof(unsigned long long));
         if (e == hipSuccess) {
             e = hipMemset(p->progress, 0, kProgressStride * 2 * static_cast<size_t>(batch) * sizeof(unsigned long long));
-        }
-        if (e == hipSuccess) {
-            e = hipMemcpy(p->chunk_order, order.data(), order.size() * sizeof(int), hipMemcpyHostToDevice);
         }
         if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->proj_stream, hipStreamNonBlocking);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&p->proj_fork, hipEventDisableTiming);

@@ -413,10 +413,10 @@ __device__ __forceinline__ StreamTile stream_tile(const ProjArgs &a, int q) {
     const int ct = q & 3;
     const int rest = q >> 2;
     const int g = rest % a.groups;
-    const int id = rest / a.groups;  // walk position · 2 + direction
+    const int id = rest / a.groups;  // chunk · 2 + direction
     StreamTile t;
     t.dir = id & 1;
-    t.c = a.chunk_order[id >> 1];
+    t.c = id >> 1;
     t.w0 = g * a.group_windows;
     t.s0 = t.c * a.chunk;
     t.n0 = t.dir * kGates + ct * BN;
@@ -654,7 +654,7 @@ hipError_t launch_projection(const ProjArgs &args, int workgroups, size_t dynami
     nwg = std::max(8, nwg / 8 * 8);
     if (args.chunk > 0) {
         // streamed order: FP32 kernel only
-        if (args.w_hi != nullptr || args.ready == nullptr || args.chunk_order == nullptr ||
+        if (args.w_hi != nullptr || args.ready == nullptr ||
             args.chunk * args.group_windows != kProjTileM || (1 << args.chunk_shift) != args.chunk) {
             return hipErrorInvalidValue;
         }
