@@ -326,9 +326,18 @@ void recurrence_kernel(RecurArgs a) {
         float acc[4][BT];
         {
             const float *hp = &hs[cur][36 * q * BT];
+            // every LDS read of h first, so their latencies overlap (the FMAs then wait for
+            // each in turn). Left to itself the compiler spaced them out in the streamed and
+            // multi-window kernels; there a scheduling barrier keeps them together (measured:
+            // streamed b32 forward 1.30 -> 1.298 ms, two windows 0.998 -> 0.955 us per step),
+            // while it slows the plain one-window kernel (0.471 -> 0.491 us), already in order.
+            v4f hv[8 * BT];
+#pragma unroll
+            for (int v = 0; v < 8 * BT; ++v) hv[v] = *reinterpret_cast<const v4f *>(hp + 4 * v);
+            if constexpr (STREAM || BT > 1) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int v = 0; v < 8 * BT; ++v) {
-                const v4f h4 = *reinterpret_cast<const v4f *>(hp + 4 * v);
+                const v4f h4 = hv[v];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int idx = 4 * v + e;  // = k_local·BT + b
