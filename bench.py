@@ -81,8 +81,8 @@ def recorded_traffic(workload: str, info: dict):
               "windows_per_launch": rec["windows_per_launch"], "source": "profiles/recurrence_traffic.json"}
     same = rec.get("slices") == info["slices"] and rec.get("pipeline", 0) == info["pipeline"]
     if not same:
-        detail["note"] = ("proxy: the unstreamed recurrence under --pmc; the timed launch is the streamed "
-                          "kernel, which counter collection (kernels one at a time) cannot run")
+        detail["note"] = ("proxy: the unstreamed recurrence of one layer under --pmc; the timed launch is the "
+                          "streamed kernel, which counter collection (kernels one at a time) cannot run")
     return (detail["bytes_per_launch"] if same else None), detail
 
 
@@ -178,11 +178,18 @@ def main() -> int:
     timed_phases = plan.phase_times()
 
     # The recurrence launch bracketed by the plan's events in the last timed forward (the first
-    # slice's launch when the batch runs in slices): the dominant kernel's duration.
-    launch_dur_ms = statistics.mean(timed_phases["recurrence_launch_ms"])
+    # slice's launch when the batch runs in slices): the dominant kernel's duration. With the
+    # four streamed recurrences in one launch, the four values are that launch's per-layer
+    # shares and add up to its duration.
+    fused = bool(info["stream_fused"])
+    layers_per_launch = 4 if fused else 1
+    if fused:
+        launch_dur_ms = sum(timed_phases["recurrence_launch_ms"])
+    else:
+        launch_dur_ms = statistics.mean(timed_phases["recurrence_launch_ms"])
     slice_windows = info["slice_windows"] if info["slices"] > 1 else wl.batch
     launch_dirs = 2 if info["concurrent"] == 2 else 1
-    flop_per_launch = launch_dirs * recurrence_flops_per_layer(slice_windows * wl.steps) / 2
+    flop_per_launch = layers_per_launch * launch_dirs * recurrence_flops_per_layer(slice_windows * wl.steps) / 2
 
     # Each kernel alone, outside the timed region, on the whole batch: the projection of every
     # layer (bilstm_project) and the recurrence of every layer (bilstm_recur), each between HIP
@@ -290,15 +297,18 @@ def main() -> int:
                                         "concurrent": info["concurrent"]},
                    "slices": info["slices"], "slice_windows": info["slice_windows"],
                    "streamed_gates": {"on": bool(info["pipeline"]), "chunk_steps": info["stream_chunk"],
-                                      "layers_overlap": bool(info["stream_overlap"])}},
-        "roofline": {"kernel": f"recurrence_kernel<{groups}, {tile}, {'true' if info['pipeline'] else 'false'}> "
-                               f"({launch_dirs} direction(s) per launch"
+                                      "layers_overlap": bool(info["stream_overlap"]),
+                                      "one_recurrence_launch": fused}},
+        "roofline": {"kernel": (f"recurrence_stream_kernel<{tile}>" if info["pipeline"]
+                                else f"recurrence_kernel<{groups}, {tile}>") +
+                               f" ({launch_dirs} direction(s), {layers_per_launch} layer(s) per launch"
                                f"{', streamed gates' if info['pipeline'] else ''})",
                      "bound": "alu", "achieved": rec_tflops, "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
                      "frac": rec_tflops / PEAK_FP32_VECTOR_TFLOPS,
                      "traffic": traffic,
                      "launch_ms": launch_dur_ms,
                      "flop_per_launch": flop_per_launch,
+                     "layers_per_launch": layers_per_launch,
                      "windows_per_launch": slice_windows,
                      "traffic_detail": traffic_detail},
         "recurrence_step": {"us_per_step": us_per_step, "bound_us": bound_us,

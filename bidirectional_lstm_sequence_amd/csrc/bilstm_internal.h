@@ -112,6 +112,18 @@ struct RecurArgs {
     unsigned long long progress_pass;
 };
 
+// Streamed gates: the recurrences of `layers` consecutive layers (layer[0] first) in one
+// launch of tile_count tiles × both directions; every entry has chunk > 0, direction 0 and the
+// same tiles.
+struct RecurStack {
+    RecurArgs layer[kLayers];
+    int layers;
+    // Phase timing, or nullptr: stamps[l] = the latest end of layer l over the workgroups and
+    // stamps[kLayers] = ~(the earliest start), in wall-clock ticks (atomic maxima over words
+    // cleared to zero before the launch).
+    unsigned long long *stamps;
+};
+
 // Segmentation heads after the stack: 256 -> 128 -> 128 -> 7 (class slots padded to 8).
 constexpr int kHeadIn = 256;
 constexpr int kHeadMid = 128;
@@ -173,6 +185,9 @@ hipError_t launch_projection(const ProjArgs &args, int workgroups, size_t dynami
 hipError_t projection_allow_lds(size_t bytes);
 hipError_t launch_recurrence(int groups, int tile, const RecurArgs &args, int directions,
                              size_t dynamic_lds, hipStream_t stream);
+// The streamed recurrences of several layers in one launch (single-workgroup tiles of `tile`
+// windows).
+hipError_t launch_recurrence_stack(int tile, const RecurStack &stack, size_t dynamic_lds, hipStream_t stream);
 // Allow `bytes` of dynamic LDS per recurrence workgroup of this split.
 hipError_t recurrence_allow_lds(int groups, int tile, size_t bytes);
 hipError_t launch_exchange_clear(unsigned long long *words, size_t count, hipStream_t stream);

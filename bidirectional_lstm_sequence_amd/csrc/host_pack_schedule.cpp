@@ -189,6 +189,11 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
     // (3): measured faster both where the recurrence sets the pace (b32: 1.44 -> 1.39 ms) and
     // where the projection does (b64_t4096: 10.45 -> 10.32 ms).
     info->stream_overlap = pipeline && want_pipe != 3 ? 1 : 0;
+    // With overlap, the four layers' recurrences run as one launch when one launch holds both
+    // directions of every tile (measured: each layer boundary then costs the first chunk's
+    // latency only, not also a kernel launch after the previous layer's end); 4 keeps a launch
+    // per layer.
+    info->stream_fused = info->stream_overlap && concurrent == 2 && launches == 1 && want_pipe != 4 ? 1 : 0;
     info->recur_groups = groups;
     info->recur_tile = tile;
     info->recur_tiles = tiles;

@@ -86,6 +86,8 @@ struct bilstm_plan {
     unsigned long long *ready = nullptr;
     size_t ready_words = 0;
     unsigned long long *progress = nullptr;  // [batch][2] recurrence progress words
+    unsigned long long *stamps = nullptr;    // phase timing of a one-launch recurrence (after progress)
+    bool phases_fused = false;               // the recorded forward ran its recurrences as one launch
     int stream_groups = 0;
     int stream_chunks = 0;
     uint32_t ready_passes[2] = {0, 0};  // streamed passes per gate buffer since the last clear
@@ -100,6 +102,7 @@ struct bilstm_plan {
     unsigned long long timeout_ticks = 0;
     unsigned int flag_skew = 0;
     double watchdog_ms = 0.0;
+    double wall_khz = 0.0;  // wall-clock ticks per millisecond
     uint64_t device_bytes = 0;
 };
 
@@ -285,9 +288,8 @@ bilstm_status enqueue_projection(bilstm_plan *p, int layer, const float *x, floa
 // Both directions' recurrence of one layer over window tiles [tile_lo, tile_hi) (speakrs
 // 0.6.0, page `lstmproj.rs`, `Oxide::recur`: the reverse direction on the side stream when
 // the schedule allows it, joined back before the next layer).
-bilstm_status enqueue_recurrence(bilstm_plan *p, int layer, const float *gates, float *y,
-                                 uint32_t flag_base, hipStream_t stream, bool layer_events,
-                                 int tile_lo, int tile_hi, bool streamed = false, int buffer = 0) {
+RecurArgs recurrence_args(const bilstm_plan *p, int layer, const float *gates, float *y, uint32_t flag_base,
+                          bool streamed, int buffer) {
     const bilstm_plan_info &s = p->info;
     RecurArgs base{};
     base.gates = gates;
@@ -311,7 +313,14 @@ bilstm_status enqueue_recurrence(bilstm_plan *p, int layer, const float *gates, 
         base.progress = p->progress;
         base.progress_pass = static_cast<unsigned long long>(p->layer_pass) << 32;
     }
+    return base;
+}
 
+bilstm_status enqueue_recurrence(bilstm_plan *p, int layer, const float *gates, float *y,
+                                 uint32_t flag_base, hipStream_t stream, bool layer_events,
+                                 int tile_lo, int tile_hi, bool streamed = false, int buffer = 0) {
+    const bilstm_plan_info &s = p->info;
+    const RecurArgs base = recurrence_args(p, layer, gates, y, flag_base, streamed, buffer);
     const int per_launch = (s.recur_tiles + s.recur_launches - 1) / s.recur_launches;
     const size_t lds = p->reserve_lds;
     // With phase events on, the first launch on the caller's stream is bracketed by its own
@@ -371,6 +380,9 @@ bilstm_status forward_streamed(bilstm_plan *p, const float *x, float *y, hipStre
     BL_HIP(hipEventRecord(p->proj_fork, stream), "projection fork");
     BL_HIP(hipStreamWaitEvent(p->proj_stream, p->proj_fork, 0), "projection fork wait");
     if (p->phase_events) BL_HIP(hipEventRecord(p->ev_start, stream), "phase event");
+    // the four recurrences in one launch
+    const bool one_launch = p->info.stream_fused != 0;
+    RecurStack stack{};
     for (int l = 0; l < kLayers; ++l) {
         const int buffer = l % 2;
         const float *in = l == 0 ? x : (l % 2 == 1 ? p->ybuf : y);
@@ -386,6 +398,14 @@ bilstm_status forward_streamed(bilstm_plan *p, const float *x, float *y, hipStre
             return st;
         }
         if (p->phase_events) BL_HIP(hipEventRecord(p->ev_proj[l], p->proj_stream), "phase event");
+        if (one_launch) {
+            RecurArgs &a = stack.layer[l];
+            a = recurrence_args(p, l, gates, out, base + l * p->steps, true, buffer);
+            a.direction = 0;
+            a.tile_first = 0;
+            a.tile_count = p->info.recur_tiles;
+            continue;
+        }
         if ((st = enqueue_recurrence(p, l, gates, out, base + l * p->steps, stream, true, 0, p->info.recur_tiles,
                                      true, buffer)) != BILSTM_OK) {
             return st;
@@ -393,10 +413,25 @@ bilstm_status forward_streamed(bilstm_plan *p, const float *x, float *y, hipStre
         if (!p->info.stream_overlap) BL_HIP(hipEventRecord(p->layer_done[l], stream), "layer event");
         if (p->phase_events) BL_HIP(hipEventRecord(p->ev_recur[l], stream), "phase event");
     }
+    if (one_launch) {
+        stack.layers = kLayers;
+        if (p->phase_events) {
+            // the launch between its own events; stamps split it into layers
+            BL_HIP(launch_exchange_clear(p->stamps, kLayers + 1, stream), "stamp clear");
+            stack.stamps = p->stamps;
+            BL_HIP(hipEventRecord(p->ev_launch0[0], stream), "phase event");
+        }
+        BL_HIP(launch_recurrence_stack(p->info.recur_tile, stack, p->reserve_lds, stream), "recurrence launch");
+        if (p->phase_events) {
+            BL_HIP(hipEventRecord(p->ev_launch1[0], stream), "phase event");
+            BL_HIP(hipEventRecord(p->ev_recur[kLayers - 1], stream), "phase event");
+        }
+    }
     BL_HIP(hipEventRecord(p->proj_join, p->proj_stream), "projection join");
     BL_HIP(hipStreamWaitEvent(stream, p->proj_join, 0), "projection join wait");
     p->phases_recorded = p->phase_events;
     p->phases_streamed = true;
+    p->phases_fused = one_launch;
     return BILSTM_OK;
 }
 
@@ -483,6 +518,7 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
     const int32_t wd_us = options != nullptr ? options->watchdog_us : 0;
     const double watchdog_ms = wd_us > 0 ? wd_us / 1000.0 : (wd_us < 0 ? 0.0 : kWatchdogMs);
     p->timeout_ticks = static_cast<unsigned long long>(watchdog_ms * wall_khz);
+    p->wall_khz = wall_khz;
     p->watchdog_ms = watchdog_ms;
     // watchdog_us = -1: every wait expects a flag that no producer ever writes, so its first
     // poll misses and it gives up at once: a forced, deterministic timeout
@@ -612,10 +648,12 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
             return fail_release(st);
         }
         if ((st = device_alloc(p, &p->ready, 2 * p->ready_words, "chunk counters")) != BILSTM_OK) return fail_release(st);
-        if ((st = device_alloc(p, &p->progress, kProgressStride * 2 * static_cast<size_t>(batch), "progress words")) !=
-            BILSTM_OK) {
+        // the progress words, then one line of phase stamps
+        if ((st = device_alloc(p, &p->progress, kProgressStride * (2 * static_cast<size_t>(batch) + 1),
+                               "progress words")) != BILSTM_OK) {
             return fail_release(st);
         }
+        p->stamps = p->progress + kProgressStride * 2 * static_cast<size_t>(batch);
         e = hipMemset(p->ready, 0, 2 * p->ready_words * sizeof(unsigned long long));
         if (e == hipSuccess) {
             e = hipMemset(p->progress, 0, kProgressStride * 2 * static_cast<size_t>(batch) * sizeof(unsigned long long));
@@ -720,6 +758,7 @@ bilstm_status bilstm_forward(bilstm_plan *plan, const float *x, size_t x_len, fl
     }
     plan->phases_recorded = plan->phase_events;
     plan->phases_streamed = false;
+    plan->phases_fused = false;
     return BILSTM_OK;
 }
 
@@ -788,6 +827,32 @@ bilstm_status bilstm_phase_times(bilstm_plan *plan, float *ms, size_t n) {
     DeviceScope scope(plan->device);
     BL_HIP(scope.error(), "phase_times: hipSetDevice");
     BL_HIP(hipEventSynchronize(plan->ev_recur[kLayers - 1]), "phase_times");
+    if (plan->phases_fused) {
+        // One recurrence launch for the four layers, between its own events (duration L, end
+        // E from the forward's start). The stamps place each layer's end inside it: layer l
+        // ends at E - L·(1 - f_l), f_l = (its end - the launch's start) / (the last layer's end
+        // - the launch's start) on the GPU's wall clock; its share of the launch is L·(f_l -
+        // f_{l-1}).
+        unsigned long long st[kLayers + 1];
+        BL_HIP(hipMemcpy(st, plan->stamps, sizeof(st), hipMemcpyDeviceToHost), "phase_times");
+        const unsigned long long t0 = ~st[kLayers];
+        if (st[kLayers] == 0 || st[kLayers - 1] <= t0) {
+            return fail(BILSTM_HIP_ERROR, "phase_times: the recurrence launch left no stamps");
+        }
+        float e_end = 0.0f, l_dur = 0.0f;
+        BL_HIP(hipEventElapsedTime(&e_end, plan->ev_start, plan->ev_launch1[0]), "phase_times");
+        BL_HIP(hipEventElapsedTime(&l_dur, plan->ev_launch0[0], plan->ev_launch1[0]), "phase_times");
+        const double span = static_cast<double>(st[kLayers - 1] - t0);
+        double before = 0.0;
+        for (int l = 0; l < kLayers; ++l) {
+            BL_HIP(hipEventElapsedTime(&ms[l], plan->ev_start, plan->ev_proj[l]), "phase_times");
+            const double f = st[l] > t0 ? std::min(1.0, static_cast<double>(st[l] - t0) / span) : 0.0;
+            ms[kLayers + l] = static_cast<float>(e_end - l_dur * (1.0 - f));
+            ms[2 * kLayers + l] = static_cast<float>(l_dur * (f - before));
+            before = f;
+        }
+        return BILSTM_OK;
+    }
     for (int l = 0; l < kLayers; ++l) {
         // streamed: the end of every phase from the forward's start (the phases of a layer and
         // of its neighbours overlap); else each phase's own duration

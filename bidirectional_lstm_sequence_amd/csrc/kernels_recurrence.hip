@@ -38,7 +38,9 @@
 // which see the projection's agent-scope stores once its counter shows them complete. In
 // turn the output is written with agent-scope stores and each window's progress (steps whose
 // output has completed) is published every kRing steps, for the next layer's projection when
-// it runs beside this recurrence.
+// it runs beside this recurrence. One launch can run several layers this way
+// (recurrence_stream_kernel): a workgroup that has finished a layer moves on to the next
+// with the same tile and direction.
 //
 // Waits are bounded: a poll that sees no progress for `timeout_ticks` wall-clock ticks
 // sets the error word and stops waiting, so the grid always drains.
@@ -82,10 +84,17 @@ __device__ __forceinline__ float rcp_one_plus_exp2(float z) {
 
 template <int BT>
 __device__ __forceinline__ float pick(const float (&v)[BT], int b) {
-    float r = v[0];
+    // v[b] as a register vector element: a chain of selects over the array's elements is
+    // turned by the optimizer into an indexed load from a stack copy of the array
+    if constexpr (BT == 1) {
+        return v[0];
+    } else {
+        typedef float vec_t __attribute__((ext_vector_type(BT)));
+        vec_t x;
 #pragma unroll
-    for (int i = 1; i < BT; ++i) r = (b == i) ? v[i] : r;
-    return r;
+        for (int i = 0; i < BT; ++i) x[i] = v[i];
+        return x[b];
+    }
 }
 
 __device__ __forceinline__ unsigned long long load_word(const unsigned long long *p) {
@@ -110,12 +119,10 @@ __device__ __forceinline__ void for_slots(F &&f) {
     }
 }
 
-// A workgroup is 512 / KG threads, i.e. 2 / KG waves per SIMD, and one workgroup runs per CU:
-// telling the compiler so keeps it from trading the step's latency for a higher occupancy
-// (squeezed to fit 3 waves, it serialized the LDS reads of h).
+// One layer's recurrence for this workgroup's tile and direction. `timed_out` is set once a
+// wait has given up; every later wait of the workgroup then returns at once.
 template <int KG, int BT, bool STREAM>
-__global__ __launch_bounds__(4 * (kHidden / KG)) __attribute__((amdgpu_waves_per_eu(KG == 1 ? 2 : 1, KG == 1 ? 2 : 1)))
-void recurrence_kernel(RecurArgs a) {
+__device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed_out) {
     constexpr int U = kHidden / KG;  // units per workgroup
     constexpr int NT = 4 * U;        // threads
     static_assert(KG == 1 || NT >= 128, "a polling wave besides the staging wave");
@@ -191,7 +198,6 @@ void recurrence_kernel(RecurArgs a) {
 
     // STREAM: publication counter of the chunk holding step s (clamped to the last step) for
     // this tile's window group and direction
-    bool timed_out = false;
     const unsigned int *ready_tile =
         STREAM ? a.ready + static_cast<size_t>(dir) * a.groups + win0 / a.group_windows : nullptr;
     auto ready_ptr = [&](int s) {
@@ -331,13 +337,18 @@ void recurrence_kernel(RecurArgs a) {
             // multi-window kernels; there a scheduling barrier keeps them together (measured:
             // streamed b32 forward 1.30 -> 1.298 ms, two windows 0.998 -> 0.955 us per step),
             // while it slows the plain one-window kernel (0.471 -> 0.491 us), already in order.
-            v4f hv[8 * BT];
+            // Four windows' h (128 registers) would not fit beside R: there the compiler
+            // schedules the reads.
+            constexpr bool kUpfront = BT <= 2;
+            v4f hv[kUpfront ? 8 * BT : 1];
+            if constexpr (kUpfront) {
 #pragma unroll
-            for (int v = 0; v < 8 * BT; ++v) hv[v] = *reinterpret_cast<const v4f *>(hp + 4 * v);
-            if constexpr (STREAM || BT > 1) __builtin_amdgcn_sched_barrier(0);
+                for (int v = 0; v < 8 * BT; ++v) hv[v] = *reinterpret_cast<const v4f *>(hp + 4 * v);
+                if constexpr (STREAM || BT > 1) __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int v = 0; v < 8 * BT; ++v) {
-                const v4f h4 = hv[v];
+                const v4f h4 = kUpfront ? hv[v] : *reinterpret_cast<const v4f *>(hp + 4 * v);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int idx = 4 * v + e;  // = k_local·BT + b
@@ -460,6 +471,33 @@ void recurrence_kernel(RecurArgs a) {
     }
 }
 
+// A workgroup is 512 / KG threads, i.e. 2 / KG waves per SIMD, and one workgroup runs per CU:
+// telling the compiler so keeps it from trading the step's latency for a higher occupancy
+// (squeezed to fit 3 waves, it serialized the LDS reads of h).
+template <int KG, int BT>
+__global__ __launch_bounds__(4 * (kHidden / KG)) __attribute__((amdgpu_waves_per_eu(KG == 1 ? 2 : 1, KG == 1 ? 2 : 1)))
+void recurrence_kernel(RecurArgs a) {
+    bool timed_out = false;
+    recurrence_layer<KG, BT, false>(a, timed_out);
+}
+
+// Streamed gates: the recurrences of `layers` consecutive layers in one launch. Each
+// workgroup keeps its tile and direction and goes from one layer to the next by itself: it
+// reloads R and waits for the next layer's first chunk, which the next projection computes
+// once every window of the chunk has finished this layer in both directions. No workgroup
+// waits for another layer's launch, so the gap between layers is that first chunk's latency.
+template <int BT>
+__global__ __launch_bounds__(4 * kHidden) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void recurrence_stream_kernel(RecurStack st) {
+    bool timed_out = false;
+    if (st.stamps != nullptr && threadIdx.x == 0) atomicMax(st.stamps + kLayers, ~wall_clock64());
+    for (int l = 0; l < st.layers; ++l) {
+        recurrence_layer<1, BT, true>(st.layer[l], timed_out);
+        // the layer ends with a workgroup barrier
+        if (st.stamps != nullptr && threadIdx.x == 0) atomicMax(st.stamps + l, wall_clock64());
+    }
+}
+
 __global__ void exchange_clear_kernel(unsigned long long *words, size_t count) {
     for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
          i += static_cast<size_t>(gridDim.x) * blockDim.x) {
@@ -511,33 +549,34 @@ __global__ void exchange_probe_kernel(unsigned long long *words, int partner, in
 template <int KG, int BT>
 hipError_t launch_typed(const RecurArgs &args, int directions, size_t lds, hipStream_t stream) {
     const int nwg = KG == 1 ? args.tile_count : (args.tile_count + 7) / 8 * 8 * KG;
-    if constexpr (KG == 1) {
-        if (args.chunk > 0) {
-            hipLaunchKernelGGL((recurrence_kernel<KG, BT, true>), dim3(nwg, directions), dim3(recur_threads(KG)),
-                               lds, stream, args);
+    if (args.chunk > 0) {
+        if constexpr (KG == 1) {
+            RecurStack st{};
+            st.layer[0] = args;
+            st.layers = 1;
+            hipLaunchKernelGGL((recurrence_stream_kernel<BT>), dim3(nwg, directions), dim3(recur_threads(KG)), lds,
+                               stream, st);
             return hipGetLastError();
         }
-    } else {
-        if (args.chunk > 0) return hipErrorInvalidValue;
+        return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL((recurrence_kernel<KG, BT, false>), dim3(nwg, directions), dim3(recur_threads(KG)), lds,
-                       stream, args);
+    hipLaunchKernelGGL((recurrence_kernel<KG, BT>), dim3(nwg, directions), dim3(recur_threads(KG)), lds, stream,
+                       args);
     return hipGetLastError();
 }
 
 template <int KG, int BT>
 hipError_t allow_lds_typed(size_t bytes) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&recurrence_kernel<KG, BT, false>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&recurrence_kernel<KG, BT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
     if (e != hipSuccess || KG != 1) return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&recurrence_kernel<KG, BT, KG == 1>),
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&recurrence_stream_kernel<BT>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
 }
 
 template <int KG, int BT>
 hipError_t occupancy_typed(int *per_cu) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, recurrence_kernel<KG, BT, false>, recur_threads(KG),
-                                                        0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, recurrence_kernel<KG, BT>, recur_threads(KG), 0);
 }
 
 #define BL_FOR_EACH_SPLIT(X) X(1, 1) X(1, 2) X(1, 4) X(2, 1) X(2, 2) X(2, 4) X(4, 1) X(4, 2) X(4, 4)
@@ -552,6 +591,34 @@ hipError_t launch_recurrence(int groups, int tile, const RecurArgs &args, int di
     BL_FOR_EACH_SPLIT(BL_CASE)
 #undef BL_CASE
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_recurrence_stack(int tile, const RecurStack &stack, size_t dynamic_lds, hipStream_t stream) {
+    const RecurArgs &a = stack.layer[0];
+    if (stack.layers < 1 || stack.layers > kLayers || a.tile_count <= 0 || a.direction != 0) {
+        return hipErrorInvalidValue;
+    }
+    for (int l = 0; l < stack.layers; ++l) {
+        const RecurArgs &b = stack.layer[l];
+        if (b.chunk <= 0 || b.tile_first != a.tile_first || b.tile_count != a.tile_count || b.direction != 0) {
+            return hipErrorInvalidValue;
+        }
+    }
+    const dim3 grid(a.tile_count, 2);
+    switch (tile) {
+        case 1:
+            hipLaunchKernelGGL(recurrence_stream_kernel<1>, grid, dim3(recur_threads(1)), dynamic_lds, stream, stack);
+            break;
+        case 2:
+            hipLaunchKernelGGL(recurrence_stream_kernel<2>, grid, dim3(recur_threads(1)), dynamic_lds, stream, stack);
+            break;
+        case 4:
+            hipLaunchKernelGGL(recurrence_stream_kernel<4>, grid, dim3(recur_threads(1)), dynamic_lds, stream, stack);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t recurrence_allow_lds(int groups, int tile, size_t bytes) {

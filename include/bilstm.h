@@ -124,7 +124,9 @@ typedef struct {
                              2 = on (BILSTM_UNSUPPORTED unless recur_groups = 1, projection = 0,
                              slices <= 1 and at least 8 CUs stay free), with the next layer's
                              projection starting during this layer's recurrence; 3 = on, with it
-                             starting after this layer's recurrence; 4 = the same as 2.
+                             starting after this layer's recurrence; 4 = as 2, with one
+                             recurrence launch per layer where 2 runs the four layers'
+                             recurrences as one launch (bilstm_plan_info.stream_fused).
                              Every wait on a counter is bounded by the watchdog like every other
                              wait: if the GPU is shared with other work that keeps a kernel from
                              running, bilstm_check reports BILSTM_TIMEOUT instead of hanging */
@@ -154,6 +156,10 @@ typedef struct {
                                 windows per projection row block); 0 when not streamed */
     int32_t stream_overlap;  /* streamed gates: 1 when the next layer's projection starts during
                                 this layer's recurrence, 0 when after it */
+    int32_t stream_fused;    /* streamed gates: 1 when the four layers' recurrences run as one
+                                launch (overlap on, concurrent = 2, recur_launches = 1, pipeline
+                                != 4); each workgroup then moves from a layer to the next by
+                                itself */
 } bilstm_plan_info;
 
 /*
@@ -222,7 +228,11 @@ bilstm_status bilstm_check(bilstm_plan *plan);
  * caller's stream of layers 0..3 (the launch running both directions when they share one
  * launch, else the forward direction's). n must be >= 12. With streamed gates the phases of a
  * layer and of its neighbours overlap: the first 8 values are then the time from the forward's
- * start to the end of each projection and of each recurrence.
+ * start to the end of each projection and of each recurrence. When the four recurrences run
+ * as one launch (bilstm_plan_info.stream_fused), that launch is timed by its own event pair
+ * and split into layers by wall-clock stamps the kernel records (each layer's latest end over
+ * the workgroups): the last 4 values are then each layer's share of the launch (from the
+ * previous layer's end, or the launch's start) and sum to its duration.
  */
 bilstm_status bilstm_set_phase_events(bilstm_plan *plan, int enable);
 bilstm_status bilstm_phase_times(bilstm_plan *plan, float *ms, size_t n);

@@ -60,22 +60,25 @@ SHAPES = [(1, 589, 0), (1, 1, 0), (2, 130, 0), (3, 150, 0), (3, 3, 0), (5, 7, 0)
           (8, 97, 2), (8, 64, 4), (32, 150, 0)]
 
 
-@pytest.mark.parametrize("pipeline", [4, 3])
+@pytest.mark.parametrize("pipeline", [2, 4, 3])
 @pytest.mark.parametrize("batch,steps,tile", SHAPES)
 def test_streamed_equals_unstreamed_bitwise(bl, batch, steps, tile, pipeline):
-    """pipeline 4: the next layer's projection runs during this layer's recurrence, reading the
-    rows it publishes; 3: after it."""
+    """pipeline 2: the next layer's projection runs during this layer's recurrence, reading the
+    rows it publishes, and the four recurrences run as one launch; 4: the same with a launch
+    per layer; 3: each projection after the previous layer's recurrence."""
     x = workloads.make_input(40 + batch, batch, steps)
     layers = workloads.make_layers(41)
     note(f"streamed (pipeline={pipeline}) vs unstreamed batch={batch} steps={steps} tile={tile}")
     got, info = run(bl, x, layers, pipeline=pipeline, tile=tile)
     base, binfo = run(bl, x, layers, pipeline=1, slices=1, tile=tile)
     assert info["pipeline"] == 1 and binfo["pipeline"] == 0
-    assert info["stream_overlap"] == (1 if pipeline == 4 else 0)
+    assert info["stream_overlap"] == (0 if pipeline == 3 else 1)
+    one_launch = info["concurrent"] == 2 and info["recur_launches"] == 1
+    assert info["stream_fused"] == (1 if pipeline == 2 and one_launch else 0)
     assert np.array_equal(got[0].view(np.uint32), base[0].view(np.uint32))
 
 
-@pytest.mark.parametrize("pipeline", [4, 3])
+@pytest.mark.parametrize("pipeline", [2, 4, 3])
 def test_streamed_repeated_forwards_are_bit_stable(bl, pipeline):
     """Five forwards on one plan: each pass's counters reach the next target exactly once."""
     x, layers = workloads.make_workload("b8")
@@ -97,29 +100,39 @@ def test_streamed_matches_oracle(bl, orc):
     note(f"streamed b8 max abs err {err.max():.3e} chunk {info['stream_chunk']}")
 
 
-@pytest.mark.parametrize("pipeline", [4, 3])
+@pytest.mark.parametrize("pipeline", [2, 4, 3])
 def test_streamed_phase_times(bl, pipeline):
     x, layers = workloads.make_workload("b8")
     xs = np.ascontiguousarray(x[:, :100])
     note(f"streamed phase times pipeline={pipeline}")
     plan = bl.Plan(layers, 8, 100, pipeline=pipeline)
     xd = torch.from_numpy(xs).cuda()
-    plan.forward(xd)
+    ref = plan.forward(xd).cpu().numpy()
     plan.set_phase_events(True)
-    plan.forward(xd)
+    got = plan.forward(xd).cpu().numpy()
     t = plan.phase_times()
     plan.check()
+    fused = plan.info()["stream_fused"]
     plan.close()
+    assert fused == (1 if pipeline == 2 else 0)
+    # timing changes nothing in the results
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
     rec = t["recurrence_ms"]
     for l in range(4):
         # phase ends from the forward's start: recurrences end in order, each after the
-        # projection whose gates it reads, and each launch lasts at most until its end
+        # projection whose gates it reads, and each launch (or layer's share of the one
+        # launch) lasts at most until its end
         assert 0 < t["projection_ms"][l] < rec[l] + 1e-3
         assert l == 0 or rec[l - 1] < rec[l]
         assert 0 < t["recurrence_launch_ms"][l] <= rec[l] + 1e-3
+    if fused:
+        # the shares of the one launch add up to it and end with the last recurrence
+        total = sum(t["recurrence_launch_ms"])
+        assert total <= rec[3] + 1e-3
+        assert abs((rec[3] - rec[0]) - sum(t["recurrence_launch_ms"][1:])) < 1e-2
 
 
-@pytest.mark.parametrize("pipeline", [4, 3])
+@pytest.mark.parametrize("pipeline", [2, 4, 3])
 def test_streamed_watchdog_reports_timeout_and_grid_drains(bl, pipeline):
     """Counter waits forced to time out from the host (watchdog_us = -1: every wait expects a
     count no pass reaches and gives up on its first poll): the kernels finish and the plan

@@ -203,6 +203,20 @@ def test_schedule_layer_overlap(bl, batch, steps, pipeline, overlap):
     assert s["pipeline"] == (1 if pipeline >= 2 or (pipeline == 0 and batch >= 8) else 0)
 
 
+@pytest.mark.parametrize("batch,steps,kwargs,fused", [
+    (32, 589, {}, 1), (8, 589, {}, 1), (64, 4096, {}, 1), (32, 589, dict(pipeline=2), 1),
+    (32, 589, dict(pipeline=4), 0), (32, 589, dict(pipeline=3), 0), (32, 589, dict(pipeline=1), 0),
+    (32, 589, dict(pipeline=2, concurrent=1), 0), (32, 589, dict(pipeline=2, concurrent=0), 0),
+    (4, 589, {}, 0), (1, 589, dict(pipeline=2), 1)])
+def test_schedule_one_launch_recurrence(bl, batch, steps, kwargs, fused):
+    """Streamed gates with overlap run the four layers' recurrences as one launch when that
+    launch holds both directions of every tile; pipeline = 4 keeps a launch per layer."""
+    s = bl.schedule(batch, steps, 256, 1, **kwargs)
+    assert s["stream_fused"] == fused
+    assert not fused or (s["pipeline"] == 1 and s["stream_overlap"] == 1 and s["concurrent"] == 2
+                         and s["recur_launches"] == 1)
+
+
 @pytest.mark.parametrize("kwargs,status", [
     (dict(groups=3), "BILSTM_UNSUPPORTED"), (dict(tile=3), "BILSTM_UNSUPPORTED"),
     (dict(concurrent=5), "BILSTM_INVALID_ARGUMENT"), (dict(slices=9), "BILSTM_INVALID_ARGUMENT"),
