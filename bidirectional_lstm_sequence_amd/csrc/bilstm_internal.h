@@ -74,9 +74,9 @@ struct ProjArgs {
     int steps;
     unsigned int *ready;      // [chunks][2][groups] publication counters
     // Inputs written by the previous layer's recurrence while this projection runs
-    // (progress != nullptr): before a tile's rows are read, each of its windows' progress word
-    // in both directions must reach progress_pass | steps the rows need (see StreamLayout);
-    // the rows are then read with agent-scope loads.
+    // (progress != nullptr): before each K half of a tile's rows is read, each of its windows'
+    // progress word in the direction that wrote that half must reach progress_pass | steps the
+    // rows need (see StreamLayout); the rows are then read with agent-scope loads.
     const unsigned long long *progress;  // [batch][2], kProgressStride words apart
     unsigned long long progress_pass;    // (previous layer's pass number) << 32
     unsigned int *error;                 // watchdog flag word
@@ -155,12 +155,15 @@ struct HeadArgs {
 // 4 waves adds 1 to ready[(c·2 + d)·groups + g] once its gates are stored with agent-scope
 // stores and those stores have completed, so a pass adds kReadyPerPass to every counter.
 // A tile of layer l + 1 reads the times of its chunk, all 256 columns, of layer l's output:
-// forward output up to the chunk's last time t_hi (written at forward step t_hi) and reverse
-// output down to its first time t_lo (written at reverse step T-1-t_lo). For chunk c that is
-// min(c·chunk + chunk, T) forward and T - c·chunk reverse steps (direction 0), or the same two
-// counts swapped (direction 1). The tile waits until both directions of each of its windows
-// have run stream_need(c) = max(T - c·chunk, min(c·chunk + chunk, T)) steps of layer l: the
-// middle chunks are ready first, chunk 0 last.
+// forward output (k < 128) up to the chunk's last time t_hi (written at forward step t_hi) and
+// reverse output (k >= 128) down to its first time t_lo (written at reverse step T-1-t_lo).
+// For chunk c of direction d, layer l's direction d must have run stream_near(c) = min(c·chunk
+// + chunk, T) steps and its other direction stream_far(c) = T - c·chunk steps. A tile of
+// direction d sums the K half of direction d first (forward half first for d = 0, reverse
+// half first for d = 1, in every FP32 projection kernel, so the sums are the same bits), so it
+// waits for stream_near(c) of direction d before its first half and stream_far(c) of the other
+// before its second: the first halves are ready early in layer l, and at its end only the
+// second halves of the first chunks are left.
 constexpr int kReadyPerPass = 4 * (kProjThreads / 64);
 // Dynamic LDS a streamed projection workgroup claims on top of its tiles, so that two of them
 // never share a CU (2 · (72 + 16) KB > 160 KB): its persistent grid then spreads one per CU.
@@ -171,10 +174,10 @@ inline int stream_chunks(int steps, int chunk) { return (steps + chunk - 1) / ch
 // Progress words one 128-byte line apart: each window's direction has its own line, so the
 // recurrence's stores and the projection's polls of different windows never share one.
 constexpr int kProgressStride = 16;
-__host__ __device__ inline int stream_need(int steps, int chunk, int c) {
-    const int hi = c * chunk + chunk < steps ? c * chunk + chunk : steps;
-    return steps - c * chunk > hi ? steps - c * chunk : hi;
+__host__ __device__ inline int stream_near(int steps, int chunk, int c) {
+    return c * chunk + chunk < steps ? c * chunk + chunk : steps;
 }
+__host__ __device__ inline int stream_far(int steps, int chunk, int c) { return steps - c * chunk; }
 
 // Launchers (kernels_*.hip). They return the launch's hipError_t.
 hipError_t launch_heads(const HeadArgs &args, hipStream_t stream);

@@ -189,11 +189,11 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
     // (3): measured faster both where the recurrence sets the pace (b32: 1.44 -> 1.39 ms) and
     // where the projection does (b64_t4096: 10.45 -> 10.32 ms).
     info->stream_overlap = pipeline && want_pipe != 3 ? 1 : 0;
-    // With overlap, the four layers' recurrences run as one launch when one launch holds both
-    // directions of every tile (measured: each layer boundary then costs the first chunk's
-    // latency only, not also a kernel launch after the previous layer's end); 4 keeps a launch
-    // per layer.
-    info->stream_fused = info->stream_overlap && concurrent == 2 && launches == 1 && want_pipe != 4 ? 1 : 0;
+    // 4: the four layers' recurrences as one launch, when one launch holds both directions of
+    // every tile. Not the default: a layer boundary waits for the next layer's first chunk
+    // either way, which outlasts a kernel launch, and a launch per layer measured faster
+    // (b32 1.2305 against 1.2390 ms, b8 1.2069 against 1.2091, b64_t4096 10.53 against 10.60).
+    info->stream_fused = info->stream_overlap && concurrent == 2 && launches == 1 && want_pipe == 4 ? 1 : 0;
     info->recur_groups = groups;
     info->recur_tile = tile;
     info->recur_tiles = tiles;

@@ -28,13 +28,15 @@
 //    layout one store instruction writes two full 128-byte row segments.
 //  * Every row's K order is fixed and independent of the row's position and of the grid, so a
 //    row's gates are bitwise the same whatever the batch, the number of workgroups or the
-//    tile order.
+//    tile order. (Layers with 256 inputs: reverse-direction columns sum the reverse half of K
+//    first, kstep_at.)
 //  * Streamed order (projection_stream_kernel): the recurrences run at the same time on
 //    other CUs, this layer's reading the gates step by step and the previous layer's still
 //    writing this layer's input. Tiles then cover `group_windows` windows × `chunk`
 //    consecutive recurrence steps of one direction, walked in the order their inputs appear,
-//    and each waits for its rows, is computed on its own, stored with agent-scope stores and,
-//    once those have completed, published by one counter increment per wave.
+//    and each waits for each K half of its rows before summing it, is computed on its own,
+//    stored with agent-scope stores and, once those have completed, published by one counter
+//    increment per wave.
 #include <algorithm>
 
 #include "bilstm_internal.h"
@@ -62,6 +64,21 @@ constexpr int kGroups = BK / 8;                              // MFMA groups (K =
 static_assert(BM == 128 && BN == 128 && BK == 32 && kProjThreads == 256, "tile shape");
 static_assert(kLoadsPerThread == 4, "loads per thread");
 static_assert(2 * 2 * BM * kStride * sizeof(float) == kProjLdsBytes, "LDS size");
+
+// K step taken at position kt of a tile whose first gate column is n0. A layer after the
+// first reads the previous layer's output, forward h in k < 128 and reverse h in k >= 128;
+// its reverse-direction columns sum the reverse half first. For the rows of a reverse chunk
+// that is the half the previous layer finishes first (its reverse direction reaches late times
+// early), as the forward half is for a forward chunk, so the streamed order can sum the first
+// half before the second exists.
+template <int KSTEPS>
+__device__ __forceinline__ int kstep_at(int n0, int kt) {
+    if constexpr (KSTEPS * BK == kWidth) {
+        return n0 >= kGates ? (kt + KSTEPS / 2) % KSTEPS : kt;
+    } else {
+        return kt;
+    }
+}
 
 template <int KSTEPS>
 __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a) {
@@ -142,7 +159,8 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a)
     int q = first;
     int base = 0;  // LDS buffer of the tile's first K step
     if (q < a.tiles) {
-        load((q / kColTiles) * BM, (q % kColTiles) * BN, 0);
+        const int n0 = (q % kColTiles) * BN;
+        load((q / kColTiles) * BM, n0, kstep_at<KSTEPS>(n0, 0) * BK);
         store(0);
     }
     __syncthreads();
@@ -169,9 +187,10 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a)
             const bool more = kt + 1 < KSTEPS;
             // the next K step of this tile, or the first K step of the next tile
             if (more) {
-                load(m0, n0, (kt + 1) * BK);
+                load(m0, n0, kstep_at<KSTEPS>(n0, kt + 1) * BK);
             } else if (next) {
-                load((qn / kColTiles) * BM, (qn % kColTiles) * BN, 0);
+                const int nn = (qn % kColTiles) * BN;
+                load((qn / kColTiles) * BM, nn, kstep_at<KSTEPS>(nn, 0) * BK);
             }
 #pragma unroll
             for (int g = 0; g < kGroups; ++g) {
@@ -432,29 +451,35 @@ __device__ __forceinline__ int stream_row(const ProjArgs &a, const StreamTile &t
     return w * a.steps + (t.dir == 0 ? s : a.steps - 1 - s);
 }
 
-// Inputs written by the previous layer's recurrence during this kernel: a tile's rows exist
-// once both directions of each of its windows have published enough steps. Lane 2i + d of a
-// wave watches window w0 + i, direction d (the other lanes watch nothing).
+// Inputs written by the previous layer's recurrence during this kernel: a K half of a tile's
+// rows exists once the direction that writes it has published enough steps for each of the
+// tile's windows. Lane 2i + d of a wave watches window w0 + i, direction d (the other lanes
+// watch nothing); the tile's first half is written by direction t.dir (kstep_at).
 __device__ __forceinline__ const unsigned long long *watched_word(const ProjArgs &a, const StreamTile &t, int lane) {
     const int w = t.w0 + (lane >> 1);
     if (a.progress == nullptr || lane >= 2 * a.group_windows || w >= a.batch) return nullptr;
     return a.progress + kProgressStride * (2 * w + (lane & 1));
 }
 
-__device__ __forceinline__ unsigned long long wanted_word(const ProjArgs &a, const StreamTile &t) {
-    return a.progress_pass | static_cast<unsigned int>(stream_need(a.steps, a.chunk, t.c));
+// Whether this lane's word, `seen`, lets the first (second) half of the tile's rows be read.
+__device__ __forceinline__ bool half_ready(const ProjArgs &a, const StreamTile &t, int lane, unsigned long long seen,
+                                          bool first) {
+    if (watched_word(a, t, lane) == nullptr || ((lane & 1) == t.dir) != first) return true;
+    const int need = first ? stream_near(a.steps, a.chunk, t.c) : stream_far(a.steps, a.chunk, t.c);
+    return seen >= (a.progress_pass | static_cast<unsigned int>(need));
 }
 
-// Wait until the tile's rows exist; the wave goes on when all its lanes have seen them.
-__device__ __forceinline__ void wait_rows(const ProjArgs &a, const StreamTile &t, int lane, bool &timed_out) {
+// Wait until the first (second) half of the tile's rows exists; the wave goes on when all its
+// lanes have seen it.
+__device__ __forceinline__ void wait_half(const ProjArgs &a, const StreamTile &t, int lane, bool first,
+                                          bool &timed_out) {
     const unsigned long long *p = watched_word(a, t, lane);
-    if (p == nullptr || timed_out) return;
-    const unsigned long long want = wanted_word(a, t);
-    if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) return;
+    if (p == nullptr || timed_out || ((lane & 1) == t.dir) != first) return;
+    if (half_ready(a, t, lane, __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), first)) return;
     const unsigned long long t0 = wall_clock64();
     while (true) {
         __builtin_amdgcn_s_sleep(2);
-        if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) break;
+        if (half_ready(a, t, lane, __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), first)) break;
         if (wall_clock64() - t0 > a.timeout_ticks) {
             atomicOr(a.error, 4u);
             timed_out = true;
@@ -536,9 +561,11 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
         __hip_atomic_fetch_add(a.ready + t.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
     bool timed_out = false;
-    // The next tile's first K step is loaded during the current tile's last one when its rows
-    // already exist (known from a progress read issued at the current tile's start); else the
-    // wave waits for them after the current tile is published.
+    // The next tile's first K step is loaded during the current tile's last one when its first
+    // half already exists (known from a progress read issued at the current tile's start); else
+    // the wave waits for it after the current tile is published. Likewise the current tile's
+    // second half is loaded during its first half's last K step when it exists, else after
+    // that step's products, once it does.
     bool staged = false;  // this wave already staged the tile's first K step in LDS buffer 0
     for (int q = first; q < a.tiles; q += nwg) {
         const StreamTile t = stream_tile(a, q);
@@ -547,16 +574,20 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
 #pragma unroll
         for (int j = 0; j < 2; ++j) sbias[j] = a.bias[n0 + wn * 64 + j * 32 + (lane & 31)];
         if (!staged) {
-            wait_rows(a, t, lane, timed_out);
+            wait_half(a, t, lane, true, timed_out);
             rows_of(t);
-            load(n0, 0);
+            load(n0, kstep_at<KSTEPS>(n0, 0) * BK);
             store(0);
         }
         __syncthreads();
         v4f af[2][2], bf[2][2];
         frags(0, 0, af[0], bf[0]);
 
-        // progress of the next tile's windows, read now and checked in the last K step
+        // progress of this tile's and of the next tile's windows, read now and checked at the
+        // end of this tile's first half and in its last K step
+        const unsigned long long *pc = watched_word(a, t, lane);
+        const unsigned long long seen_cur =
+            pc != nullptr ? __hip_atomic_load(pc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : ~0ull;
         const int qn = q + nwg;
         const bool next = qn < a.tiles;
         const StreamTile tn = stream_tile(a, next ? qn : q);
@@ -577,11 +608,17 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
         for (int kt = 0; kt < KSTEPS; ++kt) {
             const int cur = kt & 1;
             const bool more = kt + 1 < KSTEPS;
+            // K step kt + 1 starts the tile's second half, which may not exist yet
+            bool late = false;
             if (more) {
-                load(n0, (kt + 1) * BK);
-            } else if (next && __all(seen_next >= wanted_word(a, tn))) {
+                if (KSTEPS * BK == kWidth && kt + 1 == KSTEPS / 2 && !__all(half_ready(a, t, lane, seen_cur, false))) {
+                    late = true;
+                } else {
+                    load(n0, kstep_at<KSTEPS>(n0, kt + 1) * BK);
+                }
+            } else if (next && __all(half_ready(a, tn, lane, seen_next, true))) {
                 rows_of(tn);
-                load(tn.n0, 0);
+                load(tn.n0, kstep_at<KSTEPS>(tn.n0, 0) * BK);
                 staged = true;
             }
 #pragma unroll
@@ -596,6 +633,10 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
                         for (int j = 0; j < 2; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[p][i][e], bf[p][j][e],
                                                                              acc[i][j], 0, 0, 0);
+            }
+            if (late) {
+                wait_half(a, t, lane, false, timed_out);
+                load(n0, kstep_at<KSTEPS>(n0, kt + 1) * BK);
             }
             // the last K step reads buffer 1, so the next tile's first K step goes to buffer 0
             if (more || staged) store(cur ^ 1);

@@ -124,9 +124,9 @@ typedef struct {
                              2 = on (BILSTM_UNSUPPORTED unless recur_groups = 1, projection = 0,
                              slices <= 1 and at least 8 CUs stay free), with the next layer's
                              projection starting during this layer's recurrence; 3 = on, with it
-                             starting after this layer's recurrence; 4 = as 2, with one
-                             recurrence launch per layer where 2 runs the four layers'
-                             recurrences as one launch (bilstm_plan_info.stream_fused).
+                             starting after this layer's recurrence; 4 = as 2, with the four
+                             layers' recurrences as one launch where possible
+                             (bilstm_plan_info.stream_fused), not a launch per layer.
                              Every wait on a counter is bounded by the watchdog like every other
                              wait: if the GPU is shared with other work that keeps a kernel from
                              running, bilstm_check reports BILSTM_TIMEOUT instead of hanging */
@@ -157,9 +157,8 @@ typedef struct {
     int32_t stream_overlap;  /* streamed gates: 1 when the next layer's projection starts during
                                 this layer's recurrence, 0 when after it */
     int32_t stream_fused;    /* streamed gates: 1 when the four layers' recurrences run as one
-                                launch (overlap on, concurrent = 2, recur_launches = 1, pipeline
-                                != 4); each workgroup then moves from a layer to the next by
-                                itself */
+                                launch (pipeline = 4, concurrent = 2, recur_launches = 1); each
+                                workgroup then moves from a layer to the next by itself */
 } bilstm_plan_info;
 
 /*

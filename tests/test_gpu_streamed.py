@@ -64,8 +64,8 @@ SHAPES = [(1, 589, 0), (1, 1, 0), (2, 130, 0), (3, 150, 0), (3, 3, 0), (5, 7, 0)
 @pytest.mark.parametrize("batch,steps,tile", SHAPES)
 def test_streamed_equals_unstreamed_bitwise(bl, batch, steps, tile, pipeline):
     """pipeline 2: the next layer's projection runs during this layer's recurrence, reading the
-    rows it publishes, and the four recurrences run as one launch; 4: the same with a launch
-    per layer; 3: each projection after the previous layer's recurrence."""
+    rows it publishes; 4: the same with the four recurrences as one launch; 3: each projection
+    after the previous layer's recurrence."""
     x = workloads.make_input(40 + batch, batch, steps)
     layers = workloads.make_layers(41)
     note(f"streamed (pipeline={pipeline}) vs unstreamed batch={batch} steps={steps} tile={tile}")
@@ -74,7 +74,7 @@ def test_streamed_equals_unstreamed_bitwise(bl, batch, steps, tile, pipeline):
     assert info["pipeline"] == 1 and binfo["pipeline"] == 0
     assert info["stream_overlap"] == (0 if pipeline == 3 else 1)
     one_launch = info["concurrent"] == 2 and info["recur_launches"] == 1
-    assert info["stream_fused"] == (1 if pipeline == 2 and one_launch else 0)
+    assert info["stream_fused"] == (1 if pipeline == 4 and one_launch else 0)
     assert np.array_equal(got[0].view(np.uint32), base[0].view(np.uint32))
 
 
@@ -114,7 +114,7 @@ def test_streamed_phase_times(bl, pipeline):
     plan.check()
     fused = plan.info()["stream_fused"]
     plan.close()
-    assert fused == (1 if pipeline == 2 else 0)
+    assert fused == (1 if pipeline == 4 else 0)
     # timing changes nothing in the results
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
     rec = t["recurrence_ms"]

@@ -204,13 +204,13 @@ def test_schedule_layer_overlap(bl, batch, steps, pipeline, overlap):
 
 
 @pytest.mark.parametrize("batch,steps,kwargs,fused", [
-    (32, 589, {}, 1), (8, 589, {}, 1), (64, 4096, {}, 1), (32, 589, dict(pipeline=2), 1),
-    (32, 589, dict(pipeline=4), 0), (32, 589, dict(pipeline=3), 0), (32, 589, dict(pipeline=1), 0),
-    (32, 589, dict(pipeline=2, concurrent=1), 0), (32, 589, dict(pipeline=2, concurrent=0), 0),
-    (4, 589, {}, 0), (1, 589, dict(pipeline=2), 1)])
+    (32, 589, {}, 0), (8, 589, {}, 0), (64, 4096, {}, 0), (32, 589, dict(pipeline=2), 0),
+    (32, 589, dict(pipeline=4), 1), (64, 4096, dict(pipeline=4), 1), (32, 589, dict(pipeline=3), 0),
+    (32, 589, dict(pipeline=1), 0), (32, 589, dict(pipeline=4, concurrent=1), 0),
+    (32, 589, dict(pipeline=4, concurrent=0), 0), (4, 589, {}, 0), (1, 589, dict(pipeline=4), 1)])
 def test_schedule_one_launch_recurrence(bl, batch, steps, kwargs, fused):
-    """Streamed gates with overlap run the four layers' recurrences as one launch when that
-    launch holds both directions of every tile; pipeline = 4 keeps a launch per layer."""
+    """pipeline = 4 runs the four layers' recurrences as one launch when that launch holds both
+    directions of every tile; otherwise streamed gates launch each layer's recurrence."""
     s = bl.schedule(batch, steps, 256, 1, **kwargs)
     assert s["stream_fused"] == fused
     assert not fused or (s["pipeline"] == 1 and s["stream_overlap"] == 1 and s["concurrent"] == 2
