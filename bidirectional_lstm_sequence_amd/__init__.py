@@ -80,7 +80,8 @@ class PlanInfo(ctypes.Structure):
                 ("device_bytes", ctypes.c_uint64), ("slices", ctypes.c_int32),
                 ("slice_windows", ctypes.c_int32), ("projection", ctypes.c_int32),
                 ("pipeline", ctypes.c_int32), ("stream_chunk", ctypes.c_int32),
-                ("stream_overlap", ctypes.c_int32), ("stream_fused", ctypes.c_int32)]
+                ("stream_overlap", ctypes.c_int32), ("stream_split", ctypes.c_int32),
+                ("stream_fused", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}

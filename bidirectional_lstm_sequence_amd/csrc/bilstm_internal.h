@@ -70,6 +70,7 @@ struct ProjArgs {
     int chunk_shift;     // log2(chunk)
     int group_windows;   // windows per tile row block
     int groups;          // ceil(batch / group_windows)
+    int split;           // tiles of chunk 0 per 128 gate columns (stream_split)
     int batch;
     int steps;
     unsigned int *ready;      // [chunks][2][groups] publication counters
@@ -150,10 +151,13 @@ struct HeadArgs {
 // block holds `group_windows` windows × `chunk` steps (128 rows): row r is window
 // g·group_windows + r / chunk at step s = c·chunk + r % chunk of direction d, i.e. time s
 // (forward) or steps - 1 - s (reverse); rows past the batch or past the last step are
-// skipped. Tile q = ((c·2 + d)·groups + g)·4 + column tile, columns d·512 + 128·(column
-// tile): the walk goes chunk by chunk, the order the recurrence reads them. Each of a tile's
-// 4 waves adds 1 to ready[(c·2 + d)·groups + g] once its gates are stored with agent-scope
-// stores and those stores have completed, so a pass adds kReadyPerPass to every counter.
+// skipped. The walk goes chunk by chunk, the order the recurrence reads them. Chunk 0 comes
+// first, in tiles of 128 / split columns: tile q = (d·groups + g)·4·split + column tile,
+// columns d·512 + (128 / split)·(column tile). Then chunks c >= 1 in tiles of 128 columns:
+// tile 2·groups·4·split + ((c·2 + d - 2)·groups + g)·4 + column tile. Narrow first tiles
+// spread the chunk a layer boundary waits for over more workgroups. A tile of width W adds
+// W / 32 to ready[(c·2 + d)·groups + g] once all its gates are stored with agent-scope stores
+// and those stores have completed, so a pass adds kReadyPerPass to every counter.
 // A tile of layer l + 1 reads the times of its chunk, all 256 columns, of layer l's output:
 // forward output (k < 128) up to the chunk's last time t_hi (written at forward step t_hi) and
 // reverse output (k >= 128) down to its first time t_lo (written at reverse step T-1-t_lo).
@@ -164,7 +168,24 @@ struct HeadArgs {
 // waits for stream_near(c) of direction d before its first half and stream_far(c) of the other
 // before its second: the first halves are ready early in layer l, and at its end only the
 // second halves of the first chunks are left.
-constexpr int kReadyPerPass = 4 * (kProjThreads / 64);
+constexpr int kReadyPerPass = kGates / 32;
+// Tiles of chunk 0 per 128 gate columns: as many as keep every one of them in the first round
+// of `workgroups` persistent projection workgroups (1, 2 or 4).
+inline int stream_split(int groups, int workgroups) {
+    int split = 4;
+    while (split > 1 && 2 * groups * (kGates / kProjTileN) * split > workgroups) split /= 2;
+    return split;
+}
+// Persistent workgroups of a streamed projection: the CUs the recurrence's workgroups (one
+// per CU) leave free, a multiple of 8, at least 8.
+inline int stream_projection_workgroups(int cu_count, int recur_tiles, int recur_groups) {
+    const int free_cus = (cu_count - 2 * recur_tiles * recur_groups) / 8 * 8;
+    return free_cus > 8 ? free_cus : 8;
+}
+// Tiles of a streamed projection pass.
+inline int stream_tiles(int chunks, int groups, int split) {
+    return (chunks - 1 + split) * 2 * groups * (kGates / kProjTileN);
+}
 // Dynamic LDS a streamed projection workgroup claims on top of its tiles, so that two of them
 // never share a CU (2 · (72 + 16) KB > 160 KB): its persistent grid then spreads one per CU.
 constexpr size_t kProjStreamLds = 16 * 1024;

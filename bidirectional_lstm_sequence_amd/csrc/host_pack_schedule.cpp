@@ -185,6 +185,10 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
     info->projection = projection;
     info->pipeline = pipeline ? 1 : 0;
     info->stream_chunk = pipeline ? kProjTileM / group_windows : 0;
+    info->stream_split =
+        pipeline ? stream_split(static_cast<int>((batch + group_windows - 1) / group_windows),
+                                stream_projection_workgroups(cu_count, static_cast<int>(tiles), groups))
+                 : 0;
     // The next layer's projection starts during this layer's recurrence unless asked not to
     // (3): measured faster both where the recurrence sets the pace (b32: 1.44 -> 1.39 ms) and
     // where the projection does (b64_t4096: 10.45 -> 10.32 ms).

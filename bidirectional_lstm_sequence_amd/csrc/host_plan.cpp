@@ -271,7 +271,8 @@ bilstm_status enqueue_projection(bilstm_plan *p, int layer, const float *x, floa
         args.batch = static_cast<int>(p->batch);
         args.steps = static_cast<int>(p->steps);
         args.ready = reinterpret_cast<unsigned int *>(p->ready + buffer * p->ready_words);
-        args.tiles = p->stream_chunks * 2 * args.groups * (kGates / kProjTileN);
+        args.split = p->info.stream_split;
+        args.tiles = stream_tiles(p->stream_chunks, args.groups, args.split);
         args.error = p->error;
         args.timeout_ticks = p->timeout_ticks;
         if (layer > 0 && p->info.stream_overlap) {
@@ -672,8 +673,7 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
             e = recurrence_allow_lds(info.recur_groups, info.recur_tile, p->reserve_lds);
         }
         if (e == hipSuccess) e = projection_allow_lds(kProjStreamLds);
-        p->proj_workgroups_streamed =
-            std::max(8, (cu_count - 2 * info.recur_tiles * info.recur_groups) / 8 * 8);
+        p->proj_workgroups_streamed = stream_projection_workgroups(cu_count, info.recur_tiles, info.recur_groups);
     }
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {

@@ -422,23 +422,39 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_split_kernel(ProjA
 // its K loop ends, so no finished tile waits behind the inputs of the next one. Every row sums
 // its K terms in the same order as projection_kernel, so the gates are bitwise the same.
 
-// Row block of streamed tile q: first window, first step, chunk, direction, first gate column
-// and publication counter.
+// Row block of streamed tile q: first window, first step, chunk, direction, first gate
+// column, width in gate columns and publication counter.
 struct StreamTile {
-    int w0, s0, c, dir, n0, counter;
+    int w0, s0, c, dir, n0, width, counter;
 };
 
+// The tiles of chunk 0 come first, `split` of them per 128 gate columns: narrower tiles spread
+// the first chunk after a layer boundary over more workgroups. The other chunks follow in
+// 128-column tiles.
 __device__ __forceinline__ StreamTile stream_tile(const ProjArgs &a, int q) {
-    const int ct = q & 3;
-    const int rest = q >> 2;
+    const int first_tiles = 2 * a.groups * (kGates / BN) * a.split;
+    int ct, rest, id, width;
+    if (q < first_tiles) {
+        const int per = (kGates / BN) * a.split;
+        ct = q % per;
+        rest = q / per;
+        width = BN / a.split;
+        id = rest / a.groups;  // direction
+    } else {
+        const int r = q - first_tiles;
+        ct = r & 3;
+        rest = r >> 2;
+        width = BN;
+        id = rest / a.groups + 2;  // chunk · 2 + direction
+    }
     const int g = rest % a.groups;
-    const int id = rest / a.groups;  // chunk · 2 + direction
     StreamTile t;
     t.dir = id & 1;
     t.c = id >> 1;
     t.w0 = g * a.group_windows;
     t.s0 = t.c * a.chunk;
-    t.n0 = t.dir * kGates + ct * BN;
+    t.n0 = t.dir * kGates + ct * width;
+    t.width = width;
     t.counter = (t.c * 2 + t.dir) * a.groups + g;
     return t;
 }
@@ -488,6 +504,11 @@ __device__ __forceinline__ void wait_half(const ProjArgs &a, const StreamTile &t
     }
 }
 
+template <int TN>
+struct TileWidth {
+    static constexpr int value = TN;
+};
+
 template <int KSTEPS>
 __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(ProjArgs a) {
     __shared__ __attribute__((aligned(16))) float lds_a[2][BM * kStride];
@@ -501,8 +522,6 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
     // Inputs written while this kernel runs are read with agent-scope (sc1) buffer loads; the
     // buffer's range is the whole input, so a load outside it would return zeros.
     const bool coherent = a.progress != nullptr;
@@ -510,9 +529,10 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
         const_cast<float *>(a.x), 0, static_cast<int>(static_cast<unsigned int>(a.steps) * a.batch * a.in * 4),
         kBufferRsrcWord3);
 
+    // staging of one K step: the tile's 128 rows of x and its `width` rows of W
     v4f ra[kLoadsPerThread], rb[kLoadsPerThread];
     int srow[kLoadsPerThread];  // gate rows of this thread's staging rows tid / 8 + 32 j
-    auto load = [&](int n0, int k0) {
+    auto load = [&](int n0, int k0, int width) {
 #pragma unroll
         for (int j = 0; j < kLoadsPerThread; ++j) {
             const int f = tid + kProjThreads * j;
@@ -528,7 +548,9 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
                 }
             }
             ra[j] = va;
-            rb[j] = *reinterpret_cast<const v4f *>(a.w + static_cast<size_t>(n0 + row) * a.kpad + k);
+            v4f vb = {0.f, 0.f, 0.f, 0.f};
+            if (row < width) vb = *reinterpret_cast<const v4f *>(a.w + static_cast<size_t>(n0 + row) * a.kpad + k);
+            rb[j] = vb;
         }
     };
     auto store = [&](int buf) {
@@ -542,45 +564,56 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
     };
     const int frag_row = lane & 31;
     const int frag_k = (lane >> 5) * 4;
-    auto frags = [&](int buf, int g, v4f (&af)[2], v4f (&bf)[2]) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            af[t] = *reinterpret_cast<const v4f *>(
-                &lds_a[buf][(wm * 64 + t * 32 + frag_row) * kStride + g * 8 + frag_k]);
-            bf[t] = *reinterpret_cast<const v4f *>(
-                &lds_b[buf][(wn * 64 + t * 32 + frag_row) * kStride + g * 8 + frag_k]);
-        }
-    };
 
     auto rows_of = [&](const StreamTile &t) {
 #pragma unroll
         for (int j = 0; j < kLoadsPerThread; ++j) srow[j] = stream_row(a, t, (tid + kProjThreads * j) / kThreadsPerRow);
     };
 
-    auto publish = [&](const StreamTile &t) {
-        __hip_atomic_fetch_add(a.ready + t.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
     bool timed_out = false;
     // The next tile's first K step is loaded during the current tile's last one when its first
     // half already exists (known from a progress read issued at the current tile's start); else
     // the wave waits for it after the current tile is published. Likewise the current tile's
     // second half is loaded during its first half's last K step when it exists, else after
     // that step's products, once it does.
-    bool staged = false;  // this wave already staged the tile's first K step in LDS buffer 0
-    for (int q = first; q < a.tiles; q += nwg) {
-        const StreamTile t = stream_tile(a, q);
+    bool staged = false;  // the tile's first K step is already in LDS buffer 0
+
+    // One tile TN gate columns wide. The four waves split it WM x WN, each a grid of NI x NJ
+    // blocks of 32 x 32 (128 columns: 2 x 2 waves of 64 x 64; 64: 2 x 2 of 64 x 32; 32: 4 x 1
+    // of 32 x 32). Every block runs the same MFMA sequence over K whatever the width, so a
+    // gate's sum does not depend on the tile it falls in.
+    auto run = [&](const StreamTile &t, int q, auto width_tag) {
+        constexpr int TN = decltype(width_tag)::value;
+        constexpr int WN = TN >= 64 ? 2 : 1;
+        constexpr int WM = 4 / WN;
+        constexpr int NI = BM / WM / 32;
+        constexpr int NJ = TN / WN / 32;
+        const int row0 = (wave / WN) * (BM / WM);
+        const int col0 = (wave % WN) * (TN / WN);
         const int n0 = t.n0;
-        float sbias[2];
+
+        auto frags = [&](int buf, int g, v4f (&af)[NI], v4f (&bf)[NJ]) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) sbias[j] = a.bias[n0 + wn * 64 + j * 32 + (lane & 31)];
+            for (int i = 0; i < NI; ++i) {
+                af[i] = *reinterpret_cast<const v4f *>(&lds_a[buf][(row0 + i * 32 + frag_row) * kStride + g * 8 + frag_k]);
+            }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                bf[j] = *reinterpret_cast<const v4f *>(&lds_b[buf][(col0 + j * 32 + frag_row) * kStride + g * 8 + frag_k]);
+            }
+        };
+
+        float sbias[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) sbias[j] = a.bias[n0 + col0 + j * 32 + (lane & 31)];
         if (!staged) {
             wait_half(a, t, lane, true, timed_out);
             rows_of(t);
-            load(n0, kstep_at<KSTEPS>(n0, 0) * BK);
+            load(n0, kstep_at<KSTEPS>(n0, 0) * BK, TN);
             store(0);
         }
         __syncthreads();
-        v4f af[2][2], bf[2][2];
+        v4f af[2][NI], bf[2][NJ];
         frags(0, 0, af[0], bf[0]);
 
         // progress of this tile's and of the next tile's windows, read now and checked at the
@@ -595,11 +628,11 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
         const unsigned long long seen_next =
             pn != nullptr ? __hip_atomic_load(pn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : ~0ull;
 
-        v16f acc[2][2];
+        v16f acc[NI][NJ];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -614,11 +647,11 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
                 if (KSTEPS * BK == kWidth && kt + 1 == KSTEPS / 2 && !__all(half_ready(a, t, lane, seen_cur, false))) {
                     late = true;
                 } else {
-                    load(n0, kstep_at<KSTEPS>(n0, kt + 1) * BK);
+                    load(n0, kstep_at<KSTEPS>(n0, kt + 1) * BK, TN);
                 }
             } else if (next && __all(half_ready(a, tn, lane, seen_next, true))) {
                 rows_of(tn);
-                load(tn.n0, kstep_at<KSTEPS>(tn.n0, 0) * BK);
+                load(tn.n0, kstep_at<KSTEPS>(tn.n0, 0) * BK, tn.width);
                 staged = true;
             }
 #pragma unroll
@@ -628,15 +661,15 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
 #pragma unroll
-                    for (int i = 0; i < 2; ++i)
+                    for (int i = 0; i < NI; ++i)
 #pragma unroll
-                        for (int j = 0; j < 2; ++j)
+                        for (int j = 0; j < NJ; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[p][i][e], bf[p][j][e],
                                                                              acc[i][j], 0, 0, 0);
             }
             if (late) {
                 wait_half(a, t, lane, false, timed_out);
-                load(n0, kstep_at<KSTEPS>(n0, kt + 1) * BK);
+                load(n0, kstep_at<KSTEPS>(n0, kt + 1) * BK, TN);
             }
             // the last K step reads buffer 1, so the next tile's first K step goes to buffer 0
             if (more || staged) store(cur ^ 1);
@@ -644,12 +677,11 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
             if (more) frags(cur ^ 1, 0, af[0], bf[0]);
         }
 
-        // store with agent-scope stores, wait for them to complete, then publish (one counter
-        // increment per wave)
-        float *const gcol = a.gates + n0 + wn * 64 + (lane & 31);
+        // store with agent-scope stores; once every wave's stores have completed, publish
+        float *const gcol = a.gates + n0 + col0 + (lane & 31);
         auto put_row = [&](int i, int r, int m) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 __hip_atomic_store(gcol + static_cast<size_t>(m) * kGateCols + j * 32, acc[i][j][r] + sbias[j],
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
@@ -657,24 +689,40 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
         if (t.w0 + a.group_windows <= a.batch && t.s0 + a.chunk <= a.steps) {
             // every row of the tile exists (all but the ragged last chunk and group)
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < NI; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int lr = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                    const int lr = row0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                     const int sr = t.s0 + (lr & (a.chunk - 1));
                     put_row(i, r, (t.w0 + (lr >> a.chunk_shift)) * a.steps + (t.dir == 0 ? sr : a.steps - 1 - sr));
                 }
         } else {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < NI; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int m = stream_row(a, t, wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3));
+                    const int m = stream_row(a, t, row0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3));
                     if (m >= 0) put_row(i, r, m);
                 }
         }
         __builtin_amdgcn_s_waitcnt(0);
-        if (lane == 0) publish(t);
+        __syncthreads();
+        // the tiles of a counter's chunk add kReadyPerPass per pass in all: TN / 32 each
+        if (tid == 0) {
+            __hip_atomic_fetch_add(a.ready + t.counter, static_cast<unsigned int>(TN / 32), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+
+    for (int q = first; q < a.tiles; q += nwg) {
+        const StreamTile t = stream_tile(a, q);
+        if (t.width == BN) {
+            run(t, q, TileWidth<BN>{});
+        } else if (t.width == BN / 2) {
+            run(t, q, TileWidth<BN / 2>{});
+        } else {
+            run(t, q, TileWidth<BN / 4>{});
+        }
     }
 }
 

@@ -156,6 +156,9 @@ typedef struct {
                                 windows per projection row block); 0 when not streamed */
     int32_t stream_overlap;  /* streamed gates: 1 when the next layer's projection starts during
                                 this layer's recurrence, 0 when after it */
+    int32_t stream_split;    /* streamed gates: tiles per 128 gate columns of each layer's first
+                                chunk (1, 2 or 4), the chunk a layer boundary waits for: narrower
+                                tiles spread it over more workgroups; 0 when not streamed */
     int32_t stream_fused;    /* streamed gates: 1 when the four layers' recurrences run as one
                                 launch (pipeline = 4, concurrent = 2, recur_launches = 1); each
                                 workgroup then moves from a layer to the next by itself */

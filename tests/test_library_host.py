@@ -217,6 +217,21 @@ def test_schedule_one_launch_recurrence(bl, batch, steps, kwargs, fused):
                          and s["recur_launches"] == 1)
 
 
+@pytest.mark.parametrize("batch,steps,cus,split", [
+    (32, 589, 256, 2), (8, 589, 256, 4), (64, 4096, 256, 1), (1, 589, 256, 4), (16, 589, 256, 4),
+    (32, 589, 128, 1), (96, 589, 256, 1), (4, 589, 256, 0)])
+def test_schedule_first_chunk_split(bl, batch, steps, cus, split):
+    """The first chunk's tiles are as narrow (128 / split columns) as keeps all of them in the
+    first round of the streamed projection's workgroups (the CUs the recurrence leaves)."""
+    s = bl.schedule(batch, steps, cus, 1, pipeline=2 if split else 0)
+    assert s["stream_split"] == split
+    if split:
+        groups = -(-batch // (128 // s["stream_chunk"]))
+        free = max(8, (cus - 2 * s["recur_tiles"] * s["recur_groups"]) // 8 * 8)
+        assert 2 * groups * 4 * split <= free or split == 1
+        assert split == 4 or 2 * groups * 4 * split * 2 > free
+
+
 @pytest.mark.parametrize("kwargs,status", [
     (dict(groups=3), "BILSTM_UNSUPPORTED"), (dict(tile=3), "BILSTM_UNSUPPORTED"),
     (dict(concurrent=5), "BILSTM_INVALID_ARGUMENT"), (dict(slices=9), "BILSTM_INVALID_ARGUMENT"),
