@@ -189,8 +189,6 @@ inline int stream_tiles(int chunks, int groups, int split) {
 // Dynamic LDS a streamed projection workgroup claims on top of its tiles, so that two of them
 // never share a CU (2 · (72 + 16) KB > 160 KB): its persistent grid then spreads one per CU.
 constexpr size_t kProjStreamLds = 16 * 1024;
-// Streamed gates are chosen automatically from this many windows on.
-constexpr int kStreamMinBatch = 8;
 inline int stream_chunks(int steps, int chunk) { return (steps + chunk - 1) / chunk; }
 // Progress words one 128-byte line apart: each window's direction has its own line, so the
 // recurrence's stores and the projection's polls of different windows never share one.

@@ -140,12 +140,10 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
         }
         pipeline = true;
     } else if (want_pipe == 0) {
-        // auto: when the recurrence leaves at least a quarter of the CUs to the projection and
-        // the batch has at least 8 windows (measured on MI355X: 8 windows 1.303 -> 1.277 ms
-        // streamed, one window 1.230 -> 1.245 ms: there the whole projection of a layer takes
-        // about as long as its first published chunk).
-        pipeline = pipe_possible && concurrent == 2 && 4 * rec_wgs <= 3LL * cu_count &&
-                   batch >= static_cast<uint32_t>(kStreamMinBatch);
+        // auto: when the recurrence leaves at least a quarter of the CUs to the projection
+        // (measured on MI355X, 589 steps, unstreamed against streamed: 1 window 1.187 -> 1.168
+        // ms, 2 windows 1.228 -> 1.174, 4 windows 1.240 -> 1.179, 32 windows 1.405 -> 1.202).
+        pipeline = pipe_possible && concurrent == 2 && 4 * rec_wgs <= 3LL * cu_count;
     }
     // windows per projection row block: up to 4, a multiple of the recurrence tile, so a
     // recurrence tile never spans two row blocks; chunk = 128 / that many steps

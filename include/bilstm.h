@@ -118,7 +118,7 @@ typedef struct {
                              between y and a plan-owned buffer, so no kernel overwrites data a
                              running one still reads. The output is bitwise the same as without
                              it.
-                             0 = auto (on from 8 windows when recur_groups = 1, the
+                             0 = auto (on when recur_groups = 1, concurrent = 2, the
                              recurrence's grid leaves at least a quarter of the CUs free and
                              projection = 0), 1 = off,
                              2 = on (BILSTM_UNSUPPORTED unless recur_groups = 1, projection = 0,

@@ -158,13 +158,14 @@ def test_schedule_library_projection_runs_unsliced(bl):
     assert e.value.name == "BILSTM_UNSUPPORTED"
 
 
-@pytest.mark.parametrize("batch,steps,on,chunk", [(1, 589, 0, 0), (7, 589, 0, 0), (8, 589, 1, 32), (16, 589, 1, 32),
+@pytest.mark.parametrize("batch,steps,on,chunk", [(1, 589, 1, 128), (2, 589, 1, 64), (3, 589, 1, 32),
+                                                   (7, 589, 1, 32), (8, 589, 1, 32), (16, 589, 1, 32),
                                                    (32, 589, 1, 32), (64, 4096, 1, 32),
                                                    (96, 589, 1, 32), (97, 589, 0, 0), (256, 589, 0, 0)])
 def test_schedule_streams_gates_when_the_recurrence_leaves_cus(bl, batch, steps, on, chunk):
-    """Auto: streamed gates from 8 windows on, when the recurrence's grid (one workgroup per
-    window and direction) leaves at least a quarter of the 256 CUs to the projection; they
-    replace the batch slices."""
+    """Auto: streamed gates when the recurrence's grid (one workgroup per window and
+    direction) leaves at least a quarter of the 256 CUs to the projection; they replace the
+    batch slices."""
     s = bl.schedule(batch, steps, 256, 1)
     assert s["pipeline"] == on and s["stream_chunk"] == chunk
     if on:
@@ -194,13 +195,13 @@ def test_schedule_forced_streaming_checks_its_conditions(bl):
 
 @pytest.mark.parametrize("batch,steps,pipeline,overlap", [
     (32, 589, 0, 1), (16, 589, 0, 1), (64, 4096, 0, 1), (96, 589, 0, 1), (32, 589, 3, 0), (64, 4096, 4, 1),
-    (8, 589, 2, 1), (1, 589, 2, 1), (32, 589, 1, 0), (8, 589, 0, 1), (4, 589, 0, 0)])
+    (8, 589, 2, 1), (1, 589, 2, 1), (32, 589, 1, 0), (8, 589, 0, 1), (4, 589, 0, 1), (1, 589, 0, 1)])
 def test_schedule_layer_overlap(bl, batch, steps, pipeline, overlap):
     """Streamed gates overlap the next layer's projection with this layer's recurrence unless
     pipeline = 3 asks for each projection after the previous recurrence."""
     s = bl.schedule(batch, steps, 256, 1, pipeline=pipeline)
     assert s["stream_overlap"] == overlap
-    assert s["pipeline"] == (1 if pipeline >= 2 or (pipeline == 0 and batch >= 8) else 0)
+    assert s["pipeline"] == (1 if pipeline != 1 else 0)
 
 
 @pytest.mark.parametrize("batch,steps,kwargs,fused", [
@@ -219,7 +220,7 @@ def test_schedule_one_launch_recurrence(bl, batch, steps, kwargs, fused):
 
 @pytest.mark.parametrize("batch,steps,cus,split", [
     (32, 589, 256, 2), (8, 589, 256, 4), (64, 4096, 256, 1), (1, 589, 256, 4), (16, 589, 256, 4),
-    (32, 589, 128, 1), (96, 589, 256, 1), (4, 589, 256, 0)])
+    (32, 589, 128, 1), (96, 589, 256, 1), (4, 589, 256, 4), (256, 589, 256, 0)])
 def test_schedule_first_chunk_split(bl, batch, steps, cus, split):
     """The first chunk's tiles are as narrow (128 / split columns) as keeps all of them in the
     first round of the streamed projection's workgroups (the CUs the recurrence leaves)."""
