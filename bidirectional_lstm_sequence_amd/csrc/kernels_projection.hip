@@ -36,7 +36,9 @@
 //    consecutive recurrence steps of one direction, walked in the order their inputs appear,
 //    and each waits for each K half of its rows before summing it, is computed on its own,
 //    stored with agent-scope stores and, once those have completed, published by one counter
-//    increment per wave.
+//    increment. Its K steps go from memory straight into a 4-stage LDS ring (buffer loads with
+//    the LDS bit, rows swizzled instead of padded), three steps ahead of the products, with
+//    explicit counter waits and bare barriers.
 #include <algorithm>
 
 #include "bilstm_internal.h"
@@ -509,11 +511,44 @@ struct TileWidth {
     static constexpr int value = TN;
 };
 
+// LDS staging of the streamed kernel. A K step of a tile is 128 rows of x and 128 rows of W,
+// 32 floats each, written from memory straight into LDS by buffer loads with the LDS bit, so
+// no registers hold them on the way and four K steps can be in flight. Row r's eight 16-byte
+// chunks are stored swizzled, chunk c in slot c ^ ((r >> 1) & 7): the 32 rows one fragment
+// read touches then fall on distinct banks without padding. One wave instruction fills 8 rows
+// (64 lanes x 16 bytes, lane i in slot i % 8 of row 8n + i / 8), so lane i fetches chunk
+// (i % 8) ^ ((row >> 1) & 7) of its row. An out-of-range offset loads zeros (rows past the
+// batch or the steps, k past the input width, W rows past the last gate).
+constexpr int kStages = 4;                        // K steps in the LDS ring
+constexpr int kStageFloats = 2 * BM * BK;         // x rows, then W rows
+constexpr unsigned int kOutOfRange = 0x80000000u;  // a buffer offset past every buffer here
+
+__device__ __forceinline__ int swizzled(int r, int c) { return r * BK + ((c ^ ((r >> 1) & 7)) << 2); }
+
+// Wait until at most 8·n of this wave's vector memory operations are outstanding (n = K steps
+// issued after the one waited for, each 8 loads per wave, and nothing else issued since).
+// They complete in issue order. s_waitcnt fields: vmcnt[3:0] and [15:14], expcnt[6:4],
+// lgkmcnt[11:8] (7 and 15 = no wait).
+__device__ __forceinline__ void wait_steps_after(int n) {
+    n *= 8;
+    if (n >= 24) {
+        __builtin_amdgcn_s_waitcnt(0x4F78);  // vmcnt 24
+    } else if (n >= 16) {
+        __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt 16
+    } else if (n >= 8) {
+        __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt 8
+    } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
+    }
+}
+
 template <int KSTEPS>
 __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(ProjArgs a) {
-    __shared__ __attribute__((aligned(16))) float lds_a[2][BM * kStride];
-    __shared__ __attribute__((aligned(16))) float lds_b[2][BN * kStride];
-    static_assert(KSTEPS % 2 == 0, "a tile's first K step goes to LDS buffer 0");
+    __shared__ __attribute__((aligned(16))) float lds[kStages * kStageFloats];
+    // K steps loaded ahead of the one being multiplied
+    constexpr int LA = KSTEPS > kStages - 1 ? kStages - 1 : KSTEPS;
+    constexpr int kHalf = KSTEPS / 2;
+    constexpr bool kHalves = KSTEPS * BK == kWidth;  // inputs written by the previous layer
 
     const int nwg = gridDim.x;  // a multiple of 8
     const int per_xcd = nwg >> 3;
@@ -522,61 +557,62 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    // Inputs written while this kernel runs are read with agent-scope (sc1) buffer loads; the
-    // buffer's range is the whole input, so a load outside it would return zeros.
+    // Inputs written while this kernel runs are read with agent-scope (sc1) loads.
     const bool coherent = a.progress != nullptr;
     const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(a.x), 0, static_cast<int>(static_cast<unsigned int>(a.steps) * a.batch * a.in * 4),
         kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(a.w), 0, kGateCols * a.kpad * 4, kBufferRsrcWord3);
 
-    // staging of one K step: the tile's 128 rows of x and its `width` rows of W
-    v4f ra[kLoadsPerThread], rb[kLoadsPerThread];
-    int srow[kLoadsPerThread];  // gate rows of this thread's staging rows tid / 8 + 32 j
-    auto load = [&](int n0, int k0, int width) {
+    // this lane's row and chunk in each of its four load instructions per operand
+    int lrow[4], lchunk[4];
 #pragma unroll
-        for (int j = 0; j < kLoadsPerThread; ++j) {
-            const int f = tid + kProjThreads * j;
-            const int row = f / kThreadsPerRow;
-            const int k = k0 + (f % kThreadsPerRow) * 4;
-            v4f va = {0.f, 0.f, 0.f, 0.f};
-            if (srow[j] >= 0 && k < a.in) {
-                const unsigned int off = static_cast<unsigned int>(srow[j]) * a.in + k;
-                if (coherent) {
-                    va = __builtin_amdgcn_raw_buffer_load_b128(xrsrc, off * 4, 0, kCachePolicySc1);
-                } else {
-                    va = *reinterpret_cast<const v4f *>(a.x + off);
-                }
-            }
-            ra[j] = va;
-            v4f vb = {0.f, 0.f, 0.f, 0.f};
-            if (row < width) vb = *reinterpret_cast<const v4f *>(a.w + static_cast<size_t>(n0 + row) * a.kpad + k);
-            rb[j] = vb;
+    for (int i = 0; i < 4; ++i) {
+        lrow[i] = wave * 32 + 8 * i + (lane >> 3);
+        lchunk[i] = (lane & 7) ^ ((lrow[i] >> 1) & 7);
+    }
+    // byte offsets of those rows' chunks at K = 0 in x and W for the current and the next tile
+    // (the K offset goes in the scalar offset of each load)
+    unsigned int xoff[4], woff[4], xoff_next[4], woff_next[4];
+    auto offsets_of = [&](const StreamTile &t, unsigned int (&xo)[4], unsigned int (&wo)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = stream_row(a, t, lrow[i]);
+            xo[i] = r >= 0 ? (static_cast<unsigned int>(r) * a.in + 4 * lchunk[i]) * 4u : kOutOfRange;
+            const int n = t.n0 + lrow[i];
+            wo[i] = n < kGateCols ? (static_cast<unsigned int>(n) * a.kpad + 4 * lchunk[i]) * 4u : kOutOfRange;
         }
     };
-    auto store = [&](int buf) {
+    // one K step (K offset k0) into LDS stage `stage`
+    auto issue = [&](int stage, const unsigned int (&xo)[4], const unsigned int (&wo)[4], int k0) {
+        float *sa = &lds[stage * kStageFloats];
+        const int kb = k0 * 4;
 #pragma unroll
-        for (int j = 0; j < kLoadsPerThread; ++j) {
-            const int f = tid + kProjThreads * j;
-            const int off = (f / kThreadsPerRow) * kStride + (f % kThreadsPerRow) * 4;
-            *reinterpret_cast<v4f *>(&lds_a[buf][off]) = ra[j];
-            *reinterpret_cast<v4f *>(&lds_b[buf][off]) = rb[j];
+        for (int i = 0; i < 4; ++i) {
+            // layer 0: k past the 60 inputs reads zeros, not the next row
+            const unsigned int off = (KSTEPS * BK == kWidth || k0 + 4 * lchunk[i] < a.in) ? xo[i] : kOutOfRange;
+            if (coherent) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, sa + (wave * 4 + i) * 256, 16, off, kb, 0,
+                                                         kCachePolicySc1);
+            } else {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, sa + (wave * 4 + i) * 256, 16, off, kb, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, sa + BM * BK + (wave * 4 + i) * 256, 16, wo[i], kb, 0, 0);
         }
     };
     const int frag_row = lane & 31;
-    const int frag_k = (lane >> 5) * 4;
-
-    auto rows_of = [&](const StreamTile &t) {
-#pragma unroll
-        for (int j = 0; j < kLoadsPerThread; ++j) srow[j] = stream_row(a, t, (tid + kProjThreads * j) / kThreadsPerRow);
-    };
 
     bool timed_out = false;
-    // The next tile's first K step is loaded during the current tile's last one when its first
-    // half already exists (known from a progress read issued at the current tile's start); else
-    // the wave waits for it after the current tile is published. Likewise the current tile's
-    // second half is loaded during its first half's last K step when it exists, else after
-    // that step's products, once it does.
-    bool staged = false;  // the tile's first K step is already in LDS buffer 0
+    // The next tile's first K steps are loaded during the current tile's last ones when its
+    // first half already exists (known from a progress read at the current tile's start); else
+    // the tile waits for it when it starts. The current tile's second half is loaded as the
+    // ring frees when it exists; else, after the first half's last products, once it does.
+    bool staged = false;  // the tile's first LA K steps are already issued
+    int sbase = 0;        // LDS stage of the tile's first K step
 
     // One tile TN gate columns wide. The four waves split it WM x WN, each a grid of NI x NJ
     // blocks of 32 x 32 (128 columns: 2 x 2 waves of 64 x 64; 64: 2 x 2 of 64 x 32; 32: 4 x 1
@@ -592,32 +628,12 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
         const int col0 = (wave % WN) * (TN / WN);
         const int n0 = t.n0;
 
-        auto frags = [&](int buf, int g, v4f (&af)[NI], v4f (&bf)[NJ]) {
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                af[i] = *reinterpret_cast<const v4f *>(&lds_a[buf][(row0 + i * 32 + frag_row) * kStride + g * 8 + frag_k]);
-            }
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                bf[j] = *reinterpret_cast<const v4f *>(&lds_b[buf][(col0 + j * 32 + frag_row) * kStride + g * 8 + frag_k]);
-            }
-        };
-
         float sbias[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) sbias[j] = a.bias[n0 + col0 + j * 32 + (lane & 31)];
-        if (!staged) {
-            wait_half(a, t, lane, true, timed_out);
-            rows_of(t);
-            load(n0, kstep_at<KSTEPS>(n0, 0) * BK, TN);
-            store(0);
-        }
-        __syncthreads();
-        v4f af[2][NI], bf[2][NJ];
-        frags(0, 0, af[0], bf[0]);
 
-        // progress of this tile's and of the next tile's windows, read now and checked at the
-        // end of this tile's first half and in its last K step
+        // progress of this tile's and of the next tile's windows, read before any K step of
+        // this tile is issued (so every later wait counts K steps only)
         const unsigned long long *pc = watched_word(a, t, lane);
         const unsigned long long seen_cur =
             pc != nullptr ? __hip_atomic_load(pc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : ~0ull;
@@ -627,6 +643,23 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
         const unsigned long long *pn = next ? watched_word(a, tn, lane) : nullptr;
         const unsigned long long seen_next =
             pn != nullptr ? __hip_atomic_load(pn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : ~0ull;
+
+        // a whole number of rings per tile: every tile starts at stage 0 (compile-time stages)
+        auto stage_of = [&](int g) {
+            return KSTEPS % kStages == 0 ? g & (kStages - 1) : (sbase + g) & (kStages - 1);
+        };
+        if (!staged) {
+            wait_half(a, t, lane, true, timed_out);
+            offsets_of(t, xoff, woff);
+#pragma unroll
+            for (int g = 0; g < LA; ++g) issue(stage_of(g), xoff, woff, kstep_at<KSTEPS>(n0, g) * BK);
+        }
+        int last = LA - 1;  // last K step issued (steps of the next tile count from KSTEPS)
+        // whether the second half exists and whether the next tile's first half does: decided
+        // where first needed, long after the progress reads were issued
+        bool second_ok = !kHalves;
+        bool prefetch = false;
+        bool late = false;
 
         v16f acc[NI][NJ];
 #pragma unroll
@@ -639,25 +672,53 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
         staged = false;
 #pragma unroll
         for (int kt = 0; kt < KSTEPS; ++kt) {
-            const int cur = kt & 1;
-            const bool more = kt + 1 < KSTEPS;
-            // K step kt + 1 starts the tile's second half, which may not exist yet
-            bool late = false;
-            if (more) {
-                if (KSTEPS * BK == kWidth && kt + 1 == KSTEPS / 2 && !__all(half_ready(a, t, lane, seen_cur, false))) {
+            // this wave's loads of step kt have landed; then every wave's have, and every wave
+            // is done with the stage step kt - 1 used. A bare barrier: the fence of
+            // __syncthreads would wait for every load in flight, the later steps' too.
+            wait_steps_after(last - kt);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            // refill that stage with step kt + LA: of this tile, or of the next one
+            const int g = kt + LA;
+            if (kHalves && g == kHalf) second_ok = __all(half_ready(a, t, lane, seen_cur, false));
+            if (g == KSTEPS) prefetch = next && __all(half_ready(a, tn, lane, seen_next, true));
+            if (g < KSTEPS) {
+                if (kHalves && g >= kHalf && !second_ok) {
                     late = true;
                 } else {
-                    load(n0, kstep_at<KSTEPS>(n0, kt + 1) * BK, TN);
+                    issue(stage_of(g), xoff, woff, kstep_at<KSTEPS>(n0, g) * BK);
+                    last = g;
                 }
-            } else if (next && __all(half_ready(a, tn, lane, seen_next, true))) {
-                rows_of(tn);
-                load(tn.n0, kstep_at<KSTEPS>(tn.n0, 0) * BK, tn.width);
+            } else if (prefetch) {
+                if (g == KSTEPS) offsets_of(tn, xoff_next, woff_next);
+                issue(stage_of(g), xoff_next, woff_next, kstep_at<KSTEPS>(tn.n0, g - KSTEPS) * BK);
+                last = g;
                 staged = true;
             }
+            // products of step kt. The fragment addresses are recomputed every step from an
+            // opaque copy of the lane's row (a few ALU operations): hoisted out of the loops,
+            // they took over a hundred registers across the stages and tile widths.
+            const float *sa = &lds[stage_of(kt) * kStageFloats];
+            const float *sb = sa + BM * BK;
+            int fr = frag_row;
+            asm volatile("" : "+v"(fr));
+            v4f af[2][NI], bf[2][NJ];
+            auto frags = [&](int gq, v4f (&fa)[NI], v4f (&fb)[NJ]) {
+                const int c = 2 * gq + (lane >> 5);
 #pragma unroll
-            for (int g = 0; g < kGroups; ++g) {
-                const int p = g & 1;
-                if (g + 1 < kGroups) frags(cur, g + 1, af[p ^ 1], bf[p ^ 1]);
+                for (int i = 0; i < NI; ++i) {
+                    fa[i] = *reinterpret_cast<const v4f *>(&sa[swizzled(row0 + i * 32 + fr, c)]);
+                }
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    fb[j] = *reinterpret_cast<const v4f *>(&sb[swizzled(col0 + j * 32 + fr, c)]);
+                }
+            };
+            frags(0, af[0], bf[0]);
+#pragma unroll
+            for (int gq = 0; gq < kGroups; ++gq) {
+                const int p = gq & 1;
+                if (gq + 1 < kGroups) frags(gq + 1, af[p ^ 1], bf[p ^ 1]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -667,43 +728,60 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[p][i][e], bf[p][j][e],
                                                                              acc[i][j], 0, 0, 0);
             }
-            if (late) {
+            // the second half held back: after the first half's last products, wait for it
+            // and load every step of it the ring has room for
+            if (kHalves && kt == kHalf - 1 && late) {
                 wait_half(a, t, lane, false, timed_out);
-                load(n0, kstep_at<KSTEPS>(n0, kt + 1) * BK, TN);
+#pragma unroll
+                for (int h = kHalf; h <= kt + LA && h < KSTEPS; ++h) {
+                    issue(stage_of(h), xoff, woff, kstep_at<KSTEPS>(n0, h) * BK);
+                    last = h;
+                }
+                late = false;
+                second_ok = true;
             }
-            // the last K step reads buffer 1, so the next tile's first K step goes to buffer 0
-            if (more || staged) store(cur ^ 1);
-            __syncthreads();
-            if (more) frags(cur ^ 1, 0, af[0], bf[0]);
+        }
+        sbase = (sbase + KSTEPS) & (kStages - 1);
+        if (staged) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xoff[i] = xoff_next[i];
+                woff[i] = woff_next[i];
+            }
         }
 
-        // store with agent-scope stores; once every wave's stores have completed, publish
+        // store with agent-scope stores; once every wave's stores have completed, publish.
+        // Row r of block i is local row lb + i·32 + (r / 4)·8 + r % 4 (lb from an opaque copy,
+        // so the row arithmetic is not hoisted out of the tile loop into registers). A 32-row
+        // block lies in one window (chunks are 32 steps or more), so its rows are consecutive
+        // steps: gate row = the block's first row's, plus or minus the step offset.
+        int lb = row0 + (lane >> 5) * 4;
+        asm volatile("" : "+v"(lb));
         float *const gcol = a.gates + n0 + col0 + (lane & 31);
-        auto put_row = [&](int i, int r, int m) {
+        const bool full = t.w0 + a.group_windows <= a.batch && t.s0 + a.chunk <= a.steps;
+        const int dstep = t.dir == 0 ? 1 : -1;
+        int bm0[NI], bw[NI], bs0[NI];
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                __hip_atomic_store(gcol + static_cast<size_t>(m) * kGateCols + j * 32, acc[i][j][r] + sbias[j],
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = 0; i < NI; ++i) {
+            const int lr0 = lb + i * 32;                  // local row of r = 0
+            bw[i] = t.w0 + (lr0 >> a.chunk_shift);        // the block's window
+            bs0[i] = t.s0 + (lr0 & (a.chunk - 1));        // step of r = 0
+            bm0[i] = bw[i] * a.steps + (t.dir == 0 ? bs0[i] : a.steps - 1 - bs0[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ds = (r >> 2) * 8 + (r & 3);
+                if (full || (bw[i] < a.batch && bs0[i] + ds < a.steps)) {
+                    float *const p = gcol + static_cast<ptrdiff_t>(bm0[i] + dstep * ds) * kGateCols;
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        __hip_atomic_store(p + j * 32, acc[i][j][r] + sbias[j], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
             }
-        };
-        if (t.w0 + a.group_windows <= a.batch && t.s0 + a.chunk <= a.steps) {
-            // every row of the tile exists (all but the ragged last chunk and group)
-#pragma unroll
-            for (int i = 0; i < NI; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int lr = row0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                    const int sr = t.s0 + (lr & (a.chunk - 1));
-                    put_row(i, r, (t.w0 + (lr >> a.chunk_shift)) * a.steps + (t.dir == 0 ? sr : a.steps - 1 - sr));
-                }
-        } else {
-#pragma unroll
-            for (int i = 0; i < NI; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = stream_row(a, t, row0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3));
-                    if (m >= 0) put_row(i, r, m);
-                }
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
