@@ -186,9 +186,10 @@ inline int stream_projection_workgroups(int cu_count, int recur_tiles, int recur
 inline int stream_tiles(int chunks, int groups, int split) {
     return (chunks - 1 + split) * 2 * groups * (kGates / kProjTileN);
 }
-// Dynamic LDS a streamed projection workgroup claims on top of its tiles, so that two of them
-// never share a CU (2 · (72 + 16) KB > 160 KB): its persistent grid then spreads one per CU.
-constexpr size_t kProjStreamLds = 16 * 1024;
+// Dynamic LDS a streamed projection workgroup claims on top of its 128 KB K-step ring: none,
+// the ring alone keeps two of them off one CU (2 · 128 KB > 160 KB), so its persistent grid
+// spreads one per CU.
+constexpr size_t kProjStreamLds = 0;
 inline int stream_chunks(int steps, int chunk) { return (steps + chunk - 1) / chunk; }
 // Progress words one 128-byte line apart: each window's direction has its own line, so the
 // recurrence's stores and the projection's polls of different windows never share one.
