@@ -55,9 +55,10 @@ def run(bl, x, layers, repeats=1, **kw):
 
 
 # (batch, steps, tile): one window (chunks of 128 steps), two (64), three and more (32); steps
-# below one chunk, below the 8 steps the counters are read ahead, not a multiple of the chunk
-SHAPES = [(1, 589, 0), (1, 1, 0), (2, 130, 0), (3, 150, 0), (3, 3, 0), (5, 7, 0), (4, 33, 0), (8, 200, 0),
-          (8, 97, 2), (8, 64, 4), (32, 150, 0)]
+# below one chunk, below the 8 steps the counters are read ahead, just past a chunk, not a
+# whole number of chunks
+SHAPES = [(1, 589, 0), (1, 1, 0), (1, 129, 0), (2, 130, 0), (2, 65, 0), (3, 150, 0), (3, 3, 0), (5, 7, 0),
+          (4, 33, 0), (4, 17, 0), (8, 200, 0), (8, 97, 2), (8, 64, 4), (32, 150, 0)]
 
 
 @pytest.mark.parametrize("pipeline", [2, 4, 3])
