@@ -186,10 +186,6 @@ inline int stream_projection_workgroups(int cu_count, int recur_tiles, int recur
 inline int stream_tiles(int chunks, int groups, int split) {
     return (chunks - 1 + split) * 2 * groups * (kGates / kProjTileN);
 }
-// Dynamic LDS a streamed projection workgroup claims on top of its 128 KB K-step ring: none,
-// the ring alone keeps two of them off one CU (2 · 128 KB > 160 KB), so its persistent grid
-// spreads one per CU.
-constexpr size_t kProjStreamLds = 0;
 inline int stream_chunks(int steps, int chunk) { return (steps + chunk - 1) / chunk; }
 // Progress words one 128-byte line apart: each window's direction has its own line, so the
 // recurrence's stores and the projection's polls of different windows never share one.
@@ -201,11 +197,10 @@ __host__ __device__ inline int stream_far(int steps, int chunk, int c) { return 
 
 // Launchers (kernels_*.hip). They return the launch's hipError_t.
 hipError_t launch_heads(const HeadArgs &args, hipStream_t stream);
-// The projection on `workgroups` persistent workgroups (one per CU; rounded to a multiple of 8),
-// each with `dynamic_lds` bytes of dynamic LDS besides its tiles.
-hipError_t launch_projection(const ProjArgs &args, int workgroups, size_t dynamic_lds, hipStream_t stream);
-// Allow `bytes` of dynamic LDS per streamed projection workgroup.
-hipError_t projection_allow_lds(size_t bytes);
+// The projection on `workgroups` persistent workgroups (one per CU; rounded to a multiple of 8).
+// The streamed kernel's 128 KB K-step ring keeps two of its workgroups off one CU (2 · 128 KB
+// > 160 KB), so its persistent grid spreads one per CU.
+hipError_t launch_projection(const ProjArgs &args, int workgroups, hipStream_t stream);
 hipError_t launch_recurrence(int groups, int tile, const RecurArgs &args, int directions,
                              size_t dynamic_lds, hipStream_t stream);
 // The streamed recurrences of several layers in one launch (single-workgroup tiles of `tile`

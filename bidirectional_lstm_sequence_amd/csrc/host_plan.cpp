@@ -282,7 +282,7 @@ bilstm_status enqueue_projection(bilstm_plan *p, int layer, const float *x, floa
             args.progress_pass = static_cast<unsigned long long>(p->layer_pass - 1) << 32;
         }
     }
-    BL_HIP(launch_projection(args, workgroups, streamed ? kProjStreamLds : 0, stream), "projection launch");
+    BL_HIP(launch_projection(args, workgroups, stream), "projection launch");
     return BILSTM_OK;
 }
 
@@ -672,7 +672,6 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
             p->reserve_lds = kCuLdsBytes - kProjLdsBytes + 4096;
             e = recurrence_allow_lds(info.recur_groups, info.recur_tile, p->reserve_lds);
         }
-        if (e == hipSuccess) e = projection_allow_lds(kProjStreamLds);
         p->proj_workgroups_streamed = stream_projection_workgroups(cu_count, info.recur_tiles, info.recur_groups);
     }
     if (e == hipSuccess) e = hipDeviceSynchronize();

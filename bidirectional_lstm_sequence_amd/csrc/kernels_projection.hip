@@ -418,11 +418,12 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_split_kernel(ProjA
 
 // ---- streamed order ------------------------------------------------------------------------
 //
-// The same MFMA tile as projection_kernel over the streamed row blocks (StreamLayout in the
-// internal header). A tile's first K step is loaded once its rows exist (during the previous
-// tile's last K step if they already do), and its outputs are stored and published as soon as
-// its K loop ends, so no finished tile waits behind the inputs of the next one. Every row sums
-// its K terms in the same order as projection_kernel, so the gates are bitwise the same.
+// The same MFMA blocks as projection_kernel over the streamed row blocks (StreamLayout in the
+// internal header). A tile's first K steps are loaded once its first half exists (during the
+// previous tile's last K steps if it already does), its second half once that exists, and its
+// outputs are stored and published as soon as its K loop ends, so no finished tile waits
+// behind the inputs of the next one. Every row sums its K terms in the same order as
+// projection_kernel, so the gates are bitwise the same.
 
 // Row block of streamed tile q: first window, first step, chunk, direction, first gate
 // column, width in gate columns and publication counter.
@@ -806,15 +807,7 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
 
 }  // namespace
 
-hipError_t projection_allow_lds(size_t bytes) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&projection_stream_kernel<2>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
-    if (e != hipSuccess) return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&projection_stream_kernel<8>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
-}
-
-hipError_t launch_projection(const ProjArgs &args, int workgroups, size_t dynamic_lds, hipStream_t stream) {
+hipError_t launch_projection(const ProjArgs &args, int workgroups, hipStream_t stream) {
     if (args.tiles <= 0) return hipSuccess;
     // a multiple of 8 (the XCD-ordered walk), at most one workgroup per tile group of 8
     int nwg = std::min(workgroups, (args.tiles + 7) / 8 * 8);
@@ -827,10 +820,10 @@ hipError_t launch_projection(const ProjArgs &args, int workgroups, size_t dynami
         }
         switch (args.kpad / kProjTileK) {
             case 2:
-                hipLaunchKernelGGL(projection_stream_kernel<2>, dim3(nwg), dim3(kProjThreads), dynamic_lds, stream, args);
+                hipLaunchKernelGGL(projection_stream_kernel<2>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
                 break;
             case 8:
-                hipLaunchKernelGGL(projection_stream_kernel<8>, dim3(nwg), dim3(kProjThreads), dynamic_lds, stream, args);
+                hipLaunchKernelGGL(projection_stream_kernel<8>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
                 break;
             default:
                 return hipErrorInvalidValue;
