@@ -75,9 +75,8 @@ constexpr int kBcast = L * 0x55;  // quad_perm L,L,L,L: every lane reads quad la
 // Activations on the hardware exp2 and reciprocal: σ(a) = 1/(1 + 2^(-a·log2 e)) and
 // tanh(a) = 2σ(2a) - 1. The recurrent rows arrive pre-multiplied by -log2 e (i, f, o) or
 // -2·log2 e (g) (kGateExpScale), and the gate input is scaled the same way, so a gate's sum is
-// already the exponent z and its activation is A·rcp(1 + 2^z) + B with (A, B) = (1, 0) for
-// σ and (2, -1) for tanh. For z -> +inf, 2^z overflows to +inf and the reciprocal returns the
-// exact limit 0, so no clamp is needed.
+// already the exponent z and rcp(1 + 2^z) is σ (i, f, o) or (tanh + 1)/2 (g). For z -> +inf,
+// 2^z overflows to +inf and the reciprocal returns the exact limit 0, so no clamp is needed.
 __device__ __forceinline__ float rcp_one_plus_exp2(float z) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
 }
@@ -293,9 +292,10 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
     }
     const bool is_g = q == 2;
     const float zscale = is_g ? kGateExpScale[2] : kGateExpScale[0];  // of gate q
-    const float act_a = is_g ? 2.0f : 1.0f;
-    const float act_b = is_g ? -1.0f : 0.0f;
-    float cst = 0.0f;  // cell state of (unit ug, window qe)
+    // The cell state is kept multiplied by kCellScale = -2·log2 e, the factor tanh's exponent
+    // needs, so no multiply stands between c and its exponential.
+    constexpr float kCellScale = kGateExpScale[2];
+    float cst = 0.0f;  // kCellScale · cell state of (unit ug, window qe)
 
     // One step s; P is the step's slot in the prefetch ring (s mod kRing), a compile-time
     // constant so the ring stays in registers.
@@ -373,24 +373,28 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
             sum[b] = t0 + dpp<kXor2>(t2);
         }
 
-        // (3) activation of gate q for each window, then every lane updates the cell of
-        // window qe
-        float act[BT];
+        // (3) σ of gate q for each window (i, f, o are read as they are; lane 2 turns its
+        // value r into kCellScale·tanh = kCellScale·(2r - 1), one fma beside the broadcasts of
+        // i and f), then every lane updates the cell of window qe
+        float sig[BT], gsc[BT];
 #pragma unroll
-        for (int b = 0; b < BT; ++b) act[b] = fmaf(act_a, rcp_one_plus_exp2(sum[b]), act_b);
+        for (int b = 0; b < BT; ++b) {
+            sig[b] = rcp_one_plus_exp2(sum[b]);
+            gsc[b] = fmaf(2.0f * kCellScale, sig[b], -kCellScale);
+        }
         float ig[BT], fg[BT], gg[BT], og[BT];
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
-            ig[b] = dpp<kBcast<0>>(act[b]);
-            fg[b] = dpp<kBcast<1>>(act[b]);
-            gg[b] = dpp<kBcast<2>>(act[b]);
-            og[b] = dpp<kBcast<3>>(act[b]);
+            ig[b] = dpp<kBcast<0>>(sig[b]);
+            fg[b] = dpp<kBcast<1>>(sig[b]);
+            gg[b] = dpp<kBcast<2>>(gsc[b]);
+            og[b] = dpp<kBcast<3>>(sig[b]);
         }
         const float i_w = pick<BT>(ig, qe), f_w = pick<BT>(fg, qe);
         const float g_w = pick<BT>(gg, qe), o_w = pick<BT>(og, qe);
         cst = fmaf(f_w, cst, i_w * g_w);
-        // h = o·tanh(c) = 2o·rcp(1 + 2^(-2c·log2 e)) - o
-        const float hval = fmaf(o_w + o_w, rcp_one_plus_exp2(cst * kGateExpScale[2]), -o_w);
+        // h = o·tanh(c) = 2o·rcp(1 + 2^(kCellScale·c)) - o
+        const float hval = fmaf(o_w + o_w, rcp_one_plus_exp2(cst), -o_w);
 
         // h to LDS for the next step (lanes of one window write the same value)
         hs[nxt][hpad(ug) * BT + qe] = hval;
