@@ -241,18 +241,22 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
         }
     };
     float *const ycol = a.y + static_cast<size_t>(win0 + qe) * steps * kWidth + dir * kHidden + ug;
-    // One-window tiles (KG = 1, BT = 1): the gate row of the next refill and the output row of
+    // Single-workgroup tiles (KG = 1): the gate row of the next refill and the output row of
     // the current step are uniform pointers moved by one row per step (a scalar add; the
     // refill stops at the last step), instead of addresses rebuilt from the step index every
     // step: that arithmetic sat between the cell update and the barrier (measured: streamed
-    // b32 forward 1.192 -> 1.159 ms, plain one-window recurrence -2 %).
-    constexpr bool kRowPtrs = KG == 1 && BT == 1;
+    // b32 forward 1.192 -> 1.159 ms, plain one-window recurrence -2 %, two-window -3.5 %).
+    constexpr bool kRowPtrs = KG == 1;
     const long gate_row_step = dir == 0 ? kGateCols : -static_cast<long>(kGateCols);
     const long y_row_step = dir == 0 ? kWidth : -static_cast<long>(kWidth);
     const float *gate_row = a.gates + (static_cast<size_t>(win0) * steps + time_of(max(0, min(kRing, steps - 1)))) * kGateCols;
-    float *y_row = a.y + (static_cast<size_t>(win0 + qe) * steps + time_of(0)) * kWidth;
+    float *y_row = a.y + (static_cast<size_t>(win0) * steps + time_of(0)) * kWidth;
     const int gate_off = static_cast<int>(gate_col);
-    const int y_off = dir * kHidden + ug;
+    const size_t y_off = static_cast<size_t>(qe) * steps * kWidth + dir * kHidden + ug;
+    // window b's gate rows relative to window 0's (windows past the batch read window 0's)
+    size_t win_off[BT];
+#pragma unroll
+    for (int b = 0; b < BT; ++b) win_off[b] = win0 + b < a.batch ? static_cast<size_t>(b) * steps * kGateCols : 0;
 
     // KG == 1: per-lane register ring of gate inputs.
     float ring[kRing][BT];
@@ -426,8 +430,11 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
         if constexpr (KG == 1) {
             // refill this ring slot with step s + kRing
             if constexpr (kRowPtrs) {
-                ring[P][0] = STREAM ? __hip_atomic_load(gate_row + gate_off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                    : gate_row[gate_off];
+#pragma unroll
+                for (int b = 0; b < BT; ++b) {
+                    const float *gp = gate_row + win_off[b] + gate_off;
+                    ring[P][b] = STREAM ? __hip_atomic_load(gp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *gp;
+                }
                 gate_row = s + kRing + 1 < steps ? gate_row + gate_row_step : gate_row;
             } else {
 #pragma unroll
