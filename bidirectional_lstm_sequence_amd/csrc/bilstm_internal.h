@@ -103,7 +103,8 @@ struct RecurArgs {
     // Streamed gates (chunk > 0): before reading the gates of steps [c·chunk, (c+1)·chunk) of
     // window group g, wait until ready[(c·2 + dir)·groups + g] reaches ready_target.
     const unsigned int *ready;
-    int chunk;
+    int chunk;                     // a power of two
+    int chunk_shift;               // log2(chunk)
     int group_windows;
     int groups;
     unsigned int ready_target;

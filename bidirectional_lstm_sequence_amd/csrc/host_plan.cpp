@@ -307,6 +307,8 @@ RecurArgs recurrence_args(const bilstm_plan *p, int layer, const float *gates, f
     if (streamed) {
         base.ready = reinterpret_cast<const unsigned int *>(p->ready + buffer * p->ready_words);
         base.chunk = s.stream_chunk;
+        base.chunk_shift = 0;
+        while ((1 << base.chunk_shift) < base.chunk) ++base.chunk_shift;
         base.group_windows = kProjTileM / s.stream_chunk;
         base.groups = p->stream_groups;
         // a forced timeout expects a count no pass reaches

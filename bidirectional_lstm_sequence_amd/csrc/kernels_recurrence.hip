@@ -201,7 +201,7 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
         STREAM ? a.ready + static_cast<size_t>(dir) * a.groups + win0 / a.group_windows : nullptr;
     auto ready_ptr = [&](int s) {
         const int sc = s < steps ? s : steps - 1;
-        return ready_tile + static_cast<size_t>(sc / a.chunk) * 2 * a.groups;
+        return ready_tile + static_cast<unsigned int>(sc >> a.chunk_shift) * (2u * a.groups);
     };
     auto read_ready = [&](int s) -> unsigned int {
         return __hip_atomic_load(ready_ptr(s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -211,12 +211,14 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
     // after. The per-lane address keeps the value in a vector register across the group (a
     // value the compiler sees as uniform would be moved to a scalar register at once, which
     // waits for the load, and with it for every gate prefetch, right after it is issued).
+    const int lane_chunk = (tid & 1) * a.chunk;
     auto read_ready_ahead = [&](int s) -> unsigned int {
-        return __hip_atomic_load(ready_ptr(s + (tid & 1) * a.chunk), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return __hip_atomic_load(ready_ptr(s + lane_chunk), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-    // Wait until the chunk of step s is published; `seen` is what read_ready_ahead(s) returned.
+    // Wait until the chunk of step s is published; `seen` is what read_ready_ahead(s) returned,
+    // checked in lane 0 (an even lane) with a scalar compare.
     auto wait_ready = [&](unsigned int seen, int s) {
-        if (__builtin_expect(__all((tid & 1) || published(seen)) || timed_out, 1)) return;
+        if (__builtin_expect(published(__builtin_amdgcn_readfirstlane(seen)) || timed_out, 1)) return;
         const unsigned long long t0 = wall_clock64();
         while (true) {
             __builtin_amdgcn_s_sleep(1);
@@ -230,13 +232,18 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
     };
     unsigned int ready_seen = 0;  // counter of the chunk of the group after the current one
     // STREAM: progress[window][dir] = progress_pass | steps whose output stores have completed,
-    // for every window of the tile (read by the next layer's projection)
+    // for every window of the tile (read by the next layer's projection). Written by wave 0
+    // (`publisher`, a wave-uniform test, so no lane mask is set up); its lanes store the same
+    // word.
+    unsigned long long *const progress_tile = STREAM ? a.progress + kProgressStride * (2 * win0 + dir) : nullptr;
+    const unsigned long long progress_pass = a.progress_pass;
+    const bool publisher = __builtin_amdgcn_readfirstlane(tid) == 0;
     auto publish = [&](unsigned int done) {
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
             if (win0 + b < a.batch) {
-                __hip_atomic_store(a.progress + kProgressStride * (2 * (win0 + b) + dir), a.progress_pass | done,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(progress_tile + kProgressStride * 2 * b, progress_pass | done, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     };
@@ -320,17 +327,6 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
         const int cur = s & 1;
         const int nxt = cur ^ 1;
 
-        if constexpr (STREAM && P == 0) {
-            // this group refills the ring with steps s + kRing .. s + 2·kRing - 1 (one chunk):
-            // check the counter read a group ago, and read the one for the next group
-            wait_ready(ready_seen, s + kRing);
-            ready_seen = read_ready_ahead(s + 2 * kRing);
-            // Publish this tile's progress. Every wave has passed the previous step's barrier
-            // and, before it, waited for the gate load issued kRing steps earlier; vector
-            // memory operations complete in issue order, so every output store of the steps
-            // before s - 2·kRing has completed.
-            if (tid == 0) publish(static_cast<unsigned int>(s >= 2 * kRing ? s - 2 * kRing : 0));
-        }
 
         // (1) partial dot products over this lane's K quarter; gate q's scaled input starts
         // the sum in slot 0, so the reduction below yields the whole exponent
@@ -365,6 +361,20 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
 #pragma unroll
                 for (int v = 0; v < 8 * BT; ++v) hv[v] = *reinterpret_cast<const v4f *>(hp + 4 * v);
                 if constexpr (STREAM || BT > 1) __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (STREAM && P == 0) {
+                // This group refills the ring with steps s + kRing .. s + 2·kRing - 1 (one
+                // chunk): check the counter read a group ago, and read the one for the next
+                // group. Done while the h reads above are in flight (measured: streamed b32
+                // forward 1.150 -> 1.144 ms against doing it before them).
+                wait_ready(ready_seen, s + kRing);
+                ready_seen = read_ready_ahead(s + 2 * kRing);
+                // Publish this tile's progress. Every wave has passed the previous step's
+                // barrier and, before it, waited for the gate load issued kRing steps earlier;
+                // vector memory operations complete in issue order, so every output store of
+                // the steps before s - 2·kRing has completed.
+                if (publisher) publish(static_cast<unsigned int>(s >= 2 * kRing ? s - 2 * kRing : 0));
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int v = 0; v < 8 * BT; ++v) {
@@ -501,7 +511,7 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
         // every wave's output stores have completed: the whole sequence is published
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (tid == 0) publish(static_cast<unsigned int>(steps));
+        if (publisher) publish(static_cast<unsigned int>(steps));
     }
 }
 
