@@ -8,15 +8,18 @@
 // Work split. A launch covers `tile_count` tiles of BT windows for one direction (or both,
 // gridDim.y = 2). Each tile is served by KG workgroups; workgroup `member` owns hidden
 // units [member·U, (member+1)·U), U = 128/KG, i.e. the 4U packed gate rows 4j+g of R, held
-// in VGPRs for the whole launch. Four adjacent lanes (a quad) share a unit: lane q holds the
-// unit's four gate rows over the K quarter [32q, 32q+32) — 128 values. Its register slot s
-// holds gate q XOR s, which turns the quad reduction into a reduce-scatter with no selects.
+// in VGPRs for the whole launch. Eight adjacent lanes share two units (8 gate rows): lane l
+// of the group holds all 8 rows over the K eighth [16l, 16l+16) — 128 values — so a lane
+// reads only 16·BT values of h per step (half of what a K quarter per lane would need; the LDS
+// reads of h co-limit the step). Its register slot s holds row l ^ slot_row(s), which turns
+// the group's reduction into a reduce-scatter with no selects; lane l ends with row l, so
+// each quad holds one unit's gates i, f, g, o.
 //
 // One step s (t = s forward, T-1-s reverse):
-//  1. every lane: 4·BT dot products of its rows with its quarter of h_{t-1} (from LDS), each
+//  1. every lane: 8·BT dot products of its rows with its eighth of h_{t-1} (from LDS), each
 //     summed in k order from the first product;
-//  2. quad reduce-scatter with DPP: lane q ends with gate q's full sum, always combined as
-//     ((p0 + p1) + (p2 + p3)) over the quarters — one fixed order for every split;
+//  2. reduce-scatter over the group with DPP (partners l ^ 7, l ^ 2, l ^ 1): lane l ends with
+//     row l's full sum, combined in one fixed order for every split and tile;
 //  3. lane q: a = gate input + sum; the activation of gate q (σ for i, f, o; tanh for g,
 //     as 2σ(2a) - 1); the lane of window b collects the four activations, updates
 //     c = f·c + i·g and h = o·tanh(c), and writes h to LDS, to the output and, when KG > 1,
@@ -58,10 +61,17 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kRingPlain = 4;
 constexpr int kRingStream = 8;
 
-// Padded h index: 4 floats of padding after every 32, so the four K quarters of h start on
-// different LDS banks.
-__device__ __forceinline__ int hpad(int k) { return k + (k >> 5) * 4; }
-constexpr int kHPad = kHidden + kHidden / 8;
+// LDS index of h element f = k·BT + b (unit k, window b of the tile): 4 floats of padding
+// after every 64, so the eight K eighths a wave reads (16·BT consecutive elements each) start
+// on distinct banks.
+__device__ __forceinline__ int hidx(int f) { return f + 4 * (f >> 6); }
+template <int BT>
+constexpr int kHLen = kHidden * BT + 4 * (kHidden * BT / 64);
+
+// Register slot s of a lane holds row l ^ slot_row(s) of its 8-lane group (l = lane in the
+// group): s = 4·b1 + 2·b2 + b3 maps to 7·b1 ^ 2·b2 ^ b3, the partners of the three reduction
+// levels (half-row mirror l ^ 7, then l ^ 2, then l ^ 1).
+__host__ __device__ constexpr int slot_row(int s) { return ((s & 4) ? 7 : 0) ^ ((s & 2) ? 2 : 0) ^ (s & 1); }
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -69,6 +79,7 @@ __device__ __forceinline__ float dpp(float v) {
 }
 constexpr int kXor1 = 0xB1;       // quad_perm 1,0,3,2
 constexpr int kXor2 = 0x4E;       // quad_perm 2,3,0,1
+constexpr int kMirror8 = 0x141;   // row_half_mirror: lane l of each 8 reads lane 7 - l = l ^ 7
 template <int L>
 constexpr int kBcast = L * 0x55;  // quad_perm L,L,L,L: every lane reads quad lane L
 
@@ -154,30 +165,31 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
     // lane runs the same straight-line code and their stores are idempotent.
     const int qe = (q < BT && win0 + q < a.batch) ? q : 0;
 
-    __shared__ __attribute__((aligned(16))) float hs[2][kHPad * BT];
+    __shared__ __attribute__((aligned(16))) float hs[2][kHLen<BT>];
     __shared__ __attribute__((aligned(16))) float gs[KG > 1 ? 2 : 1][KG > 1 ? U * 4 * BT : 4];
 
-    // ---- recurrent weights into VGPRs: slot s = gate q^s, K quarter q ----------------------
-    float rr[4][32];
+    // ---- recurrent weights into VGPRs: slot s = row l ^ slot_row(s) of the lane's 8-lane
+    // group (the group's rows are units 2·grp, 2·grp + 1 × gates i, f, g, o), K eighth l ------
+    const int l8 = tid & 7;
+    float rr[8][16];
     {
-        const float *rdir = a.r + static_cast<size_t>(dir) * kGates * kHidden;
+        const float *rgrp = a.r + (static_cast<size_t>(dir) * kGates + 4 * (member * U) + 8 * (tid >> 3)) * kHidden;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const v4f *p = reinterpret_cast<const v4f *>(
-                rdir + static_cast<size_t>(4 * ug + (q ^ s)) * kHidden + 32 * q);
+        for (int sl = 0; sl < 8; ++sl) {
+            const v4f *p = reinterpret_cast<const v4f *>(rgrp + static_cast<size_t>(l8 ^ slot_row(sl)) * kHidden + 16 * l8);
 #pragma unroll
-            for (int v = 0; v < 8; ++v) {
+            for (int v = 0; v < 4; ++v) {
                 const v4f x = p[v];
-                rr[s][4 * v + 0] = x[0];
-                rr[s][4 * v + 1] = x[1];
-                rr[s][4 * v + 2] = x[2];
-                rr[s][4 * v + 3] = x[3];
+                rr[sl][4 * v + 0] = x[0];
+                rr[sl][4 * v + 1] = x[1];
+                rr[sl][4 * v + 2] = x[2];
+                rr[sl][4 * v + 3] = x[3];
             }
         }
     }
 
     // h_{-1} = 0
-    for (int i = tid; i < 2 * kHPad * BT; i += NT) (&hs[0][0])[i] = 0.0f;
+    for (int i = tid; i < 2 * kHLen<BT>; i += NT) (&hs[0][0])[i] = 0.0f;
 
     auto time_of = [&](int s) { return dir == 0 ? s : steps - 1 - s; };
     // Gate input of gate q, unit ug, window b of the tile at step s. Steps past the end and
@@ -345,9 +357,9 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
             }
             zin[b] = gin * zscale;
         }
-        float acc[4][BT];
+        float acc[8][BT];
         {
-            const float *hp = &hs[cur][36 * q * BT];
+            const float *hp = &hs[cur][hidx(16 * l8 * BT)];
             // every LDS read of h first, so their latencies overlap (the FMAs then wait for
             // each in turn). Left to itself the compiler spaced them out in the streamed and
             // multi-window kernels; there a scheduling barrier keeps them together (measured:
@@ -356,10 +368,10 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
             // Four windows' h (128 registers) would not fit beside R: there the compiler
             // schedules the reads.
             constexpr bool kUpfront = BT <= 2;
-            v4f hv[kUpfront ? 8 * BT : 1];
+            v4f hv[kUpfront ? 4 * BT : 1];
             if constexpr (kUpfront) {
 #pragma unroll
-                for (int v = 0; v < 8 * BT; ++v) hv[v] = *reinterpret_cast<const v4f *>(hp + 4 * v);
+                for (int v = 0; v < 4 * BT; ++v) hv[v] = *reinterpret_cast<const v4f *>(hp + 4 * v);
                 if constexpr (STREAM || BT > 1) __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (STREAM && P == 0) {
@@ -377,7 +389,7 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
-            for (int v = 0; v < 8 * BT; ++v) {
+            for (int v = 0; v < 4 * BT; ++v) {
                 const v4f h4 = kUpfront ? hv[v] : *reinterpret_cast<const v4f *>(hp + 4 * v);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -385,7 +397,7 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
                     const int kk = idx / BT;
                     const int b = idx % BT;
 #pragma unroll
-                    for (int sl = 0; sl < 4; ++sl) {
+                    for (int sl = 0; sl < 8; ++sl) {
                         acc[sl][b] = kk != 0   ? fmaf(rr[sl][kk], h4[e], acc[sl][b])
                                      : sl == 0 ? fmaf(rr[0][0], h4[e], zin[b])
                                                : rr[sl][0] * h4[e];
@@ -394,13 +406,17 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
             }
         }
 
-        // (2) reduce-scatter: lane q keeps gate q's exponent ((p0+p1)+(p2+p3))
+        // (2) reduce-scatter over the 8-lane group: lane l keeps row l's exponent (gate q of
+        // unit ug), its eighths combined level by level with the partners l ^ 7, l ^ 2, l ^ 1
         float sum[BT];
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
-            const float t0 = acc[0][b] + dpp<kXor1>(acc[1][b]);  // gate q, quads {q, q^1}
-            const float t2 = acc[2][b] + dpp<kXor1>(acc[3][b]);  // gate q^2
-            sum[b] = t0 + dpp<kXor2>(t2);
+            float t[4];
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl) t[sl] = acc[sl][b] + dpp<kMirror8>(acc[sl + 4][b]);
+            const float u0 = t[0] + dpp<kXor2>(t[2]);
+            const float u1 = t[1] + dpp<kXor2>(t[3]);
+            sum[b] = u0 + dpp<kXor1>(u1);
         }
 
         // (3) σ of gate q for each window (i, f, o are read as they are; lane 2 turns its
@@ -427,7 +443,7 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
         const float hval = fmaf(o_w + o_w, rcp_one_plus_exp2(cst), -o_w);
 
         // h to LDS for the next step (lanes of one window write the same value)
-        hs[nxt][hpad(ug) * BT + qe] = hval;
+        hs[nxt][hidx(ug * BT + qe)] = hval;
         const unsigned int flag = a.flag_base + static_cast<unsigned int>(s) + 1u;
         if constexpr (KG > 1) {
             if (q < BT) {
@@ -483,7 +499,7 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
                             }
                         }
                     }
-                    hs[nxt][hpad(ugo) * BT + b] = __uint_as_float(static_cast<unsigned int>(w));
+                    hs[nxt][hidx(ugo * BT + b)] = __uint_as_float(static_cast<unsigned int>(w));
                 }
             }
         }
