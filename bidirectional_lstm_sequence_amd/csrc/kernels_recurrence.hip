@@ -340,8 +340,9 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
         const int nxt = cur ^ 1;
 
 
-        // (1) partial dot products over this lane's K quarter; gate q's scaled input starts
-        // the sum in slot 0, so the reduction below yields the whole exponent
+        // (1) partial dot products of the lane's 8 rows over its K eighth; slot 0 (row l of the
+        // group = gate q of unit ug) starts from that gate's scaled input, so the reduction
+        // below yields the whole exponent
         float zin[BT];
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
@@ -365,7 +366,7 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
             // multi-window kernels; there a scheduling barrier keeps them together (measured:
             // streamed b32 forward 1.30 -> 1.298 ms, two windows 0.998 -> 0.955 us per step),
             // while it slows the plain one-window kernel (0.471 -> 0.491 us), already in order.
-            // Four windows' h (128 registers) would not fit beside R: there the compiler
+            // Four windows' h (64 registers) would not fit beside R and the 32 sums: there the compiler
             // schedules the reads.
             constexpr bool kUpfront = BT <= 2;
             v4f hv[kUpfront ? 4 * BT : 1];
