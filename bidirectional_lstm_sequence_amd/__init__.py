@@ -170,6 +170,42 @@ def _options(groups: int, tile: int, concurrent: int, watchdog_us: int = 0, slic
     return o
 
 
+def layers_from_state_dict(state_dict) -> list[dict[str, np.ndarray]]:
+    """The four layer dicts ``Plan`` takes, from the parameters of
+    ``torch.nn.LSTM(60, 128, num_layers=4, bidirectional=True, batch_first=True)``.
+
+    Per layer k and direction d (``""`` forward, ``"_reverse"``): ``weight_ih_l{k}{d}`` is W,
+    ``weight_hh_l{k}{d}`` is R, ``bias_ih_l{k}{d}`` is Wb and ``bias_hh_l{k}{d}`` is Rb (an LSTM
+    built with ``bias=False`` gives zero biases). Both use nn.LSTM's gate row order i, f, g, o,
+    the order the library takes. Values are copied to float32 on the host; nothing is computed.
+    """
+    def host(name):
+        v = state_dict[name]
+        if hasattr(v, "detach"):
+            v = v.detach().to("cpu").numpy()
+        return np.asarray(v, dtype=np.float32)
+
+    layers = []
+    for k in range(LAYERS):
+        width = FEATURES if k == 0 else WIDTH
+        w, r, b = [], [], []
+        for suffix in ("", "_reverse"):
+            wk, rk = host(f"weight_ih_l{k}{suffix}"), host(f"weight_hh_l{k}{suffix}")
+            if wk.shape != (GATES, width) or rk.shape != (GATES, HIDDEN):
+                raise ValueError(f"layer {k}{suffix}: weight_ih {wk.shape} / weight_hh {rk.shape}, expected "
+                                 f"({GATES}, {width}) / ({GATES}, {HIDDEN})")
+            zero = np.zeros(GATES, np.float32)
+            bi = host(f"bias_ih_l{k}{suffix}") if f"bias_ih_l{k}{suffix}" in state_dict else zero
+            bh = host(f"bias_hh_l{k}{suffix}") if f"bias_hh_l{k}{suffix}" in state_dict else zero
+            if bi.shape != (GATES,) or bh.shape != (GATES,):
+                raise ValueError(f"layer {k}{suffix}: biases {bi.shape} / {bh.shape}, expected ({GATES},)")
+            w.append(wk)
+            r.append(rk)
+            b.append(np.stack([bi, bh]))
+        layers.append({"w": np.stack(w), "r": np.stack(r), "b": np.stack(b)})
+    return layers
+
+
 def pack_layer(layer: dict, width: int) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Host-side packer (no GPU): packed W [1024, kpad], R [2, 512, 128], bias [1024]."""
     lib = library()

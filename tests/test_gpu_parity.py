@@ -350,3 +350,21 @@ def test_stack_degenerate_shapes(bl, orc, batch, steps, slices, projection):
     got, info = run_stack(bl, x, layers, slices=slices, projection=projection)
     ref = orc.stack(x, layers)
     assert_close(got, ref, f"b{batch} t{steps}")
+
+
+def test_torch_lstm_parameters_run_on_the_library(bl):
+    # an nn.LSTM's own parameters, converted by the binding, against the module in float64
+    torch.manual_seed(21)
+    net = torch.nn.LSTM(60, 128, num_layers=4, bidirectional=True, batch_first=True)
+    layers = bl.layers_from_state_dict(net.state_dict())
+    x = torch.randn(3, 61, 60)
+    note("torch nn.LSTM parameters: batch 3, steps 61")
+    with torch.no_grad():
+        ref, _ = net.double()(x.double())
+    plan = bl.Plan(layers, 3, 61, device=0)
+    try:
+        y = plan.forward(x.to("cuda:0"))
+        plan.check()
+        assert_close(y.cpu().numpy(), ref.numpy(), "nn.LSTM parameters")
+    finally:
+        plan.close()

@@ -298,3 +298,47 @@ def test_heads_create_argument_checks_without_gpu(bl):
     assert lib.bilstm_heads_create(0, None, ctypes.byref(h)) == 1
     assert lib.bilstm_heads_forward(None, None, 0, None, 0, None) == 1
     lib.bilstm_heads_destroy(None)
+
+
+def _float32_lstm(bias: bool, seed: int):
+    """nn.LSTM(60, 128, 4, bidirectional) in float64 whose parameters hold float32 values, so
+    the converter's float32 copy and the module see the same numbers."""
+    torch = pytest.importorskip("torch")
+    torch.manual_seed(seed)
+    net = torch.nn.LSTM(60, 128, num_layers=4, bidirectional=True, batch_first=True, bias=bias,
+                        dtype=torch.float64)
+    with torch.no_grad():
+        for p in net.parameters():
+            p.copy_(p.to(torch.float32).to(torch.float64))
+    return net
+
+
+@pytest.mark.parametrize("bias", [True, False])
+def test_layers_from_state_dict_match_the_torch_module(oracle_lib, bias):
+    # the oracle on converted parameters reproduces the module itself (directions, gate rows
+    # i, f, g, o, bias_ih as Wb and bias_hh as Rb, zero biases for bias=False)
+    torch = pytest.importorskip("torch")
+    import bidirectional_lstm_sequence_amd as bl
+    net = _float32_lstm(bias, seed=11)
+    layers = bl.layers_from_state_dict(net.state_dict())
+    assert [l["w"].shape for l in layers] == [(2, 512, 60)] + [(2, 512, 256)] * 3
+    assert all(l["r"].shape == (2, 512, 128) and l["b"].shape == (2, 2, 512) for l in layers)
+    assert all(l["w"].dtype == np.float32 for l in layers)
+    if not bias:
+        assert all(not l["b"].any() for l in layers)
+    x = np.random.default_rng(4).standard_normal((2, 9, 60)).astype(np.float32)
+    with torch.no_grad():
+        ref, _ = net(torch.from_numpy(x.astype(np.float64)))
+    got = oracle_lib.stack(x, layers)
+    assert np.abs(got - ref.numpy()).max() < 1e-12
+
+
+def test_layers_from_state_dict_rejects_other_shapes():
+    torch = pytest.importorskip("torch")
+    import bidirectional_lstm_sequence_amd as bl
+    net = torch.nn.LSTM(61, 128, num_layers=4, bidirectional=True, batch_first=True)
+    with pytest.raises(ValueError, match="layer 0"):
+        bl.layers_from_state_dict(net.state_dict())
+    net = torch.nn.LSTM(60, 128, num_layers=3, bidirectional=True, batch_first=True)
+    with pytest.raises(KeyError):
+        bl.layers_from_state_dict(net.state_dict())
