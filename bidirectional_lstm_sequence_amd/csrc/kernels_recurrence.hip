@@ -57,9 +57,13 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // Prefetch depth in steps: gate loads of step s are issued at step s - depth. Streamed gates
 // are read with agent-scope loads, which go past the L2, so they are issued further ahead, as
 // they are for single-window tiles, whose steps are shortest (measured: 8 steps 0.472 against
-// 4 steps 0.480 us per step; for two-window tiles 4 steps is better).
+// 4 steps 0.480 us per step; for two-window tiles 4 steps is better). Streamed one-window
+// tiles take 16: their group start (chunk counter check, progress word) then comes every 16
+// steps (measured: b32 forward 1.121 -> 1.112 ms; the plain kernel is 0.6 % slower with 16).
+// A chunk (32, 64 or 128 steps) is always a whole number of rings.
 constexpr int kRingPlain = 4;
-constexpr int kRingStream = 8;
+constexpr int kRingOne = 8;
+constexpr int kRingStreamOne = 16;
 
 // LDS index of h element f = k·BT + b (unit k, window b of the tile): 4 floats of padding
 // after every 64, so the eight K eighths a wave reads (16·BT consecutive elements each) start
@@ -137,7 +141,7 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
     constexpr int NT = 4 * U;        // threads
     static_assert(KG == 1 || NT >= 128, "a polling wave besides the staging wave");
     static_assert(!STREAM || KG == 1, "streamed gates: single-workgroup tiles only");
-    constexpr int kRing = STREAM || (KG == 1 && BT == 1) ? kRingStream : kRingPlain;
+    constexpr int kRing = STREAM && BT == 1 ? kRingStreamOne : (STREAM || (KG == 1 && BT == 1)) ? kRingOne : kRingPlain;
 
     // ---- which tile, member and direction ------------------------------------------------
     int tile, member;
