@@ -131,7 +131,7 @@ constexpr int kHeadIn = 256;
 constexpr int kHeadMid = 128;
 constexpr int kHeadClasses = 7;
 constexpr int kHeadClassSlots = 8;
-constexpr int kHeadTileRows = 64;
+constexpr int kHeadTileRows = 32;
 constexpr int kHeadThreads = 256;
 
 struct HeadArgs {
