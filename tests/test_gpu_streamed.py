@@ -153,3 +153,34 @@ def test_streamed_watchdog_reports_timeout_and_grid_drains(bl, pipeline):
     got, _ = run(bl, xs, layers, pipeline=2)
     base, _ = run(bl, xs, layers, pipeline=1)
     assert np.array_equal(got[0].view(np.uint32), base[0].view(np.uint32))
+
+
+@pytest.mark.parametrize("pipeline", [0, 1])
+def test_forward_follows_the_callers_stream(bl, pipeline):
+    # The forward runs in the order of the stream it is given: work queued on that stream
+    # before it (a long spin, then new input) is seen by every layer, and work queued after it
+    # (a copy of the output) sees the whole stack. Streamed (pipeline 0 = auto) and unstreamed.
+    batch, steps = 8, 300
+    layers = workloads.make_layers(77)
+    x_old = torch.from_numpy(workloads.make_input(78, batch, steps)).cuda()
+    x_new = torch.from_numpy(workloads.make_input(79, batch, steps)).cuda()
+    note(f"caller's stream: pipeline {pipeline}, batch {batch}, steps {steps}")
+    plan = bl.Plan(layers, batch, steps, device=0, pipeline=pipeline)
+    try:
+        ref = plan.forward(x_new)
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()  # default priority
+        x = x_old.clone()
+        y = torch.zeros_like(ref)
+        out = torch.empty_like(ref)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            torch.cuda._sleep(20_000_000)   # keeps the stream busy for milliseconds
+            x.copy_(x_new)
+            plan.forward(x, y, stream=side)
+            out.copy_(y)
+        side.synchronize()
+        plan.check()
+        assert torch.equal(out, ref)
+    finally:
+        plan.close()
