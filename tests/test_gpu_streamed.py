@@ -59,6 +59,8 @@ def run(bl, x, layers, repeats=1, **kw):
 # whole number of chunks
 SHAPES = [(1, 589, 0), (1, 1, 0), (1, 129, 0), (2, 130, 0), (2, 65, 0), (3, 150, 0), (3, 3, 0), (5, 7, 0),
           (4, 33, 0), (4, 17, 0), (8, 200, 0), (8, 97, 2), (8, 64, 4), (32, 150, 0),
+          # one-window tiles prefetch 16 steps: sequences just short of, at and past whole rings
+          (3, 15, 0), (2, 16, 0), (4, 32, 0), (1, 48, 0),
           # projection grids of 128 and 64 workgroups beside the recurrence
           (64, 70, 0), (96, 40, 0)]
 
