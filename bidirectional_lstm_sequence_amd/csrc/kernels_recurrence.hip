@@ -59,7 +59,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // they are for single-window tiles, whose steps are shortest (measured: 8 steps 0.472 against
 // 4 steps 0.480 us per step; for two-window tiles 4 steps is better). Streamed one-window
 // tiles take 16: their group start (chunk counter check, progress word) then comes every 16
-// steps (measured: b32 forward 1.121 -> 1.112 ms; the plain kernel is 0.6 % slower with 16).
+// steps (measured: b32 forward 1.121 -> 1.112 ms; the plain kernel is 0.6 % slower with 16;
+// a 32-step ring is slower again, 1.114 -> 1.127 ms).
 // A chunk (32, 64 or 128 steps) is always a whole number of rings.
 constexpr int kRingPlain = 4;
 constexpr int kRingOne = 8;
