@@ -57,7 +57,7 @@ class Options(ctypes.Structure):
     _fields_ = [("recur_groups", ctypes.c_int32), ("recur_tile", ctypes.c_int32),
                 ("concurrent", ctypes.c_int32), ("watchdog_us", ctypes.c_int32),
                 ("slices", ctypes.c_int32), ("projection", ctypes.c_int32), ("pipeline", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 1)]
+                ("near_wrap", ctypes.c_int32)]
 
 
 class HeadWeights(ctypes.Structure):
@@ -81,7 +81,7 @@ class PlanInfo(ctypes.Structure):
                 ("slice_windows", ctypes.c_int32), ("projection", ctypes.c_int32),
                 ("pipeline", ctypes.c_int32), ("stream_chunk", ctypes.c_int32),
                 ("stream_overlap", ctypes.c_int32), ("stream_split", ctypes.c_int32),
-                ("stream_fused", ctypes.c_int32)]
+                ("stream_fused", ctypes.c_int32), ("clears", ctypes.c_uint32)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -158,8 +158,9 @@ def _layer_struct(layer: dict, keep: list) -> Layer:
 
 
 def _options(groups: int, tile: int, concurrent: int, watchdog_us: int = 0, slices: int = 0,
-             projection: int = 0, pipeline: int = 0) -> Options:
+             projection: int = 0, pipeline: int = 0, near_wrap: int = 0) -> Options:
     o = Options()
+    o.near_wrap = near_wrap
     o.projection = projection
     o.pipeline = pipeline
     o.recur_groups = groups
@@ -270,18 +271,19 @@ class Plan:
     2 through the library's split-precision kernel; ``pipeline`` streams each layer's gates
     from its projection into its recurrence while both run (0 = auto, 1 = off, 2 = on, 3 = on with
     each projection after the previous layer's recurrence, 4 = on with the next layer's projection
-    during this layer's recurrence).
+    during this layer's recurrence); ``near_wrap`` = 1 starts the plan's flag epoch and pass
+    counters just below the values at which it clears them (a test hook for the clear paths).
     """
 
     def __init__(self, layers, batch: int, steps: int, device: int = 0, groups: int = 0,
                  tile: int = 0, concurrent: int = -1, watchdog_us: int = 0, slices: int = 0,
-                 projection: int = 0, pipeline: int = 0):
+                 projection: int = 0, pipeline: int = 0, near_wrap: int = 0):
         if len(layers) != LAYERS:
             raise ValueError(f"expected {LAYERS} layers, got {len(layers)}")
         lib = library()
         keep: list = []
         arr = (Layer * LAYERS)(*[_layer_struct(l, keep) for l in layers])
-        opt = _options(groups, tile, concurrent, watchdog_us, slices, projection, pipeline)
+        opt = _options(groups, tile, concurrent, watchdog_us, slices, projection, pipeline, near_wrap)
         handle = ctypes.c_void_p()
         _check(lib.bilstm_plan_create_ex(device, batch, steps, arr, ctypes.byref(opt), ctypes.byref(handle)))
         self._lib = lib
@@ -333,7 +335,7 @@ class Plan:
         return y
 
     def check(self) -> None:
-        """Wait for the plan's work; raise BilstmError(BILSTM_TIMEOUT) if a watchdog fired."""
+        """Wait for the plan's last call; raise BilstmError(BILSTM_TIMEOUT) if a watchdog fired."""
         _check(self._lib.bilstm_check(self._h))
 
     def set_phase_events(self, enable: bool) -> None:

@@ -52,6 +52,14 @@ inline size_t exchange_words_per_direction(int tiles, int tile) {
     return static_cast<size_t>(tiles) * 2 * kHidden * tile;
 }
 
+// Watchdog reports. A wait that gives up stores 1 into the word of its kind; the plan keeps
+// the words in host-mapped coherent memory, so the host reads them without a device
+// synchronization, and the next call on the plan reports them.
+constexpr int kErrExchange = 0;  // a recurrence exchange wait (flagged h words)
+constexpr int kErrCounter = 1;   // a recurrence wait for a chunk counter (streamed gates)
+constexpr int kErrProgress = 2;  // a projection wait for the previous layer's progress
+constexpr int kErrWords = 4;
+
 struct ProjArgs {
     const float *x;      // [rows][in]
     const float *w;      // [1024][kpad]
@@ -80,7 +88,7 @@ struct ProjArgs {
     // rows need (see StreamLayout); the rows are then read with agent-scope loads.
     const unsigned long long *progress;  // [batch][2], kProgressStride words apart
     unsigned long long progress_pass;    // (previous layer's pass number) << 32
-    unsigned int *error;                 // watchdog flag word
+    unsigned int *error;                 // [kErrWords] watchdog reports
     unsigned long long timeout_ticks;
 };
 
@@ -89,7 +97,7 @@ struct RecurArgs {
     const float *r;                // [2][512][128] packed rows 4j+g
     float *y;                      // [batch][steps][256]
     unsigned long long *exchange;  // [2][tiles][2][128][tile] words (groups > 1)
-    unsigned int *error;           // watchdog flag word
+    unsigned int *error;           // [kErrWords] watchdog reports
     int batch;
     int steps;
     int direction;                 // direction of blockIdx.y == 0
@@ -198,6 +206,12 @@ __host__ __device__ inline int stream_far(int steps, int chunk, int c) { return 
 
 // Launchers (kernels_*.hip). They return the launch's hipError_t.
 hipError_t launch_heads(const HeadArgs &args, hipStream_t stream);
+#ifdef __HIP__  // HIP-language sources only; the host .cpp files include this header as C++
+// Report a wait that gave up (one system-scope store; the host may be reading the word).
+__device__ __forceinline__ void report_timeout(unsigned int *error, int kind) {
+    __hip_atomic_store(error + kind, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+#endif
 // The projection on `workgroups` persistent workgroups (one per CU; rounded to a multiple of 8).
 // The streamed kernel's 128 KB K-step ring keeps two of its workgroups off one CU (2 · 128 KB
 // > 160 KB), so its persistent grid spreads one per CU.

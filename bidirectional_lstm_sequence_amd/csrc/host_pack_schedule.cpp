@@ -46,7 +46,9 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
                     cu_count, per_cu);
     }
     if (opt != nullptr) {
-        if (opt->reserved[0] != 0) return fail(BILSTM_INVALID_ARGUMENT, "options: reserved[0] must be 0");
+        if (opt->near_wrap != 0 && opt->near_wrap != 1) {
+            return fail(BILSTM_INVALID_ARGUMENT, "options: near_wrap %d is not 0 or 1", opt->near_wrap);
+        }
         if (opt->pipeline < 0 || opt->pipeline > 4) {
             return fail(BILSTM_INVALID_ARGUMENT, "options: pipeline %d is not one of 0..4", opt->pipeline);
         }

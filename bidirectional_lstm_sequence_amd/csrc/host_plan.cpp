@@ -18,6 +18,13 @@ namespace bl {
 namespace {
 thread_local std::string g_last_error;
 
+// Streamed gates: pass counts above which the counters and progress words are cleared and the
+// counts start again from zero. A counter holds kReadyPerPass per pass (a 32-bit word, compared
+// wrap-safely against its target, so it must stay far from 2^32 / kReadyPerPass passes); a
+// progress word holds the layer pass in its upper 32 bits.
+constexpr uint32_t kReadyPassLimit = 0x03FFFFFFu;
+constexpr uint32_t kLayerPassLimit = 0x0FFFFFF0u;
+
 // Watchdog of a recurrence wait, in milliseconds. A step normally takes microseconds; the
 // limit only has to end a wait whose producer can never arrive.
 constexpr double kWatchdogMs = 2000.0;
@@ -58,7 +65,10 @@ struct bilstm_plan {
     float *gates = nullptr;
     unsigned long long *exchange = nullptr;
     size_t exchange_words = 0;
-    unsigned int *error = nullptr;
+    unsigned int *error = nullptr;       // device address of the watchdog reports
+    unsigned int *error_host = nullptr;  // the same kErrWords words, host-mapped
+    hipEvent_t done = nullptr;           // recorded on the caller's stream at the end of every call
+    uint32_t clears = 0;                 // clears of the exchange words or streamed counters
     hipStream_t side = nullptr;
     hipEvent_t fork[kLayers] = {nullptr, nullptr, nullptr, nullptr};
     hipEvent_t join[kLayers] = {nullptr, nullptr, nullptr, nullptr};
@@ -201,7 +211,8 @@ void release(bilstm_plan *p) {
     if (p->library) library_projection_destroy(p->library);
     if (p->gates) (void)hipFree(p->gates);
     if (p->exchange) (void)hipFree(p->exchange);
-    if (p->error) (void)hipFree(p->error);
+    if (p->error_host) (void)hipHostFree(p->error_host);
+    if (p->done) (void)hipEventDestroy(p->done);
     if (p->side) (void)hipStreamDestroy(p->side);
     delete p;
 }
@@ -232,6 +243,7 @@ bilstm_status reserve_flags(bilstm_plan *p, uint32_t count, hipStream_t stream, 
     if (static_cast<uint64_t>(p->epoch) + count + 1 > 0xFFFFFFFFull) {
         BL_HIP(launch_exchange_clear(p->exchange, p->exchange_words, stream), "exchange clear");
         p->epoch = 0;
+        ++p->clears;
     }
     *base = p->epoch;
     p->epoch += count;
@@ -350,11 +362,16 @@ bilstm_status enqueue_recurrence(bilstm_plan *p, int layer, const float *gates, 
     if (s.concurrent == 1) {
         BL_HIP(hipEventRecord(p->fork[layer], stream), "fork");
         BL_HIP(hipStreamWaitEvent(p->side, p->fork[layer], 0), "fork wait");
-        if ((st = launch_direction(0, 1, stream)) != BILSTM_OK) return st;
-        if ((st = launch_direction(1, 1, p->side)) != BILSTM_OK) return st;
-        BL_HIP(hipEventRecord(p->join[layer], p->side), "join");
-        BL_HIP(hipStreamWaitEvent(stream, p->join[layer], 0), "join wait");
-        return BILSTM_OK;
+        st = launch_direction(0, 1, stream);
+        if (st == BILSTM_OK) st = launch_direction(1, 1, p->side);
+        // join the side stream back, also when a launch failed
+        hipError_t e = hipEventRecord(p->join[layer], p->side);
+        if (e == hipSuccess) e = hipStreamWaitEvent(stream, p->join[layer], 0);
+        if (e != hipSuccess) {
+            (void)hipStreamSynchronize(p->side);
+            if (st == BILSTM_OK) st = fail(BILSTM_HIP_ERROR, "recurrence join: %s", hipGetErrorString(e));
+        }
+        return st;
     }
     if ((st = launch_direction(0, 1, stream)) != BILSTM_OK) return st;
     return launch_direction(1, 1, stream);
@@ -370,8 +387,8 @@ bilstm_status enqueue_recurrence(bilstm_plan *p, int layer, const float *gates, 
 // projection reads.
 bilstm_status forward_streamed(bilstm_plan *p, const float *x, float *y, hipStream_t stream, uint32_t base) {
     bilstm_status st;
-    if (p->ready_dirty || p->layer_pass > 0x0FFFFFF0u || p->ready_passes[0] > 0x03FFFFFFu ||
-        p->ready_passes[1] > 0x03FFFFFFu) {
+    if (p->ready_dirty || p->layer_pass > kLayerPassLimit || p->ready_passes[0] > kReadyPassLimit ||
+        p->ready_passes[1] > kReadyPassLimit) {
         // counters out of step with the pass counts (a failed enqueue), or close to wrapping
         BL_HIP(launch_exchange_clear(p->ready, 2 * p->ready_words, stream), "counter clear");
         BL_HIP(launch_exchange_clear(p->progress, kProgressStride * 2 * static_cast<size_t>(p->batch), stream),
@@ -379,9 +396,26 @@ bilstm_status forward_streamed(bilstm_plan *p, const float *x, float *y, hipStre
         p->ready_passes[0] = p->ready_passes[1] = 0;
         p->layer_pass = 0;
         p->ready_dirty = false;
+        ++p->clears;
     }
     BL_HIP(hipEventRecord(p->proj_fork, stream), "projection fork");
     BL_HIP(hipStreamWaitEvent(p->proj_stream, p->proj_fork, 0), "projection fork wait");
+    // From here on the projection stream is forked: whatever happens, join it back into the
+    // caller's stream before returning, so the caller's stream order covers every projection
+    // already enqueued (the next pass's counter clear must not overtake them).
+    struct Join {
+        bilstm_plan *p;
+        hipStream_t stream;
+        bool armed = true;
+        ~Join() {
+            if (!armed) return;
+            if (hipEventRecord(p->proj_join, p->proj_stream) == hipSuccess) {
+                (void)hipStreamWaitEvent(stream, p->proj_join, 0);
+            } else {
+                (void)hipStreamSynchronize(p->proj_stream);
+            }
+        }
+    } join{p, stream};
     if (p->phase_events) BL_HIP(hipEventRecord(p->ev_start, stream), "phase event");
     // the four recurrences in one launch
     const bool one_launch = p->info.stream_fused != 0;
@@ -430,12 +464,112 @@ bilstm_status forward_streamed(bilstm_plan *p, const float *x, float *y, hipStre
             BL_HIP(hipEventRecord(p->ev_recur[kLayers - 1], stream), "phase event");
         }
     }
+    join.armed = false;
     BL_HIP(hipEventRecord(p->proj_join, p->proj_stream), "projection join");
     BL_HIP(hipStreamWaitEvent(stream, p->proj_join, 0), "projection join wait");
     p->phases_recorded = p->phase_events;
     p->phases_streamed = true;
     p->phases_fused = one_launch;
     return BILSTM_OK;
+}
+
+// The stack without streamed gates: per layer the projection, then the recurrence, each
+// batch slice as its own chain of layers on its own stream (slice 0 on the caller's stream).
+bilstm_status forward_sliced(bilstm_plan *plan, const float *x, float *y, hipStream_t stream, uint32_t base) {
+    const bilstm_plan_info &info = plan->info;
+    const int slices = info.slices;
+    bilstm_status st;
+    if (slices > 1) {
+        // fork: every slice stream starts after the caller's prior work
+        BL_HIP(hipEventRecord(plan->slice_fork, stream), "slice fork");
+        for (int i = 1; i < slices; ++i) {
+            BL_HIP(hipStreamWaitEvent(plan->slice_stream[i], plan->slice_fork, 0), "slice fork wait");
+        }
+    }
+    // From here on the slice streams are forked: join every one back into the caller's
+    // stream before returning, also when an enqueue fails part way.
+    struct Join {
+        bilstm_plan *p;
+        hipStream_t stream;
+        int slices;
+        bilstm_status join() {
+            bilstm_status r = BILSTM_OK;
+            for (int i = 1; i < slices; ++i) {
+                hipError_t e = hipEventRecord(p->slice_join[i], p->slice_stream[i]);
+                if (e == hipSuccess) e = hipStreamWaitEvent(stream, p->slice_join[i], 0);
+                if (e != hipSuccess) {
+                    (void)hipStreamSynchronize(p->slice_stream[i]);
+                    if (r == BILSTM_OK) r = fail(BILSTM_HIP_ERROR, "slice join: %s", hipGetErrorString(e));
+                }
+            }
+            slices = 0;
+            return r;
+        }
+        ~Join() { (void)join(); }
+    } joiner{plan, stream, slices};
+    if (plan->phase_events) BL_HIP(hipEventRecord(plan->ev_start, stream), "phase event");
+    for (int l = 0; l < kLayers; ++l) {
+        for (int i = 0; i < slices; ++i) {
+            // slice i holds windows [w0, w1); its chain runs on its own stream
+            const uint32_t w0 = static_cast<uint32_t>(i) * info.slice_windows;
+            const uint32_t w1 = std::min<uint32_t>(plan->batch, w0 + info.slice_windows);
+            hipStream_t on = i > 0 ? plan->slice_stream[i] : stream;
+            // The first projections run one slice after another, so the slices' recurrences
+            // start staggered and each later projection meets recurrences, not projections.
+            if (slices > 1 && l == 0 && i > 0) {
+                BL_HIP(hipStreamWaitEvent(on, plan->slice_first[i - 1], 0), "slice stagger");
+            }
+            // every layer after the first reads the previous layer's complete output from y
+            if ((st = enqueue_projection(plan, l, l == 0 ? x : y, plan->gates, on,
+                                         static_cast<size_t>(w0) * plan->steps,
+                                         static_cast<size_t>(w1 - w0) * plan->steps,
+                                         slices > 1 ? plan->proj_workgroups_sliced : plan->proj_workgroups)) !=
+                BILSTM_OK) {
+                return st;
+            }
+            if (slices > 1 && l == 0) BL_HIP(hipEventRecord(plan->slice_first[i], on), "slice stagger");
+            if (plan->phase_events && i == 0) BL_HIP(hipEventRecord(plan->ev_proj[l], on), "phase event");
+            const int t0 = static_cast<int>(w0 / info.recur_tile);
+            const int t1 = static_cast<int>((w1 + info.recur_tile - 1) / info.recur_tile);
+            if ((st = enqueue_recurrence(plan, l, plan->gates, y, base + l * plan->steps, on, i == 0, t0, t1)) !=
+                BILSTM_OK) {
+                return st;
+            }
+            if (plan->phase_events && i == 0) BL_HIP(hipEventRecord(plan->ev_recur[l], on), "phase event");
+        }
+    }
+    // join: the caller's stream waits for every other slice
+    if ((st = joiner.join()) != BILSTM_OK) return st;
+    plan->phases_recorded = plan->phase_events;
+    plan->phases_streamed = false;
+    plan->phases_fused = false;
+    return BILSTM_OK;
+}
+
+// A watchdog report of an earlier call, read from the host-mapped words without a device
+// synchronization: cleared and returned as BILSTM_TIMEOUT, so a caller that never calls
+// bilstm_check still learns that an output it may have consumed is invalid.
+bilstm_status take_timeout_report(bilstm_plan *p, const char *context) {
+    volatile unsigned int *words = p->error_host;
+    unsigned int seen = 0;
+    for (int k = 0; k < kErrWords; ++k) seen |= words[k] != 0 ? 1u << k : 0u;
+    if (seen == 0) return BILSTM_OK;
+    for (int k = 0; k < kErrWords; ++k) words[k] = 0;
+    return fail(BILSTM_TIMEOUT,
+                "%s: a wait of an earlier call on this plan hit its %.3f ms watchdog (%s%s%s); that call's "
+                "outputs are invalid; nothing was enqueued",
+                context, p->watchdog_ms, (seen & (1u << kErrExchange)) ? "exchange " : "",
+                (seen & (1u << kErrCounter)) ? "chunk counter " : "", (seen & (1u << kErrProgress)) ? "progress" : "");
+}
+
+// The end of a call that enqueued work: the plan's completion event goes on the caller's
+// stream (after any join), whatever `st` is, so bilstm_check waits for all of it.
+bilstm_status mark_done(bilstm_plan *p, hipStream_t stream, bilstm_status st, const char *context) {
+    const hipError_t e = hipEventRecord(p->done, stream);
+    if (st == BILSTM_OK && e != hipSuccess) {
+        return fail(BILSTM_HIP_ERROR, "%s: completion event: %s", context, hipGetErrorString(e));
+    }
+    return st;
 }
 
 bilstm_status check_plan_buffers(const char *context, const bilstm_plan *p, const void *a,
@@ -603,8 +737,18 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
             return fail_release(st);
         }
     }
-    if ((st = device_alloc(p, &p->error, 1, "error word")) != BILSTM_OK) return fail_release(st);
-    e = hipMemset(p->error, 0, sizeof(unsigned int));
+    // watchdog reports: host-mapped, coherent words the kernels store into and the host reads
+    // without synchronizing
+    e = hipHostMalloc(reinterpret_cast<void **>(&p->error_host), kErrWords * sizeof(unsigned int),
+                      hipHostMallocMapped | hipHostMallocCoherent);
+    if (e != hipSuccess) {
+        p->error_host = nullptr;
+        return fail_release(fail(BILSTM_HIP_ERROR, "plan_create: hipHostMalloc of the watchdog words: %s",
+                                 hipGetErrorString(e)));
+    }
+    std::memset(p->error_host, 0, kErrWords * sizeof(unsigned int));
+    e = hipHostGetDevicePointer(reinterpret_cast<void **>(&p->error), p->error_host, 0);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->done, hipEventDisableTiming);
     if (info.recur_groups > 1) {
         p->exchange_words = 2 * exchange_words_per_direction(info.recur_tiles, info.recur_tile);
         if ((st = device_alloc(p, &p->exchange, p->exchange_words, "exchange")) != BILSTM_OK) {
@@ -676,6 +820,20 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
         }
         p->proj_workgroups_streamed = stream_projection_workgroups(cu_count, info.recur_tiles, info.recur_groups);
     }
+    if (e == hipSuccess && options != nullptr && options->near_wrap != 0) {
+        // Test hook: flags and pass numbers start just below their clear thresholds (those of
+        // reserve_flags and forward_streamed), so the first forward runs near the top of their
+        // range and the second one clears. The counters hold kReadyPerPass per pass so far.
+        const uint32_t count = kLayers * steps;
+        p->epoch = 0xFFFFFFFFu - 1u - count - count / 2;
+        p->ready_passes[0] = p->ready_passes[1] = kReadyPassLimit - 1;
+        p->layer_pass = kLayerPassLimit - (kLayers - 1);
+        if (p->ready != nullptr) {
+            e = hipMemsetD32(reinterpret_cast<hipDeviceptr_t>(p->ready),
+                             static_cast<int>((kReadyPassLimit - 1) * static_cast<uint32_t>(kReadyPerPass)),
+                             4 * p->ready_words);
+        }
+    }
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         return fail_release(fail(BILSTM_HIP_ERROR, "plan_create: scratch setup: %s", hipGetErrorString(e)));
@@ -702,65 +860,17 @@ bilstm_status bilstm_forward(bilstm_plan *plan, const float *x, size_t x_len, fl
     auto stream = static_cast<hipStream_t>(stream_ptr);
     DeviceScope scope(plan->device);
     BL_HIP(scope.error(), "forward: hipSetDevice");
+    if ((st = take_timeout_report(plan, "forward")) != BILSTM_OK) return st;
 
     uint32_t base = 0;
     if ((st = reserve_flags(plan, kLayers * plan->steps, stream, &base)) != BILSTM_OK) return st;
-    const bilstm_plan_info &info = plan->info;
-    if (info.pipeline) {
+    if (plan->info.pipeline) {
         st = forward_streamed(plan, x, y, stream, base);
         if (st != BILSTM_OK) plan->ready_dirty = true;
-        return st;
+    } else {
+        st = forward_sliced(plan, x, y, stream, base);
     }
-    const int slices = info.slices;
-    if (slices > 1) {
-        // fork: every slice stream starts after the caller's prior work
-        BL_HIP(hipEventRecord(plan->slice_fork, stream), "slice fork");
-        for (int i = 1; i < slices; ++i) {
-            BL_HIP(hipStreamWaitEvent(plan->slice_stream[i], plan->slice_fork, 0), "slice fork wait");
-        }
-    }
-    if (plan->phase_events) BL_HIP(hipEventRecord(plan->ev_start, stream), "phase event");
-    for (int l = 0; l < kLayers; ++l) {
-        for (int i = 0; i < slices; ++i) {
-            // slice i holds windows [w0, w1); its chain runs on its own stream
-            const uint32_t w0 = static_cast<uint32_t>(i) * info.slice_windows;
-            const uint32_t w1 = std::min<uint32_t>(plan->batch, w0 + info.slice_windows);
-            hipStream_t on = i > 0 ? plan->slice_stream[i] : stream;
-            // The first projections run one slice after another, so the slices' recurrences
-            // start staggered and each later projection meets recurrences, not projections.
-            if (slices > 1 && l == 0 && i > 0) {
-                BL_HIP(hipStreamWaitEvent(on, plan->slice_first[i - 1], 0), "slice stagger");
-            }
-            // every layer after the first reads the previous layer's complete output from y
-            if ((st = enqueue_projection(plan, l, l == 0 ? x : y, plan->gates, on,
-                                         static_cast<size_t>(w0) * plan->steps,
-                                         static_cast<size_t>(w1 - w0) * plan->steps,
-                                         slices > 1 ? plan->proj_workgroups_sliced : plan->proj_workgroups)) !=
-                BILSTM_OK) {
-                return st;
-            }
-            if (slices > 1 && l == 0) BL_HIP(hipEventRecord(plan->slice_first[i], on), "slice stagger");
-            if (plan->phase_events && i == 0) BL_HIP(hipEventRecord(plan->ev_proj[l], on), "phase event");
-            const int t0 = static_cast<int>(w0 / info.recur_tile);
-            const int t1 = static_cast<int>((w1 + info.recur_tile - 1) / info.recur_tile);
-            if ((st = enqueue_recurrence(plan, l, plan->gates, y, base + l * plan->steps, on, i == 0, t0, t1)) !=
-                BILSTM_OK) {
-                return st;
-            }
-            if (plan->phase_events && i == 0) BL_HIP(hipEventRecord(plan->ev_recur[l], on), "phase event");
-        }
-    }
-    if (slices > 1) {
-        // join: the caller's stream waits for every other slice
-        for (int i = 1; i < slices; ++i) {
-            BL_HIP(hipEventRecord(plan->slice_join[i], plan->slice_stream[i]), "slice join");
-            BL_HIP(hipStreamWaitEvent(stream, plan->slice_join[i], 0), "slice join wait");
-        }
-    }
-    plan->phases_recorded = plan->phase_events;
-    plan->phases_streamed = false;
-    plan->phases_fused = false;
-    return BILSTM_OK;
+    return mark_done(plan, stream, st, "forward");
 }
 
 bilstm_status bilstm_project(bilstm_plan *plan, int layer, const float *x, size_t x_len,
@@ -772,8 +882,10 @@ bilstm_status bilstm_project(bilstm_plan *plan, int layer, const float *x, size_
     if ((st = check_len("project gates", plan->rows * kGateCols, gates_len)) != BILSTM_OK) return st;
     DeviceScope scope(plan->device);
     BL_HIP(scope.error(), "project: hipSetDevice");
-    return enqueue_projection(plan, layer, x, gates, static_cast<hipStream_t>(stream_ptr), 0, plan->rows,
-                              plan->proj_workgroups);
+    if ((st = take_timeout_report(plan, "project")) != BILSTM_OK) return st;
+    auto stream = static_cast<hipStream_t>(stream_ptr);
+    st = enqueue_projection(plan, layer, x, gates, stream, 0, plan->rows, plan->proj_workgroups);
+    return mark_done(plan, stream, st, "project");
 }
 
 bilstm_status bilstm_recur(bilstm_plan *plan, int layer, const float *gates, size_t gates_len,
@@ -786,14 +898,17 @@ bilstm_status bilstm_recur(bilstm_plan *plan, int layer, const float *gates, siz
     auto stream = static_cast<hipStream_t>(stream_ptr);
     DeviceScope scope(plan->device);
     BL_HIP(scope.error(), "recur: hipSetDevice");
+    if ((st = take_timeout_report(plan, "recur")) != BILSTM_OK) return st;
     uint32_t base = 0;
     if ((st = reserve_flags(plan, plan->steps, stream, &base)) != BILSTM_OK) return st;
-    return enqueue_recurrence(plan, layer, gates, y, base, stream, false, 0, plan->info.recur_tiles);
+    st = enqueue_recurrence(plan, layer, gates, y, base, stream, false, 0, plan->info.recur_tiles);
+    return mark_done(plan, stream, st, "recur");
 }
 
 bilstm_status bilstm_plan_get_info(const bilstm_plan *plan, bilstm_plan_info *info) {
     if (plan == nullptr || info == nullptr) return fail(BILSTM_INVALID_ARGUMENT, "get_info: NULL argument");
     *info = plan->info;
+    info->clears = plan->clears;
     return BILSTM_OK;
 }
 
@@ -801,16 +916,10 @@ bilstm_status bilstm_check(bilstm_plan *plan) {
     if (plan == nullptr) return fail(BILSTM_INVALID_ARGUMENT, "check: plan is NULL");
     DeviceScope scope(plan->device);
     BL_HIP(scope.error(), "check: hipSetDevice");
-    BL_HIP(hipDeviceSynchronize(), "check");
-    unsigned int flag = 0;
-    BL_HIP(hipMemcpy(&flag, plan->error, sizeof(flag), hipMemcpyDeviceToHost), "check");
-    if (flag != 0) {
-        BL_HIP(hipMemset(plan->error, 0, sizeof(unsigned int)), "check");
-        BL_HIP(hipDeviceSynchronize(), "check");
-        return fail(BILSTM_TIMEOUT, "check: a recurrence wait hit its %.3f ms watchdog; outputs are invalid",
-                    plan->watchdog_ms);
-    }
-    return BILSTM_OK;
+    // the plan's last call only: its completion event, after every join into the caller's
+    // stream (a never-recorded event is complete)
+    BL_HIP(hipEventSynchronize(plan->done), "check");
+    return take_timeout_report(plan, "check");
 }
 
 bilstm_status bilstm_set_phase_events(bilstm_plan *plan, int enable) {

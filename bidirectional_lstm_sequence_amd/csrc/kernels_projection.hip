@@ -500,7 +500,7 @@ __device__ __forceinline__ void wait_half(const ProjArgs &a, const StreamTile &t
         __builtin_amdgcn_s_sleep(2);
         if (half_ready(a, t, lane, __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), first)) break;
         if (wall_clock64() - t0 > a.timeout_ticks) {
-            atomicOr(a.error, 4u);
+            report_timeout(a.error, kErrProgress);
             timed_out = true;
             break;
         }

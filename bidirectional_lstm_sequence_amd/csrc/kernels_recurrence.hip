@@ -241,7 +241,7 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
             __builtin_amdgcn_s_sleep(1);
             if (published(read_ready(s))) break;
             if (wall_clock64() - t0 > a.timeout_ticks) {
-                atomicOr(a.error, 2u);
+                report_timeout(a.error, kErrCounter);
                 timed_out = true;
                 break;
             }
@@ -499,7 +499,7 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
                             w = load_word(wp);
                             if (static_cast<unsigned int>(w >> 32) == expect) break;
                             if (wall_clock64() - t0 > a.timeout_ticks) {
-                                atomicOr(a.error, 1u);
+                                report_timeout(a.error, kErrExchange);
                                 timed_out = true;
                                 break;
                             }

@@ -130,7 +130,13 @@ typedef struct {
                              Every wait on a counter is bounded by the watchdog like every other
                              wait: if the GPU is shared with other work that keeps a kernel from
                              running, bilstm_check reports BILSTM_TIMEOUT instead of hanging */
-    int32_t reserved[1];  /* must be zero */
+    int32_t near_wrap;    /* test hook for the clear paths: 1 = the flag epoch of the exchange
+                             words and the pass numbers of the streamed gates' counters and
+                             progress words start just below the values at which the plan clears
+                             those words and starts again from zero (the counters are filled to
+                             match), so the first forward runs with flags and counts near the top
+                             of their range and the second one runs the clears (speakrs 0.6.0,
+                             page `lstmproj.rs`, `clear_state`). 0 = off */
 } bilstm_options;
 
 /* What a plan chose; filled by bilstm_plan_get_info. */
@@ -162,6 +168,9 @@ typedef struct {
     int32_t stream_fused;    /* streamed gates: 1 when the four layers' recurrences run as one
                                 launch (pipeline = 4, concurrent = 2, recur_launches = 1); each
                                 workgroup then moves from a layer to the next by itself */
+    uint32_t clears;         /* times the plan has cleared its exchange words or its streamed
+                                counters and progress words since creation (before the 32-bit flag
+                                or pass space would wrap, or after a failed enqueue) */
 } bilstm_plan_info;
 
 /*
@@ -215,9 +224,16 @@ bilstm_status bilstm_recur(bilstm_plan *plan, int layer, const float *gates, siz
 bilstm_status bilstm_plan_get_info(const bilstm_plan *plan, bilstm_plan_info *info);
 
 /*
- * Wait for the plan's device work to finish and report whether any recurrence wait hit its
- * watchdog since the last check (BILSTM_TIMEOUT; the outputs of that call are then
- * garbage). Clears the flag. Blocks the calling thread.
+ * Wait until the work of the plan's last call (bilstm_forward, bilstm_project or bilstm_recur)
+ * has finished — an event the call recorded on its stream, so work of other streams is not
+ * waited for — and report whether a wait of any earlier call hit its watchdog
+ * (BILSTM_TIMEOUT: the outputs of the call that timed out are invalid). Clears the report.
+ * Blocks the calling thread.
+ *
+ * The kernels write a timeout report into host-mapped memory, so it reaches the caller
+ * without this call as well: bilstm_forward, bilstm_project and bilstm_recur first look at it
+ * and, if a wait of an earlier call on the plan has timed out and finished, clear the report
+ * and return BILSTM_TIMEOUT without enqueueing anything (the next call runs normally).
  */
 bilstm_status bilstm_check(bilstm_plan *plan);
 

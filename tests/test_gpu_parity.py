@@ -7,6 +7,7 @@ The projection alone is held to the rigorous fp32 dot-product bound
 
 import os
 import sys
+import time
 
 import numpy as np
 import pytest
@@ -45,9 +46,9 @@ def assert_close(got, ref, what):
     got = np.asarray(got, np.float64)
     err = np.abs(got - ref)
     bound = ATOL + RTOL * np.abs(ref)
-    bad = err > bound
+    bad = ~(err <= bound)  # NaN (an element never written) fails too
     if bad.any():
-        idx = np.unravel_index(np.argmax(err - bound), err.shape)
+        idx = np.unravel_index(np.argmax(np.where(bad, np.nan_to_num(err - bound, nan=np.inf), -np.inf)), err.shape)
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} elements outside tolerance; worst at "
                              f"{idx}: gpu {got[idx]!r} oracle {ref[idx]!r} (max abs err {err.max():.3e})")
     return float(err.max())
@@ -152,26 +153,57 @@ def run_stack(bl, x, layers, **kw):
     return out, info
 
 
-@pytest.mark.parametrize("name", ["b1", "b8", "b32"])
-def test_stack_matches_oracle_whole_batch(bl, orc, name):
-    x, layers = workloads.make_workload(name)
-    note(f"stack {name} shape={x.shape}")
-    got, info = run_stack(bl, x, layers)
-    ref = orc.stack(x, layers, threads=min(16, os.cpu_count() or 1))
-    err = assert_close(got, ref, name)
-    assert np.all(np.abs(got) <= 1.0)
-    note(f"stack {name} max abs err {err:.3e} plan {info}")
+def run_repeated(bl, x, layers, repeats=3, **kw):
+    """`repeats` forwards on one plan, each into an output filled with NaN first, so an element
+    a forward leaves unwritten cannot pass as stable or as close to the oracle."""
+    plan = bl.Plan(layers, x.shape[0], x.shape[1], **kw)
+    xd = torch.from_numpy(x).cuda()
+    outs = []
+    for _ in range(repeats):
+        y = torch.full((x.shape[0], x.shape[1], 256), float("nan"), dtype=torch.float32, device="cuda")
+        plan.forward(xd, y)
+        outs.append(y.cpu().numpy())
+    plan.check()
+    info = plan.info()
+    plan.close()
+    return outs, info
 
 
-@pytest.mark.parametrize("name,windows", [("b256", [0, 1, 10, 127, 200, 255]), ("b64_t4096", [0, 37])])
-def test_stack_matches_oracle_sampled_windows(bl, orc, name, windows):
-    """Full-size workloads in the default launch configuration; the oracle checks sampled windows."""
+THREADS = min(16, os.cpu_count() or 1)
+_REFERENCE = {}
+
+
+def oracle_reference(orc, name):
+    """The oracle's whole [B, T, 256] output of a workload (fp64), computed once per session."""
+    if name not in _REFERENCE:
+        x, layers = workloads.make_workload(name)
+        t0 = time.perf_counter()
+        _REFERENCE[name] = orc.stack(x, layers, threads=THREADS)
+        note(f"oracle {name}: {x.shape[0]} windows in {time.perf_counter() - t0:.1f} s on {THREADS} threads")
+    return _REFERENCE[name]
+
+
+ALL_WORKLOADS = ["b1", "b8", "b32", "b256", "b64_t4096"]
+
+
+def assert_bitwise_equal(runs, what):
+    for k, r in enumerate(runs[1:], 1):
+        same = r.view(np.uint32) == runs[0].view(np.uint32)
+        assert same.all(), f"{what}: forward {k} differs from forward 0 in {(~same).sum()} elements"
+
+
+@pytest.mark.parametrize("name", ALL_WORKLOADS)
+def test_stack_whole_output_matches_oracle_and_is_bit_stable(bl, orc, name):
+    """Every window of every workload, in the plan the library chooses by default (the launch
+    configuration the benchmark times): three forwards on one plan agree bit for bit, and
+    every element of the [B, T, 256] output is within tolerance of the fp64 oracle."""
     x, layers = workloads.make_workload(name)
-    note(f"stack {name} shape={x.shape} sampled windows={windows}")
-    got, info = run_stack(bl, x, layers)
-    ref = orc.stack(x, layers, windows=windows, threads=min(16, os.cpu_count() or 1))
-    err = assert_close(got[windows], ref, name)
-    assert np.all(np.abs(got) <= 1.0) and np.all(np.isfinite(got))
+    note(f"stack {name} shape={x.shape}: 3 forwards, whole output against the oracle")
+    runs, info = run_repeated(bl, x, layers)
+    assert_bitwise_equal(runs, name)
+    got = runs[0]
+    assert np.all(np.isfinite(got)) and np.all(np.abs(got) <= 1.0)
+    err = assert_close(got, oracle_reference(orc, name), name)
     note(f"stack {name} max abs err {err:.3e} plan {info}")
     if name == "b256":
         # every all-zero window (b % 10 == 0) gives bitwise the same output
@@ -179,33 +211,84 @@ def test_stack_matches_oracle_sampled_windows(bl, orc, name, windows):
         assert np.all(zeros.view(np.uint32) == zeros[0].view(np.uint32)[None])
 
 
-def test_stack_bit_stable_and_batch_invariant(bl):
+def test_stack_batch_invariant(bl):
+    """A window's output is bitwise the same alone, inside 8 windows and inside 32."""
     x, layers = workloads.make_workload("b32")
-    note("bit stability b32 x3, batch invariance b1/b8/b32")
-    plan = bl.Plan(layers, 32, x.shape[1])
-    xd = torch.from_numpy(x).cuda()
-    runs = [plan.forward(xd).cpu().numpy() for _ in range(3)]
-    plan.check()
-    plan.close()
-    for r in runs[1:]:
-        assert np.array_equal(r.view(np.uint32), runs[0].view(np.uint32))
+    note("batch invariance b1/b8/b32")
+    y32, _ = run_stack(bl, x, layers)
     y1, _ = run_stack(bl, np.ascontiguousarray(x[5:6]), layers)
     y8, _ = run_stack(bl, np.ascontiguousarray(x[:8]), layers)
-    assert np.array_equal(y1[0].view(np.uint32), runs[0][5].view(np.uint32))
-    assert np.array_equal(y8.view(np.uint32), runs[0][:8].view(np.uint32))
+    assert np.array_equal(y1[0].view(np.uint32), y32[5].view(np.uint32))
+    assert np.array_equal(y8.view(np.uint32), y32[:8].view(np.uint32))
 
 
-@pytest.mark.parametrize("name,windows", [("b8", None), ("b32", None), ("b256", [0, 3, 10, 255]),
-                                          ("b64_t4096", [5])])
-def test_stack_with_split_projection_matches_oracle(bl, orc, name, windows):
-    """Split-precision projections (bf16 x 3) keep the whole stack within the output tolerance."""
+@pytest.mark.parametrize("name", ALL_WORKLOADS)
+def test_stack_with_split_projection_matches_oracle(bl, orc, name):
+    """Split-precision projections (bf16 x 3) keep every element of the whole stack's output
+    within the output tolerance, bit-stable over three forwards."""
     x, layers = workloads.make_workload(name)
-    note(f"stack {name} projection=2 windows={windows}")
-    got, info = run_stack(bl, x, layers, projection=2)
+    note(f"stack {name} projection=2: 3 forwards, whole output against the oracle")
+    runs, info = run_repeated(bl, x, layers, projection=2)
     assert info["projection"] == 2
-    ref = orc.stack(x, layers, windows=windows, threads=min(16, os.cpu_count() or 1))
-    err = assert_close(got if windows is None else got[windows], ref, f"{name} split projection")
+    assert_bitwise_equal(runs, f"{name} split projection")
+    err = assert_close(runs[0], oracle_reference(orc, name), f"{name} split projection")
     note(f"stack {name} projection=2 max abs err {err:.3e}")
+
+
+EXCHANGE_SPLITS = [(2, 1), (2, 2), (2, 4), (4, 1), (4, 2), (4, 4)]
+
+
+@pytest.mark.parametrize("groups,tile", EXCHANGE_SPLITS)
+def test_exchange_stack_matches_oracle_over_repeated_forwards(bl, orc, groups, tile):
+    """The whole four-layer stack with KG workgroups per tile exchanging h through flagged
+    words. Each layer's flags start above the previous layer's and each pass's above the last
+    pass's, so three forwards on one plan run flag_base = epoch + layer·T over twelve layer
+    passes: all three agree bit for bit, match the oracle, and equal the single-workgroup
+    default (every split sums in the same order)."""
+    x, layers = workloads.make_workload("b8")
+    note(f"exchange stack b8 groups={groups} tile={tile}: 3 forwards")
+    runs, info = run_repeated(bl, x, layers, groups=groups, tile=tile)
+    assert info["recur_groups"] == groups and info["recur_tile"] == tile
+    assert_bitwise_equal(runs, f"groups={groups} tile={tile}")
+    err = assert_close(runs[0], oracle_reference(orc, "b8"), f"b8 groups={groups} tile={tile}")
+    base, _ = run_stack(bl, x, layers)
+    assert np.array_equal(runs[0].view(np.uint32), base.view(np.uint32))
+    note(f"exchange stack b8 groups={groups} tile={tile} max abs err {err:.3e} plan {info}")
+
+
+def test_serial_directions_b256_match_oracle(bl, orc):
+    """b256 with four workgroups per one-window tile: 2048 workgroups, twice what the device
+    keeps resident, so the two directions run one after the other. The whole output matches
+    the oracle and equals the default plan bit for bit."""
+    x, layers = workloads.make_workload("b256")
+    note("serial directions b256 groups=4 tile=1")
+    got, info = run_stack(bl, x, layers, groups=4, tile=1)
+    note(f"serial-direction plan {info}")
+    assert info["concurrent"] == 0
+    err = assert_close(got, oracle_reference(orc, "b256"), "b256 groups=4 tile=1")
+    base, _ = run_stack(bl, x, layers)
+    assert np.array_equal(got.view(np.uint32), base.view(np.uint32))
+    note(f"serial directions b256 max abs err {err:.3e}")
+
+
+@pytest.mark.parametrize("batch,steps,groups,tile", [(384, 96, 4, 1), (520, 40, 4, 1), (520, 40, 2, 1),
+                                                     (1024, 24, 4, 2)])
+def test_multi_launch_schedule_matches_oracle(bl, orc, batch, steps, groups, tile):
+    """More workgroups per direction than the device keeps resident: each direction's
+    recurrence is cut into several launches, run serially, each over its own tiles. Three
+    forwards on one plan (each layer of each pass takes its own flag range) agree bit for
+    bit, match the oracle and equal the default plan."""
+    layers = workloads.make_layers(91)
+    x = workloads.make_input(92 + batch, batch, steps)
+    note(f"multi-launch batch={batch} steps={steps} groups={groups} tile={tile}: 3 forwards")
+    runs, info = run_repeated(bl, x, layers, groups=groups, tile=tile)
+    note(f"multi-launch plan {info}")
+    assert info["recur_launches"] > 1
+    assert_bitwise_equal(runs, f"multi-launch b{batch}")
+    err = assert_close(runs[0], orc.stack(x, layers, threads=THREADS), f"multi-launch b{batch}")
+    base, _ = run_stack(bl, x, layers)
+    assert np.array_equal(runs[0].view(np.uint32), base.view(np.uint32))
+    note(f"multi-launch batch={batch} launches={info['recur_launches']} max abs err {err:.3e}")
 
 
 def test_split_projection_batch_invariant(bl):
@@ -289,8 +372,96 @@ def test_watchdog_reports_timeout_and_grid_drains(bl, concurrent):
     with pytest.raises(bl.BilstmError) as e:
         plan.check()
     assert e.value.name == "BILSTM_TIMEOUT"
-    plan.check()  # the flag was cleared
+    plan.check()  # the report was cleared
     plan.close()
+
+
+@pytest.mark.parametrize("pipeline,groups", [(1, 4), (2, 1)])
+def test_timeout_reaches_the_next_forward_without_check(bl, pipeline, groups):
+    """A forward whose waits time out (forced) returns OK when it enqueues; once it has run, the
+    next forward on the plan returns BILSTM_TIMEOUT by itself, without bilstm_check, enqueues
+    nothing, and clears the report, so the forward after it is accepted again."""
+    x, layers = workloads.make_workload("b8")
+    xs = torch.from_numpy(np.ascontiguousarray(x[:, :64])).cuda()
+    note(f"timeout without check: pipeline={pipeline} groups={groups}")
+    plan = bl.Plan(layers, 8, 64, groups=groups, tile=1, pipeline=pipeline, watchdog_us=-1)
+    try:
+        y = torch.zeros((8, 64, 256), dtype=torch.float32, device="cuda")
+        plan.forward(xs, y)
+        torch.cuda.synchronize()  # the caller waits on its own stream only
+        marker = torch.full_like(y, 7.0)
+        with pytest.raises(bl.BilstmError) as e:
+            plan.forward(xs, marker)
+        assert e.value.name == "BILSTM_TIMEOUT" and "earlier call" in str(e.value)
+        torch.cuda.synchronize()
+        assert bool(torch.all(marker == 7.0)), "a forward that reported a timeout enqueued work"
+        plan.forward(xs, y)  # accepted again
+        torch.cuda.synchronize()
+        with pytest.raises(bl.BilstmError) as e:
+            plan.check()
+        assert e.value.name == "BILSTM_TIMEOUT"
+    finally:
+        plan.close()
+
+
+def test_check_waits_for_the_plan_only(bl):
+    """bilstm_check waits for the plan's last call, not for the device: work pending on another
+    stream is still running when it returns."""
+    x, layers = workloads.make_workload("b8")
+    xs = torch.from_numpy(np.ascontiguousarray(x[:, :100])).cuda()
+    plan = bl.Plan(layers, 8, 100)
+    try:
+        # calibrate torch's spin kernel: cycles per millisecond on this device
+        probe = torch.cuda.Stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(probe):
+            e0.record()
+            torch.cuda._sleep(10_000_000)
+            e1.record()
+        probe.synchronize()
+        per_ms = 10_000_000 / max(e0.elapsed_time(e1), 1e-3)
+        note(f"check scope: spin kernel {per_ms:.0f} cycles/ms")
+        other = torch.cuda.Stream()
+        y = torch.empty((8, 100, 256), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(other):
+            torch.cuda._sleep(int(per_ms * 1500))  # about 1.5 s
+        t0 = time.perf_counter()
+        plan.forward(xs, y)
+        plan.check()
+        waited = time.perf_counter() - t0
+        busy = not other.query()
+        other.synchronize()
+        note(f"check scope: check returned after {waited * 1e3:.1f} ms; other stream still busy: {busy}")
+        assert busy and waited < 1.0
+    finally:
+        plan.close()
+
+
+@pytest.mark.parametrize("groups,pipeline", [(1, 2), (1, 4), (1, 3), (4, 1), (2, 1)])
+def test_near_wrap_counters_clear_and_stay_bitwise(bl, groups, pipeline):
+    """Flags and pass numbers started just below their clear thresholds (test hook): the first
+    forward runs with values at the top of their range, the second clears the exchange words
+    (groups > 1) or the streamed counters and progress words (pipeline 2-4) and starts from
+    zero. Four forwards agree bit for bit with a plan that never came near a wrap."""
+    x, layers = workloads.make_workload("b8")
+    xs = np.ascontiguousarray(x[:, :150])
+    note(f"near wrap groups={groups} pipeline={pipeline}")
+    plan = bl.Plan(layers, 8, 150, groups=groups, tile=1, pipeline=pipeline, near_wrap=1)
+    xd = torch.from_numpy(xs).cuda()
+    try:
+        outs, clears = [], []
+        for _ in range(4):
+            outs.append(plan.forward(xd).cpu().numpy())
+            clears.append(plan.info()["clears"])
+        plan.check()
+    finally:
+        plan.close()
+    note(f"near wrap groups={groups} pipeline={pipeline}: clears after each forward {clears}")
+    assert clears[0] == 0 and clears[1] == 1 and clears[-1] == 1
+    base, _ = run_stack(bl, xs, layers, groups=groups, tile=1, pipeline=pipeline)
+    for o in outs:
+        assert np.array_equal(o.view(np.uint32), base.view(np.uint32))
 
 
 def test_forward_rejects_bad_buffers(bl):
