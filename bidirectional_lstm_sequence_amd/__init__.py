@@ -32,7 +32,7 @@ EXPORTS = ["bilstm_plan_create", "bilstm_plan_create_ex", "bilstm_forward", "bil
            "bilstm_recur", "bilstm_plan_get_info", "bilstm_check", "bilstm_set_phase_events",
            "bilstm_phase_times", "bilstm_destroy", "bilstm_last_error", "bilstm_pack_layer",
            "bilstm_schedule", "bilstm_probe_exchange", "bilstm_heads_create", "bilstm_heads_forward",
-           "bilstm_heads_destroy"]
+           "bilstm_heads_destroy", "bilstm_forward_noalloc"]
 HEAD_IN, HEAD_MID, HEAD_CLASSES = 256, 128, 7
 
 
@@ -125,6 +125,8 @@ def library():
         "bilstm_heads_create": ([ctypes.c_int, ctypes.POINTER(HeadWeights), ctypes.POINTER(P)], st),
         "bilstm_heads_forward": ([P, P, ctypes.c_size_t, P, ctypes.c_size_t, P], st),
         "bilstm_heads_destroy": ([P], None),
+        "bilstm_forward_noalloc": ([ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(Layer), P,
+                                    ctypes.c_size_t, P, ctypes.c_size_t, P], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -364,6 +366,42 @@ class Plan:
 
     def __exit__(self, *exc):
         self.close()
+
+
+def device_layers(layers, device="cuda") -> list[dict]:
+    """The four layer dicts of ``Plan`` as contiguous float32 tensors on ``device``, for
+    ``forward_noalloc`` (a copy; nothing computed)."""
+    import torch
+    return [{k: torch.from_numpy(_f32(l[k])).to(device) for k in ("w", "r", "b")} for l in layers]
+
+
+def forward_noalloc(layers, x, y, stream=None, device: int = 0) -> None:
+    """The whole stack without a plan and without allocating (bilstm_forward_noalloc).
+
+    ``layers``: four dicts of contiguous float32 device tensors ``w [2,512,in]``, ``r [2,512,128]``,
+    ``b [2,2,512]`` (see ``device_layers``); ``x [B,T,60]`` and ``y [B,T,256]`` float32 device
+    tensors, ``y`` written. Only marshals pointers: no tensor is created here.
+    """
+    import torch
+    if len(layers) != LAYERS:
+        raise ValueError(f"expected {LAYERS} layers, got {len(layers)}")
+    batch, steps = int(x.shape[0]), int(x.shape[1])
+    arr = (Layer * LAYERS)()
+    for k, l in enumerate(layers):
+        width = FEATURES if k == 0 else WIDTH
+        for name, shape in (("w", (2, GATES, width)), ("r", (2, GATES, HIDDEN)), ("b", (2, 2, GATES))):
+            t = l[name]
+            if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+                raise TypeError(f"layer {k} {name} must be a contiguous float32 device tensor")
+            if tuple(t.shape) != shape:
+                raise ValueError(f"layer {k} {name} has shape {tuple(t.shape)}, expected {shape}")
+        arr[k] = Layer(ctypes.cast(l["w"].data_ptr(), ctypes.POINTER(ctypes.c_float)), l["w"].numel(),
+                       ctypes.cast(l["r"].data_ptr(), ctypes.POINTER(ctypes.c_float)), l["r"].numel(),
+                       ctypes.cast(l["b"].data_ptr(), ctypes.POINTER(ctypes.c_float)), l["b"].numel())
+    xp = _dev_ptr(x, "x", (batch, steps, FEATURES))
+    yp = _dev_ptr(y, "y", (batch, steps, WIDTH))
+    _check(library().bilstm_forward_noalloc(device, batch, steps, arr, xp, x.numel(), yp, y.numel(),
+                                            _stream_handle(stream)))
 
 
 def gate_column(direction: int, unit: int, gate: int) -> int:

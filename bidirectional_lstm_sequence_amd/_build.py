@@ -14,7 +14,8 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 OBJ_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["host_plan.cpp", "host_pack_schedule.cpp", "host_heads.cpp", "host_library_projection.cpp",
-           "kernels_projection.hip", "kernels_recurrence.hip", "kernels_heads.hip"]
+           "kernels_projection.hip", "kernels_recurrence.hip", "kernels_heads.hip",
+           "forward_noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

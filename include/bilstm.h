@@ -261,6 +261,30 @@ void bilstm_destroy(bilstm_plan *plan);
 /* Text of the last error recorded on the calling thread ("" if none). */
 const char *bilstm_last_error(void);
 
+/* ---- the stack without a plan, for callers that cannot allocate ------------------- */
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. The whole stack, as bilstm_forward computes it, with
+ * no plan: this call allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *   layers  the four layers' weights as DEVICE pointers on `device` (same layout and lengths as
+ *           bilstm_layer; read only, 4-byte aligned)
+ *   x       [batch][steps][60]  device, fp32, 16-byte aligned; x_len = batch·steps·60
+ *   y       [batch][steps][256] device, fp32, 16-byte aligned; y_len = batch·steps·256; also the
+ *           inter-layer buffer (updated in place layer by layer); must not overlap x
+ * Its scratch — the packed weights (repacked from `layers` by every call) and the gate
+ * pre-activations — is one static device array of 96 MiB per device, taken by the first call
+ * on that device and held until the process ends, so batch·steps is limited to 23,227 rows
+ * (e.g. 39 windows of 589 frames); larger calls return BILSTM_DIMENSION_OVERFLOW. Calls that
+ * overlap on one device race on that array (serialize them, e.g. on one stream); calls on
+ * different devices do not. Runs the projection and the single-workgroup recurrence on
+ * `stream`, both directions per layer in one launch; the output is bitwise the same as a
+ * plan's bilstm_forward for the same inputs.
+ */
+bilstm_status bilstm_forward_noalloc(int device, uint32_t batch, uint32_t steps,
+                                     const bilstm_layer layers[BILSTM_LAYERS], const float *x, size_t x_len,
+                                     float *y, size_t y_len, void *stream);
+
 /* ---- segmentation heads after the stack ------------------------------------------- */
 
 /*
