@@ -55,5 +55,28 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+MODEL_SOURCE = os.path.join(CSRC, "protocol_model.cpp")
+MODEL_LIB = os.path.join(PKG, "libbilstm_protocol_model.so")
+
+
+def build_protocol_model(out_path: str = MODEL_LIB, source_dir: str = CSRC, extra=(), main: bool = False) -> str:
+    """Compile the CPU model of the publication protocols (host only, g++).
+
+    ``source_dir`` holds protocol_model.cpp and the protocol.h it includes (the tests compile
+    copies with planted mistakes); ``main`` builds the stand-alone driver executable instead of
+    the shared library; ``extra`` adds flags (e.g. ``-fsanitize=thread``)."""
+    src = os.path.join(source_dir, "protocol_model.cpp")
+    kind = ["-DBILSTM_MODEL_MAIN"] if main else ["-shared", "-fPIC"]
+    tmp = out_path + ".tmp"
+    cmd = ["g++", "-O2", "-g", "-std=c++17", "-pthread", "-Wall", "-Wextra", *kind, *extra,
+           "-I", source_dir, src, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"g++ failed for the protocol model:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, out_path)
+    return out_path
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_protocol_model())

@@ -7,6 +7,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "protocol.h"
+
 namespace bl {
 
 constexpr int kHidden = 128;               // H
@@ -177,7 +179,7 @@ struct HeadArgs {
 // waits for stream_near(c) of direction d before its first half and stream_far(c) of the other
 // before its second: the first halves are ready early in layer l, and at its end only the
 // second halves of the first chunks are left.
-constexpr int kReadyPerPass = kGates / 32;
+static_assert(kReadyPerPass == kGates / 32, "a pass adds width / 32 per tile over 512 columns");
 // Tiles of chunk 0 per 128 gate columns: as many as keep every one of them in the first round
 // of `workgroups` persistent projection workgroups (1, 2 or 4).
 inline int stream_split(int groups, int workgroups) {

@@ -18,13 +18,6 @@ namespace bl {
 namespace {
 thread_local std::string g_last_error;
 
-// Streamed gates: pass counts above which the counters and progress words are cleared and the
-// counts start again from zero. A counter holds kReadyPerPass per pass (a 32-bit word, compared
-// wrap-safely against its target, so it must stay far from 2^32 / kReadyPerPass passes); a
-// progress word holds the layer pass in its upper 32 bits.
-constexpr uint32_t kReadyPassLimit = 0x03FFFFFFu;
-constexpr uint32_t kLayerPassLimit = 0x0FFFFFF0u;
-
 // Watchdog of a recurrence wait, in milliseconds. A step normally takes microseconds; the
 // limit only has to end a wait whose producer can never arrive.
 constexpr double kWatchdogMs = 2000.0;
@@ -240,13 +233,15 @@ bilstm_status reserve_flags(bilstm_plan *p, uint32_t count, hipStream_t stream, 
         *base = 0;
         return BILSTM_OK;
     }
-    if (static_cast<uint64_t>(p->epoch) + count + 1 > 0xFFFFFFFFull) {
+    uint32_t epoch = p->epoch;
+    bool clear = false;
+    const uint32_t first = reserve_flag_range(epoch, count, clear);
+    if (clear) {
         BL_HIP(launch_exchange_clear(p->exchange, p->exchange_words, stream), "exchange clear");
-        p->epoch = 0;
         ++p->clears;
     }
-    *base = p->epoch;
-    p->epoch += count;
+    p->epoch = epoch;
+    *base = first;
     return BILSTM_OK;
 }
 
@@ -291,7 +286,7 @@ bilstm_status enqueue_projection(bilstm_plan *p, int layer, const float *x, floa
             // the previous layer's recurrence, running now, still writes the input: each tile
             // waits for its rows
             args.progress = p->progress;
-            args.progress_pass = static_cast<unsigned long long>(p->layer_pass - 1) << 32;
+            args.progress_pass = progress_pass_bits(p->layer_pass - 1);
         }
     }
     BL_HIP(launch_projection(args, workgroups, stream), "projection launch");
@@ -324,9 +319,9 @@ RecurArgs recurrence_args(const bilstm_plan *p, int layer, const float *gates, f
         base.group_windows = kProjTileM / s.stream_chunk;
         base.groups = p->stream_groups;
         // a forced timeout expects a count no pass reaches
-        base.ready_target = p->ready_passes[buffer] * static_cast<unsigned int>(kReadyPerPass) + p->flag_skew;
+        base.ready_target = ready_target(p->ready_passes[buffer], p->flag_skew);
         base.progress = p->progress;
-        base.progress_pass = static_cast<unsigned long long>(p->layer_pass) << 32;
+        base.progress_pass = progress_pass_bits(p->layer_pass);
     }
     return base;
 }
@@ -387,8 +382,7 @@ bilstm_status enqueue_recurrence(bilstm_plan *p, int layer, const float *gates, 
 // projection reads.
 bilstm_status forward_streamed(bilstm_plan *p, const float *x, float *y, hipStream_t stream, uint32_t base) {
     bilstm_status st;
-    if (p->ready_dirty || p->layer_pass > kLayerPassLimit || p->ready_passes[0] > kReadyPassLimit ||
-        p->ready_passes[1] > kReadyPassLimit) {
+    if (stream_counters_need_clear(p->layer_pass, p->ready_passes, p->ready_dirty)) {
         // counters out of step with the pass counts (a failed enqueue), or close to wrapping
         BL_HIP(launch_exchange_clear(p->ready, 2 * p->ready_words, stream), "counter clear");
         BL_HIP(launch_exchange_clear(p->progress, kProgressStride * 2 * static_cast<size_t>(p->batch), stream),
@@ -555,6 +549,9 @@ bilstm_status take_timeout_report(bilstm_plan *p, const char *context) {
     for (int k = 0; k < kErrWords; ++k) seen |= words[k] != 0 ? 1u << k : 0u;
     if (seen == 0) return BILSTM_OK;
     for (int k = 0; k < kErrWords; ++k) words[k] = 0;
+    // a pass that timed out may have left its counters or progress words out of step with the
+    // pass counts: the next streamed pass clears them first
+    if (seen & ((1u << kErrCounter) | (1u << kErrProgress))) p->ready_dirty = true;
     return fail(BILSTM_TIMEOUT,
                 "%s: a wait of an earlier call on this plan hit its %.3f ms watchdog (%s%s%s); that call's "
                 "outputs are invalid; nothing was enqueued",
@@ -830,7 +827,7 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
         p->layer_pass = kLayerPassLimit - (kLayers - 1);
         if (p->ready != nullptr) {
             e = hipMemsetD32(reinterpret_cast<hipDeviceptr_t>(p->ready),
-                             static_cast<int>((kReadyPassLimit - 1) * static_cast<uint32_t>(kReadyPerPass)),
+                             static_cast<int>(ready_target(kReadyPassLimit - 1, 0)),
                              4 * p->ready_words);
         }
     }

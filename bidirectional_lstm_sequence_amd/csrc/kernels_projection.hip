@@ -485,7 +485,7 @@ __device__ __forceinline__ bool half_ready(const ProjArgs &a, const StreamTile &
                                           bool first) {
     if (watched_word(a, t, lane) == nullptr || ((lane & 1) == t.dir) != first) return true;
     const int need = first ? stream_near(a.steps, a.chunk, t.c) : stream_far(a.steps, a.chunk, t.c);
-    return seen >= (a.progress_pass | static_cast<unsigned int>(need));
+    return progress_reached(seen, a.progress_pass, static_cast<uint32_t>(need));
 }
 
 // Wait until the first (second) half of the tile's rows exists; the wave goes on when all its

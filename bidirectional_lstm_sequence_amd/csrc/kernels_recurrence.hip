@@ -223,7 +223,7 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
     auto read_ready = [&](int s) -> unsigned int {
         return __hip_atomic_load(ready_ptr(s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-    auto published = [&](unsigned int v) { return static_cast<int>(v - a.ready_target) >= 0; };
+    auto published = [&](unsigned int v) { return chunk_published(v, a.ready_target); };
     // The counter read one group ahead: even lanes read the chunk of step s, odd lanes the one
     // after. The per-lane address keeps the value in a vector register across the group (a
     // value the compiler sees as uniform would be moved to a scalar register at once, which
@@ -259,7 +259,7 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
             if (win0 + b < a.batch) {
-                __hip_atomic_store(progress_tile + kProgressStride * 2 * b, progress_pass | done, __ATOMIC_RELAXED,
+                __hip_atomic_store(progress_tile + kProgressStride * 2 * b, progress_word(progress_pass, done), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
             }
         }
@@ -450,12 +450,10 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
 
         // h to LDS for the next step (lanes of one window write the same value)
         hs[nxt][hidx(ug * BT + qe)] = hval;
-        const unsigned int flag = a.flag_base + static_cast<unsigned int>(s) + 1u;
+        const unsigned int flag = exchange_flag(a.flag_base, s);
         if constexpr (KG > 1) {
             if (q < BT) {
-                const unsigned long long word =
-                    (static_cast<unsigned long long>(flag) << 32) | __float_as_uint(hval);
-                store_word(xdir + (static_cast<size_t>(cur) * kHidden + ug) * BT + q, word);
+                store_word(xdir + exchange_index(s, ug, q, kHidden, BT), exchange_word(flag, __float_as_uint(hval)));
             }
         }
 
@@ -485,19 +483,18 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
             } else {
                 // (4) gather the other workgroups' h of step s
                 constexpr int kOthers = (kHidden - U) * BT;
-                const unsigned long long *xs = xdir + static_cast<size_t>(cur) * kHidden * BT;
                 const unsigned int expect = flag + a.flag_skew;
                 for (int idx = tid - 64; idx < kOthers; idx += NT - 64) {
                     const int uo = idx / BT;
                     const int b = idx - uo * BT;
                     const int ugo = uo < member * U ? uo : uo + U;
-                    const unsigned long long *wp = xs + static_cast<size_t>(ugo) * BT + b;
+                    const unsigned long long *wp = xdir + exchange_index(s, ugo, b, kHidden, BT);
                     unsigned long long w = load_word(wp);
-                    if (static_cast<unsigned int>(w >> 32) != expect && !timed_out) {
+                    if (word_flag(w) != expect && !timed_out) {
                         const unsigned long long t0 = wall_clock64();
                         while (true) {
                             w = load_word(wp);
-                            if (static_cast<unsigned int>(w >> 32) == expect) break;
+                            if (word_flag(w) == expect) break;
                             if (wall_clock64() - t0 > a.timeout_ticks) {
                                 report_timeout(a.error, kErrExchange);
                                 timed_out = true;
@@ -505,7 +502,7 @@ __device__ __forceinline__ void recurrence_layer(const RecurArgs &a, bool &timed
                             }
                         }
                     }
-                    hs[nxt][hidx(ugo * BT + b)] = __uint_as_float(static_cast<unsigned int>(w));
+                    hs[nxt][hidx(ugo * BT + b)] = __uint_as_float(word_value(w));
                 }
             }
         }

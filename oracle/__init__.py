@@ -41,6 +41,15 @@ def build(force: bool = True) -> str:
     return compile_library(_SOURCES[0], LIB_PATH)
 
 
+def build_check(out_path: str) -> str:
+    """The oracle with AddressSanitizer and UndefinedBehaviorSanitizer, linked with its
+    stand-alone driver (check_main.c), which runs every routine on small shapes."""
+    cmd = ["gcc", "-O1", "-g", "-std=c11", "-Wall", "-Wextra", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-o", out_path, os.path.join(_HERE, "check_main.c"), _SOURCES[0], "-lm"]
+    subprocess.run(cmd, check=True, cwd=_HERE)
+    return out_path
+
+
 def use_library(path: str | None) -> None:
     """Route the functions below to another build of the oracle (None: the default one).
 
