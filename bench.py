@@ -61,11 +61,12 @@ def kernel_source_digest() -> str:
 def recorded_traffic(workload: str, info: dict):
     """HBM bytes per recurrence launch from the rocprofv3 counters recorded in profiles/.
 
-    Returns (bytes, detail): bytes only if the counters were taken on this kernel source,
-    workload and launch configuration, else None. Counter collection runs kernels one at a
-    time, so the streamed recurrence (which waits for a projection running beside it) cannot
-    be counted; its unstreamed twin, which reads the same gates and writes the same outputs,
-    is recorded instead and reported in the detail as a proxy."""
+    Returns (bytes, detail), or (None, None) unless the counters were taken on this kernel
+    source, workload, kernel (streamed or not) and recurrence split. Counter collection runs
+    kernels one at a time, so the streamed recurrence is counted in the streamed plan without
+    layer overlap (the next layer's projection starts after this layer's recurrence, so no
+    kernel waits for one that starts after it); the recurrence kernel, its gates and its outputs
+    are the same as in the default streamed plan."""
     path = os.path.join(ROOT, "profiles", "recurrence_traffic.json")
     try:
         with open(path) as f:
@@ -73,32 +74,55 @@ def recorded_traffic(workload: str, info: dict):
     except (OSError, ValueError):
         return None, None
     if (rec.get("source_sha256") != kernel_source_digest() or rec.get("workload") != workload
-            or rec.get("concurrent") != info["concurrent"] or rec.get("groups") != info["recur_groups"]
-            or rec.get("tile") != info["recur_tile"]):
+            or rec.get("streamed") != bool(info["pipeline"]) or rec.get("groups") != info["recur_groups"]
+            or rec.get("tile") != info["recur_tile"] or rec.get("concurrent") != info["concurrent"]):
         return None, None
     detail = {"bytes_per_launch": rec["fetch_bytes"] + rec["write_bytes"], "fetch_bytes": rec["fetch_bytes"],
-              "write_bytes": rec["write_bytes"], "kernel": rec["kernel"],
-              "windows_per_launch": rec["windows_per_launch"], "source": "profiles/recurrence_traffic.json"}
-    same = rec.get("slices") == info["slices"] and rec.get("pipeline", 0) == info["pipeline"]
-    if not same:
-        detail["note"] = ("proxy: the unstreamed recurrence of one layer under --pmc; the timed launch is the "
-                          "streamed kernel, which counter collection (kernels one at a time) cannot run")
-    return (detail["bytes_per_launch"] if same else None), detail
+              "write_bytes": rec["write_bytes"], "algorithmic_bytes": rec.get("algorithmic_bytes"),
+              "kernel": rec["kernel"], "windows_per_launch": rec["windows_per_launch"],
+              "counter_run": rec["command"], "source": "profiles/recurrence_traffic.json"}
+    return detail["bytes_per_launch"], detail
 
 
 def cpu_baseline(x, layers, steps, max_threads=16, target_windows=None):
+    """The oracle (fp64, unchanged) on the host: the all-threads rate over a bounded sample of
+    windows, and the single-core rate of its single-threaded routine on one window."""
     import oracle
     oracle.build(force=False)
-    threads = max(1, min(max_threads, os.cpu_count() or 1))
+    host_cores = os.cpu_count() or 1
+    threads = max(1, min(max_threads, host_cores))
     windows = target_windows or min(x.shape[0], 2 * threads)
     idx = list(range(windows))
     t0 = time.perf_counter()
     oracle.stack(x, layers, windows=idx, threads=threads)
     wall = time.perf_counter() - t0
     used = min(threads, windows)
+    t1 = time.perf_counter()
+    oracle.stack(x, layers, windows=[0], threads=1)
+    one = time.perf_counter() - t1
     return {"value": windows * steps / wall, "unit": "frames/s", "cores": used, "kind": "oracle",
             "sample": f"{windows} of the {x.shape[0]} windows ({windows * steps} frames), one window per "
-                      f"task on {used} threads, fp64 single-threaded routine per window; wall {wall:.2f} s"}
+                      f"task on {used} threads, fp64 single-threaded routine per window; wall {wall:.2f} s",
+            "host_cores": host_cores,
+            "single_core": {"value": steps / one, "unit": "frames/s", "sample": f"window 0 ({steps} frames) on "
+                            f"one thread; wall {one:.2f} s"}}
+
+
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
+
+
+def split_bf16_rates(split: dict) -> dict:
+    """The split-precision projection runs three bf16 products per FP32 product: its rate in
+    bf16 MFMA flops, against the bf16 dense peak (its own dtype's), beside the FP32-equivalent
+    rate in `achieved_tflops`."""
+    if "achieved_tflops" not in split:
+        return {}
+    bf16 = 3.0 * split["achieved_tflops"]
+    return {"note": "achieved_tflops and frac: FP32-equivalent flops over time against the FP32 MFMA peak; "
+                    "bf16_tflops and frac_of_bf16_peak: the 3 bf16 products per FP32 one that the matrix "
+                    "pipes run, against the bf16 dense peak",
+            "bf16_tflops": bf16, "bf16_peak_tflops": PEAK_BF16_MFMA_TFLOPS,
+            "frac_of_bf16_peak": bf16 / PEAK_BF16_MFMA_TFLOPS}
 
 
 def main() -> int:
@@ -113,8 +137,9 @@ def main() -> int:
     ap.add_argument("--slices", type=int, default=0)
     ap.add_argument("--projection", type=int, default=0, choices=(0, 1, 2),
                     help="0 own FP32-MFMA kernel (default), 1 vendor GEMM, 2 own split-precision kernel")
-    ap.add_argument("--pipeline", type=int, default=0, choices=(0, 1, 2, 3, 4),
-                    help="streamed gates: 0 auto, 1 off, 2 on, 3 on without and 4 on with layer overlap")
+    ap.add_argument("--pipeline", type=int, default=0, choices=(0, 1, 2, 3, 4, 5),
+                    help="streamed gates: 0 auto, 1 off, 2 on, 3 on without and 4 on with layer overlap, "
+                         "5 on with every kernel after the previous one (for counter collection)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -177,16 +202,27 @@ def main() -> int:
     value = frames * args.steps / (total_ms / 1e3)
     timed_phases = plan.phase_times()
 
-    # The recurrence launch bracketed by the plan's events in the last timed forward (the first
-    # slice's launch when the batch runs in slices): the dominant kernel's duration. With the
-    # four streamed recurrences in one launch, the four values are that launch's per-layer
-    # shares and add up to its duration.
+    # The dominant kernel's average launch duration over the timed region. With streamed gates
+    # every recurrence launch runs on the caller's stream, back to back (each waits inside for
+    # its first chunk; the projections run on the plan's own stream), so the two HIP events that
+    # bracket the timed region, on that stream, hold exactly the forwards' recurrence launches:
+    # their average is the region's time over the launches in it (an upper bound: it includes
+    # the few microseconds between launches). Otherwise (projections and recurrences alternate
+    # on the stream) the launch bracketed by the plan's phase events in the last timed forward.
     fused = bool(info["stream_fused"])
     layers_per_launch = 4 if fused else 1
-    if fused:
-        launch_dur_ms = sum(timed_phases["recurrence_launch_ms"])
+    launches_per_forward = 1 if fused else 4
+    events_ms = (sum(timed_phases["recurrence_launch_ms"]) if fused
+                 else statistics.mean(timed_phases["recurrence_launch_ms"]))
+    back_to_back = bool(info["pipeline"]) and info["concurrent"] == 2 and info["recur_launches"] == 1 \
+        and info["slices"] == 1
+    if back_to_back:
+        launch_dur_ms = total_ms / args.steps / launches_per_forward
+        launch_source = (f"timed region over its {args.steps * launches_per_forward} recurrence launches (HIP events "
+                         "on the caller's stream, where they run back to back)")
     else:
-        launch_dur_ms = statistics.mean(timed_phases["recurrence_launch_ms"])
+        launch_dur_ms = events_ms
+        launch_source = "the plan's HIP events around the launch in the last timed forward"
     slice_windows = info["slice_windows"] if info["slices"] > 1 else wl.batch
     launch_dirs = 2 if info["concurrent"] == 2 else 1
     flop_per_launch = layers_per_launch * launch_dirs * recurrence_flops_per_layer(slice_windows * wl.steps) / 2
@@ -307,6 +343,8 @@ def main() -> int:
                      "frac": rec_tflops / PEAK_FP32_VECTOR_TFLOPS,
                      "traffic": traffic,
                      "launch_ms": launch_dur_ms,
+                     "launch_ms_source": launch_source,
+                     "launch_ms_last_forward_events": events_ms,
                      "flop_per_launch": flop_per_launch,
                      "layers_per_launch": layers_per_launch,
                      "windows_per_launch": slice_windows,
@@ -319,8 +357,7 @@ def main() -> int:
                        "tflops_per_layer": proj_layer_tflops,
                        "peak_tflops": PEAK_FP32_MFMA_TFLOPS, "frac": proj_tflops / PEAK_FP32_MFMA_TFLOPS},
         "projection_vendor_gemm": library_projection,
-        "projection_split_bf16x3": dict(split_projection, note="FP32-equivalent flops over time; "
-                                        "the matrix pipes run 3 bf16 products per FP32 one"),
+        "projection_split_bf16x3": dict(split_projection, **split_bf16_rates(split_projection)),
         "heads": {"ms": heads_med, "achieved_tflops": heads_tflops, "peak_tflops": PEAK_FP32_MFMA_TFLOPS,
                   "frac": heads_tflops / PEAK_FP32_MFMA_TFLOPS,
                   "hbm_gbs": HEAD_BYTES_PER_FRAME * frames / (heads_med / 1e3) / 1e9,

@@ -81,7 +81,8 @@ class PlanInfo(ctypes.Structure):
                 ("slice_windows", ctypes.c_int32), ("projection", ctypes.c_int32),
                 ("pipeline", ctypes.c_int32), ("stream_chunk", ctypes.c_int32),
                 ("stream_overlap", ctypes.c_int32), ("stream_split", ctypes.c_int32),
-                ("stream_fused", ctypes.c_int32), ("clears", ctypes.c_uint32)]
+                ("stream_fused", ctypes.c_int32), ("stream_serial", ctypes.c_int32),
+                ("clears", ctypes.c_uint32)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -273,7 +274,7 @@ class Plan:
     2 through the library's split-precision kernel; ``pipeline`` streams each layer's gates
     from its projection into its recurrence while both run (0 = auto, 1 = off, 2 = on, 3 = on with
     each projection after the previous layer's recurrence, 4 = on with the next layer's projection
-    during this layer's recurrence); ``near_wrap`` = 1 starts the plan's flag epoch and pass
+    during this layer's recurrence, 5 = as 3 with every kernel after the previous one); ``near_wrap`` = 1 starts the plan's flag epoch and pass
     counters just below the values at which it clears them (a test hook for the clear paths).
     """
 

@@ -49,8 +49,8 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
         if (opt->near_wrap != 0 && opt->near_wrap != 1) {
             return fail(BILSTM_INVALID_ARGUMENT, "options: near_wrap %d is not 0 or 1", opt->near_wrap);
         }
-        if (opt->pipeline < 0 || opt->pipeline > 4) {
-            return fail(BILSTM_INVALID_ARGUMENT, "options: pipeline %d is not one of 0..4", opt->pipeline);
+        if (opt->pipeline < 0 || opt->pipeline > 5) {
+            return fail(BILSTM_INVALID_ARGUMENT, "options: pipeline %d is not one of 0..5", opt->pipeline);
         }
         if (opt->projection < 0 || opt->projection > 2) {
             return fail(BILSTM_INVALID_ARGUMENT, "options: projection %d is not 0, 1 or 2", opt->projection);
@@ -192,7 +192,8 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
     // The next layer's projection starts during this layer's recurrence unless asked not to
     // (3): measured faster both where the recurrence sets the pace (b32: 1.44 -> 1.39 ms) and
     // where the projection does (b64_t4096: 10.45 -> 10.32 ms).
-    info->stream_overlap = pipeline && want_pipe != 3 ? 1 : 0;
+    info->stream_overlap = pipeline && want_pipe != 3 && want_pipe != 5 ? 1 : 0;
+    info->stream_serial = pipeline && want_pipe == 5 ? 1 : 0;
     // 4: the four layers' recurrences as one launch, when one launch holds both directions of
     // every tile. Not the default: a layer boundary waits for the next layer's first chunk
     // either way, which outlasts a kernel launch, and a launch per layer measured faster

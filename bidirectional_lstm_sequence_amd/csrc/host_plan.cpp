@@ -83,6 +83,7 @@ struct bilstm_plan {
     hipEvent_t proj_fork = nullptr;
     hipEvent_t proj_join = nullptr;
     hipEvent_t layer_done[kLayers] = {nullptr, nullptr, nullptr, nullptr};  // no layer overlap
+    hipEvent_t proj_done[kLayers] = {nullptr, nullptr, nullptr, nullptr};   // kernels one at a time
     float *ybuf = nullptr;                 // [rows][256]: output of layers 0 and 2
     float *gates_odd = nullptr;            // [rows][1024]: gates of layers 1 and 3
     // chunk counters of the two gate buffers (two per word): buffer b at b·ready_words
@@ -195,6 +196,7 @@ void release(bilstm_plan *p) {
     if (p->proj_join) (void)hipEventDestroy(p->proj_join);
     for (int l = 0; l < kLayers; ++l) {
         if (p->layer_done[l]) (void)hipEventDestroy(p->layer_done[l]);
+        if (p->proj_done[l]) (void)hipEventDestroy(p->proj_done[l]);
     }
     if (p->proj_stream) (void)hipStreamDestroy(p->proj_stream);
     if (p->ybuf) (void)hipFree(p->ybuf);
@@ -429,6 +431,11 @@ bilstm_status forward_streamed(bilstm_plan *p, const float *x, float *y, hipStre
             return st;
         }
         if (p->phase_events) BL_HIP(hipEventRecord(p->ev_proj[l], p->proj_stream), "phase event");
+        if (p->info.stream_serial) {
+            // kernels one at a time: this layer's recurrence after its whole projection
+            BL_HIP(hipEventRecord(p->proj_done[l], p->proj_stream), "projection event");
+            BL_HIP(hipStreamWaitEvent(stream, p->proj_done[l], 0), "projection wait");
+        }
         if (one_launch) {
             RecurArgs &a = stack.layer[l];
             a = recurrence_args(p, l, gates, out, base + l * p->steps, true, buffer);
@@ -807,6 +814,7 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
         if (e == hipSuccess) e = hipEventCreateWithFlags(&p->proj_join, hipEventDisableTiming);
         for (int l = 0; l < kLayers && e == hipSuccess; ++l) {
             e = hipEventCreateWithFlags(&p->layer_done[l], hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&p->proj_done[l], hipEventDisableTiming);
         }
         // Each recurrence workgroup claims enough LDS that no projection workgroup fits beside
         // it, and each streamed projection workgroup enough that no second one shares its CU:

@@ -126,7 +126,11 @@ typedef struct {
                              projection starting during this layer's recurrence; 3 = on, with it
                              starting after this layer's recurrence; 4 = as 2, with the four
                              layers' recurrences as one launch where possible
-                             (bilstm_plan_info.stream_fused), not a launch per layer.
+                             (bilstm_plan_info.stream_fused), not a launch per layer; 5 = as 3,
+                             and each layer's recurrence also starts only after that layer's
+                             projection has finished: the same streamed kernels run one at a
+                             time (for profilers that serialize kernels, e.g. counter
+                             collection), none of them ever waiting for another.
                              Every wait on a counter is bounded by the watchdog like every other
                              wait: if the GPU is shared with other work that keeps a kernel from
                              running, bilstm_check reports BILSTM_TIMEOUT instead of hanging */
@@ -168,6 +172,7 @@ typedef struct {
     int32_t stream_fused;    /* streamed gates: 1 when the four layers' recurrences run as one
                                 launch (pipeline = 4, concurrent = 2, recur_launches = 1); each
                                 workgroup then moves from a layer to the next by itself */
+    int32_t stream_serial;   /* streamed gates: 1 when pipeline = 5 (kernels one at a time) */
     uint32_t clears;         /* times the plan has cleared its exchange words or its streamed
                                 counters and progress words since creation (before the 32-bit flag
                                 or pass space would wrap, or after a failed enqueue) */

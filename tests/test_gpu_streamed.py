@@ -65,19 +65,21 @@ SHAPES = [(1, 589, 0), (1, 1, 0), (1, 129, 0), (2, 130, 0), (2, 65, 0), (3, 150,
           (64, 70, 0), (96, 40, 0)]
 
 
-@pytest.mark.parametrize("pipeline", [2, 4, 3])
+@pytest.mark.parametrize("pipeline", [2, 4, 3, 5])
 @pytest.mark.parametrize("batch,steps,tile", SHAPES)
 def test_streamed_equals_unstreamed_bitwise(bl, batch, steps, tile, pipeline):
     """pipeline 2: the next layer's projection runs during this layer's recurrence, reading the
     rows it publishes; 4: the same with the four recurrences as one launch; 3: each projection
-    after the previous layer's recurrence."""
+    after the previous layer's recurrence; 5: as 3, each recurrence after its projection (the
+    streamed kernels one at a time)."""
     x = workloads.make_input(40 + batch, batch, steps)
     layers = workloads.make_layers(41)
     note(f"streamed (pipeline={pipeline}) vs unstreamed batch={batch} steps={steps} tile={tile}")
     got, info = run(bl, x, layers, pipeline=pipeline, tile=tile)
     base, binfo = run(bl, x, layers, pipeline=1, slices=1, tile=tile)
     assert info["pipeline"] == 1 and binfo["pipeline"] == 0
-    assert info["stream_overlap"] == (0 if pipeline == 3 else 1)
+    assert info["stream_overlap"] == (0 if pipeline in (3, 5) else 1)
+    assert info["stream_serial"] == (1 if pipeline == 5 else 0)
     one_launch = info["concurrent"] == 2 and info["recur_launches"] == 1
     assert info["stream_fused"] == (1 if pipeline == 4 and one_launch else 0)
     assert np.array_equal(got[0].view(np.uint32), base[0].view(np.uint32))

@@ -195,12 +195,15 @@ def test_schedule_forced_streaming_checks_its_conditions(bl):
 
 @pytest.mark.parametrize("batch,steps,pipeline,overlap", [
     (32, 589, 0, 1), (16, 589, 0, 1), (64, 4096, 0, 1), (96, 589, 0, 1), (32, 589, 3, 0), (64, 4096, 4, 1),
-    (8, 589, 2, 1), (1, 589, 2, 1), (32, 589, 1, 0), (8, 589, 0, 1), (4, 589, 0, 1), (1, 589, 0, 1)])
+    (8, 589, 2, 1), (1, 589, 2, 1), (32, 589, 1, 0), (8, 589, 0, 1), (4, 589, 0, 1), (1, 589, 0, 1),
+    (32, 589, 5, 0), (64, 4096, 5, 0)])
 def test_schedule_layer_overlap(bl, batch, steps, pipeline, overlap):
     """Streamed gates overlap the next layer's projection with this layer's recurrence unless
-    pipeline = 3 asks for each projection after the previous recurrence."""
+    pipeline = 3 asks for each projection after the previous recurrence (or 5, which also runs
+    each recurrence after its projection)."""
     s = bl.schedule(batch, steps, 256, 1, pipeline=pipeline)
     assert s["stream_overlap"] == overlap
+    assert s["stream_serial"] == (1 if pipeline == 5 else 0)
     assert s["pipeline"] == (1 if pipeline != 1 else 0)
 
 
@@ -237,7 +240,7 @@ def test_schedule_first_chunk_split(bl, batch, steps, cus, split):
     (dict(groups=3), "BILSTM_UNSUPPORTED"), (dict(tile=3), "BILSTM_UNSUPPORTED"),
     (dict(concurrent=5), "BILSTM_INVALID_ARGUMENT"), (dict(slices=9), "BILSTM_INVALID_ARGUMENT"),
     (dict(slices=-1), "BILSTM_INVALID_ARGUMENT"), (dict(projection=3), "BILSTM_INVALID_ARGUMENT"),
-    (dict(projection=-1), "BILSTM_INVALID_ARGUMENT"), (dict(pipeline=5), "BILSTM_INVALID_ARGUMENT"),
+    (dict(projection=-1), "BILSTM_INVALID_ARGUMENT"), (dict(pipeline=6), "BILSTM_INVALID_ARGUMENT"),
     (dict(pipeline=-1), "BILSTM_INVALID_ARGUMENT")])
 def test_schedule_rejects_bad_options(bl, kwargs, status):
     with pytest.raises(bl.BilstmError) as e:
