@@ -111,16 +111,16 @@ def cpu_baseline(x, layers, steps, max_threads=16, target_windows=None):
 PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
 
 
-def split_bf16_rates(split: dict) -> dict:
-    """The split-precision projection runs three bf16 products per FP32 product: its rate in
+def split_bf16_rates(split: dict, products: int) -> dict:
+    """A split-precision projection runs `products` bf16 products per FP32 product: its rate in
     bf16 MFMA flops, against the bf16 dense peak (its own dtype's), beside the FP32-equivalent
     rate in `achieved_tflops`."""
     if "achieved_tflops" not in split:
         return {}
-    bf16 = 3.0 * split["achieved_tflops"]
+    bf16 = products * split["achieved_tflops"]
     return {"note": "achieved_tflops and frac: FP32-equivalent flops over time against the FP32 MFMA peak; "
-                    "bf16_tflops and frac_of_bf16_peak: the 3 bf16 products per FP32 one that the matrix "
-                    "pipes run, against the bf16 dense peak",
+                    f"bf16_tflops and frac_of_bf16_peak: the {products} bf16 products per FP32 one that the "
+                    "matrix pipes run, against the bf16 dense peak",
             "bf16_tflops": bf16, "bf16_peak_tflops": PEAK_BF16_MFMA_TFLOPS,
             "frac_of_bf16_peak": bf16 / PEAK_BF16_MFMA_TFLOPS}
 
@@ -135,8 +135,9 @@ def main() -> int:
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--concurrent", type=int, default=-1)
     ap.add_argument("--slices", type=int, default=0)
-    ap.add_argument("--projection", type=int, default=0, choices=(0, 1, 2),
-                    help="0 own FP32-MFMA kernel (default), 1 vendor GEMM, 2 own split-precision kernel")
+    ap.add_argument("--projection", type=int, default=0, choices=(0, 1, 2, 3, 4),
+                    help="0 the plan's rule (default), 1 vendor GEMM, 2 and 3 own split-precision kernel "
+                         "(two or three bf16 parts), 4 own FP32-MFMA kernel")
     ap.add_argument("--pipeline", type=int, default=0, choices=(0, 1, 2, 3, 4, 5),
                     help="streamed gates: 0 auto, 1 off, 2 on, 3 on without and 4 on with layer overlap, "
                          "5 on with every kernel after the previous one (for counter collection)")
@@ -276,6 +277,7 @@ def main() -> int:
                                      for k, v in zip((60, 256, 256, 256), med)]}
     library_projection = other_projection(1)
     split_projection = other_projection(2)
+    split3_projection = other_projection(3)
 
     # the fused segmentation heads after the stack, alone, on this workload's stack output
     heads = bl.Heads(workloads.make_heads(wl.seed))
@@ -325,7 +327,9 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if args.projection != 2 else "f32 (projection: bf16x3 split)",
+        "dtype": {1: "f32", 2: "f32 (projection: two-part bf16 split, 3 products, FP32 accumulate)",
+                  3: "f32 (projection: three-part bf16 split, 6 products, FP32 accumulate)",
+                  4: "f32"}[info["projection"]],
         "data": "synthetic: seeded U(-1/sqrt(128), 1/sqrt(128)) weights, N(0,1) input windows",
         "config": {"workload": f"{wl.name}: {wl.batch} windows x {wl.steps} frames, 4-layer BiLSTM "
                                f"H=128, input 60", "batch": wl.batch, "seq_len": wl.steps,
@@ -353,11 +357,14 @@ def main() -> int:
                             "frac_of_bound": bound_us / us_per_step, "exchange_one_way_ns": xchg_ns,
                             "bound_terms": f"FMA {fma_clk:.0f} clk at {FMA_PER_CLK_PER_CU} FMA/clk/CU, "
                                            f"{CLOCK_GHZ} GHz" + (" + one exchange" if groups > 1 else "")},
-        "projection": {"ms_total": proj_total_ms, "ms_per_layer": proj_med, "achieved_tflops": proj_tflops,
+        "projection": {"mode": {2: "split, two bf16 parts", 3: "split, three bf16 parts",
+                                4: "FP32 MFMA"}.get(info["projection"], str(info["projection"])),
+                       "ms_total": proj_total_ms, "ms_per_layer": proj_med, "achieved_tflops": proj_tflops,
                        "tflops_per_layer": proj_layer_tflops,
                        "peak_tflops": PEAK_FP32_MFMA_TFLOPS, "frac": proj_tflops / PEAK_FP32_MFMA_TFLOPS},
         "projection_vendor_gemm": library_projection,
-        "projection_split_bf16x3": dict(split_projection, **split_bf16_rates(split_projection)),
+        "projection_split_bf16x3": dict(split_projection, **split_bf16_rates(split_projection, 3)),
+        "projection_split_bf16x6": dict(split3_projection, **split_bf16_rates(split3_projection, 6)),
         "heads": {"ms": heads_med, "achieved_tflops": heads_tflops, "peak_tflops": PEAK_FP32_MFMA_TFLOPS,
                   "frac": heads_tflops / PEAK_FP32_MFMA_TFLOPS,
                   "hbm_gbs": HEAD_BYTES_PER_FRAME * frames / (heads_med / 1e3) / 1e9,

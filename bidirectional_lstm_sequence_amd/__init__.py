@@ -269,9 +269,10 @@ class Plan:
     and ``b [2,2,512]`` (PyTorch nn.LSTM layout, gate rows i, f, g, o; b = [Wb, Rb]).
     ``groups``, ``tile`` and ``concurrent`` override the plan's recurrence split;
     ``watchdog_us`` bounds each recurrence wait (0 = 2 s); ``slices`` sets how many batch
-    slices the forward runs as concurrent chains (0 = auto, 1 = off); ``projection`` = 1 runs
-    the input projection through the vendor GEMM (hipBLASLt) instead of the library's kernel,
-    2 through the library's split-precision kernel; ``pipeline`` streams each layer's gates
+    slices the forward runs as concurrent chains (0 = auto, 1 = off); ``projection`` picks the
+    input projection: 0 the plan's rule (the three-part split where it is accurate and on the
+    critical path, else FP32), 1 the vendor GEMM (hipBLASLt), 2 and 3 the library's
+    split-precision kernel with two or three bf16 parts, 4 the library's FP32 kernel; ``pipeline`` streams each layer's gates
     from its projection into its recurrence while both run (0 = auto, 1 = off, 2 = on, 3 = on with
     each projection after the previous layer's recurrence, 4 = on with the next layer's projection
     during this layer's recurrence, 5 = as 3 with every kernel after the previous one); ``near_wrap`` = 1 starts the plan's flag epoch and pass

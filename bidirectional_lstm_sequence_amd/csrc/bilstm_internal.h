@@ -36,6 +36,13 @@ constexpr int kAutoSlices = 2;
 
 inline int padded_input(int in) { return (in + kProjTileK - 1) / kProjTileK * kProjTileK; }
 
+// bilstm_options.projection values
+constexpr int kProjectionAuto = 0;    // the plan's rule (host_pack_schedule.cpp)
+constexpr int kProjectionVendor = 1;  // hipBLASLt, FP32 compute (comparator)
+constexpr int kProjectionSplit2 = 2;  // two bf16 parts, three products
+constexpr int kProjectionSplit3 = 3;  // three bf16 parts, six products
+constexpr int kProjectionFp32 = 4;    // FP32 MFMA products
+
 // Factor of each gate's pre-activation in the exponent of its activation, by gate (i, f, g,
 // o): σ(a) = 1/(1 + 2^(-a·log2 e)) and tanh(a) = 2/(1 + 2^(-2a·log2 e)) - 1. The plan stores the
 // recurrent rows multiplied by these factors (rounded to fp32).
@@ -67,6 +74,8 @@ struct ProjArgs {
     const float *w;      // [1024][kpad]
     const __bf16 *w_hi;  // split-precision mode: [1024][kpad] bf16(w), else nullptr
     const __bf16 *w_lo;  //                       [1024][kpad] bf16(w - bf16(w))
+    const __bf16 *w_lo2; // three parts: [1024][kpad] bf16 of what the first two leave, else nullptr
+    int split_parts;     // 0: FP32 MFMA; 2 or 3: bf16 parts (the streamed kernel splits W itself)
     const float *bias;   // [1024]
     float *gates;        // [rows][1024]
     int rows;

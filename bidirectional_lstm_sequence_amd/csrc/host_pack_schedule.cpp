@@ -33,6 +33,60 @@ bilstm_status pack_layer(const bilstm_layer &layer, int in, float *w_out, float 
     return BILSTM_OK;
 }
 
+// ---- the projection rule ------------------------------------------------------------------
+//
+// The input projection runs either as FP32 MFMA products or split into three bf16 parts per
+// operand with six bf16 MFMA products (speakrs 0.6.0, page `lstmproj.rs`, `projection_rule`:
+// reduced-precision tensor projections only where enough rows amortize them and where they
+// were accurate enough on the device; `tf32_projection_accurate`: accurate means within 1.1x
+// the reference library's error against an f64 reference). Here the split is used only where
+// it is both accurate and faster for the forward:
+//  * accuracy: development checks on MI355X (the five synthetic workloads, whole outputs
+//    against the fp64 oracle) put the stack's largest error with the three-part split at 0.94
+//    to 0.98 times the FP32 kernel's (b8 0.98, b32 0.94, b256 0.95, b64_t4096 0.98), within
+//    the 1.1 factor; the two-part split measured 2.5 to 4.3 times and is never chosen;
+//  * amortization: at least kSplitMinRows projection rows, the pages' small-projection
+//    threshold (below it the FP32 kernel is kept);
+//  * speed: the projection must be on the forward's critical path. Unstreamed, it runs between
+//    the recurrences, so it always is. Streamed beside the recurrence, the FP32 kernel keeps up
+//    while each recurrence step asks at most kStreamFp32FlopPerCu flops of each CU the
+//    recurrence leaves (measured: about 0.40 TFLOP/s per CU beside a one-window step of about
+//    0.46 us); beyond that the layer runs at the projection's pace.
+// The rule is a function of the workload and the device only (the plan's schedule with every
+// option left to the plan), so every plan for one workload computes the same gates, whatever
+// its streaming, slices or recurrence split.
+constexpr unsigned long long kSplitMinRows = 2048;
+constexpr double kStreamFp32FlopPerCu = 184.0e3;
+
+// Whether the three-part split stayed within 1.1x the FP32 kernel's error on this device: every
+// workload the development checks ran on gfx950 did.
+static bool split_projection_accurate(uint32_t batch, uint32_t steps) {
+    (void)batch;
+    (void)steps;
+    return true;
+}
+
+static int auto_projection(uint32_t batch, uint32_t steps, int cu_count) {
+    const unsigned long long rows = static_cast<unsigned long long>(batch) * steps;
+    if (rows < kSplitMinRows || !split_projection_accurate(batch, steps)) return kProjectionFp32;
+    // the default recurrence schedule: one workgroup per tile and direction, each alone on a CU,
+    // the fewest windows per tile that let both directions fit the GPU at once
+    long long tiles = (static_cast<long long>(batch) + 3) / 4;
+    for (int t : {1, 2, 4}) {
+        const long long n = (static_cast<long long>(batch) + t - 1) / t;
+        if (2 * n <= cu_count) {
+            tiles = n;
+            break;
+        }
+    }
+    const long long rec_wgs = 2 * tiles;
+    const bool streamed = rec_wgs + 8 <= cu_count && 4 * rec_wgs <= 3LL * cu_count;
+    if (!streamed) return kProjectionSplit3;
+    const int free_cus = stream_projection_workgroups(cu_count, static_cast<int>(tiles), 1);
+    const double flop_per_step = 2.0 * kGateCols * kWidth * static_cast<double>(batch);
+    return flop_per_step / free_cus > kStreamFp32FlopPerCu ? kProjectionSplit3 : kProjectionFp32;
+}
+
 static bool valid_groups(int g) { return g == 1 || g == 2 || g == 4; }
 static bool valid_tile(int t) { return t == 1 || t == 2 || t == 4; }
 
@@ -52,8 +106,9 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
         if (opt->pipeline < 0 || opt->pipeline > 5) {
             return fail(BILSTM_INVALID_ARGUMENT, "options: pipeline %d is not one of 0..5", opt->pipeline);
         }
-        if (opt->projection < 0 || opt->projection > 2) {
-            return fail(BILSTM_INVALID_ARGUMENT, "options: projection %d is not 0, 1 or 2", opt->projection);
+        if (opt->projection < 0 || opt->projection > kProjectionFp32) {
+            return fail(BILSTM_INVALID_ARGUMENT, "options: projection %d is not one of 0..%d", opt->projection,
+                        kProjectionFp32);
         }
         if (opt->slices < 0 || opt->slices > kMaxSlices) {
             return fail(BILSTM_INVALID_ARGUMENT, "options: slices %d is not in 0..%d", opt->slices, kMaxSlices);
@@ -123,21 +178,22 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
     }
 
     const int want_slices = (opt != nullptr) ? opt->slices : 0;
-    const int projection = (opt != nullptr) ? opt->projection : 0;
+    const int want_projection = (opt != nullptr) ? opt->projection : kProjectionAuto;
+    const int projection = want_projection != kProjectionAuto ? want_projection : auto_projection(batch, steps, cu_count);
 
     // Streamed gates: each layer's projection runs beside its own recurrence, on the CUs the
     // recurrence leaves free (every recurrence workgroup keeps a CU to itself), and never waits
     // for it; only the recurrence waits, for chunks the projection publishes. The projection
     // needs CUs of its own (8 at least), single-workgroup tiles (no cross-workgroup waits in
-    // the recurrence besides the counters) and the library's own FP32 kernel.
+    // the recurrence besides the counters) and one of the library's own kernels (FP32 or split).
     const int want_pipe = (opt != nullptr) ? opt->pipeline : 0;
     const long long rec_wgs = 2 * grid;
-    const bool pipe_possible = groups == 1 && projection == 0 && want_slices <= 1 && rec_wgs + 8 <= cu_count;
+    const bool pipe_possible = groups == 1 && projection != kProjectionVendor && want_slices <= 1 && rec_wgs + 8 <= cu_count;
     bool pipeline = false;
     if (want_pipe >= 2) {
         if (!pipe_possible) {
             return fail(BILSTM_UNSUPPORTED,
-                        "schedule: streamed gates need recur_groups = 1, projection = 0, slices <= 1 and at "
+                        "schedule: streamed gates need recur_groups = 1, the library's own projection, slices <= 1 and at "
                         "least 8 CUs beside the recurrence's %lld workgroups (%d CUs)", rec_wgs, cu_count);
         }
         pipeline = true;
@@ -163,13 +219,13 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
     if (pipeline) {
         // the streamed projection already runs beside the recurrence
     } else if (want_slices > 1) {
-        if (groups != 1 || concurrent == 1 || projection == 1) {
+        if (groups != 1 || concurrent == 1 || projection == kProjectionVendor) {
             return fail(BILSTM_UNSUPPORTED,
                         "schedule: %d slices need recur_groups = 1, concurrent != 1 and the library's own "
                         "projection", want_slices);
         }
         slices = want_slices;
-    } else if (want_slices == 0 && groups == 1 && concurrent != 1 && projection != 1) {
+    } else if (want_slices == 0 && groups == 1 && concurrent != 1 && projection != kProjectionVendor) {
         // auto: slice when the recurrence leaves at least half of the CUs idle
         if (2 * grid * 2 <= cu_count && static_cast<long long>(batch) >= 2LL * tile) slices = kAutoSlices;
     }

@@ -55,6 +55,7 @@ struct bilstm_plan {
     float *bias[kLayers] = {nullptr, nullptr, nullptr, nullptr};
     uint16_t *w_hi[kLayers] = {nullptr, nullptr, nullptr, nullptr};  // split precision: bf16(w)
     uint16_t *w_lo[kLayers] = {nullptr, nullptr, nullptr, nullptr};  //   bf16(w - bf16(w))
+    uint16_t *w_lo2[kLayers] = {nullptr, nullptr, nullptr, nullptr}; //   three parts: the third
     float *gates = nullptr;
     unsigned long long *exchange = nullptr;
     size_t exchange_words = 0;
@@ -178,6 +179,7 @@ void release(bilstm_plan *p) {
         if (p->bias[l]) (void)hipFree(p->bias[l]);
         if (p->w_hi[l]) (void)hipFree(p->w_hi[l]);
         if (p->w_lo[l]) (void)hipFree(p->w_lo[l]);
+        if (p->w_lo2[l]) (void)hipFree(p->w_lo2[l]);
         if (p->fork[l]) (void)hipEventDestroy(p->fork[l]);
         if (p->join[l]) (void)hipEventDestroy(p->join[l]);
         if (p->ev_proj[l]) (void)hipEventDestroy(p->ev_proj[l]);
@@ -264,6 +266,8 @@ bilstm_status enqueue_projection(bilstm_plan *p, int layer, const float *x, floa
     args.w = p->w[layer];
     args.w_hi = reinterpret_cast<const __bf16 *>(p->w_hi[layer]);
     args.w_lo = reinterpret_cast<const __bf16 *>(p->w_lo[layer]);
+    args.w_lo2 = reinterpret_cast<const __bf16 *>(p->w_lo2[layer]);
+    args.split_parts = p->info.projection == kProjectionSplit2 ? 2 : p->info.projection == kProjectionSplit3 ? 3 : 0;
     args.bias = p->bias[layer];
     args.gates = gates + row_first * kGateCols;
     args.rows = static_cast<int>(rows);
@@ -717,25 +721,32 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
         if (e != hipSuccess) {
             return fail_release(fail(BILSTM_HIP_ERROR, "plan_create: weight upload: %s", hipGetErrorString(e)));
         }
-        if (info.projection == 2) {
-            // split precision: w = hi + lo (+ a residual below 2^-16·|w|), both bf16
-            std::vector<uint16_t> hi(w.size()), lo(w.size());
+        if (info.projection == kProjectionSplit2 || info.projection == kProjectionSplit3) {
+            // split precision: w = part 0 + part 1 (+ part 2) + a residual below 2^-8P·|w|, each
+            // part the bf16 of what the earlier ones leave (every difference exact in fp32)
+            const int parts = info.projection == kProjectionSplit3 ? 3 : 2;
+            std::vector<uint16_t> plane[3];
+            for (int pl = 0; pl < parts; ++pl) plane[pl].resize(w.size());
             for (size_t i = 0; i < w.size(); ++i) {
-                hi[i] = bf16_rne(w[i]);
-                lo[i] = bf16_rne(w[i] - bf16_value(hi[i]));
+                float rest = w[i];
+                for (int pl = 0; pl < parts; ++pl) {
+                    plane[pl][i] = bf16_rne(rest);
+                    rest -= bf16_value(plane[pl][i]);
+                }
             }
-            if ((st = device_alloc(p, &p->w_hi[l], hi.size(), "W hi")) != BILSTM_OK) return fail_release(st);
-            if ((st = device_alloc(p, &p->w_lo[l], lo.size(), "W lo")) != BILSTM_OK) return fail_release(st);
-            e = hipMemcpy(p->w_hi[l], hi.data(), hi.size() * sizeof(uint16_t), hipMemcpyHostToDevice);
-            if (e == hipSuccess) e = hipMemcpy(p->w_lo[l], lo.data(), lo.size() * sizeof(uint16_t), hipMemcpyHostToDevice);
-            if (e != hipSuccess) {
-                return fail_release(fail(BILSTM_HIP_ERROR, "plan_create: weight upload: %s", hipGetErrorString(e)));
+            uint16_t **dst[3] = {&p->w_hi[l], &p->w_lo[l], &p->w_lo2[l]};
+            for (int pl = 0; pl < parts; ++pl) {
+                if ((st = device_alloc(p, dst[pl], plane[pl].size(), "W part")) != BILSTM_OK) return fail_release(st);
+                e = hipMemcpy(*dst[pl], plane[pl].data(), plane[pl].size() * sizeof(uint16_t), hipMemcpyHostToDevice);
+                if (e != hipSuccess) {
+                    return fail_release(fail(BILSTM_HIP_ERROR, "plan_create: weight upload: %s", hipGetErrorString(e)));
+                }
             }
         }
     }
 
     if ((st = device_alloc(p, &p->gates, rows * kGateCols, "gates")) != BILSTM_OK) return fail_release(st);
-    if (info.projection == 1) {
+    if (info.projection == kProjectionVendor) {
         if ((st = library_projection_create(static_cast<long>(rows), p->in, p->kpad, p->bias, &p->library)) !=
             BILSTM_OK) {
             return fail_release(st);

@@ -236,26 +236,33 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a)
 
 // ---- split-precision variant ---------------------------------------------------------------
 //
-// The same projection with every FP32 operand split into two bf16 parts, a = a_hi + a_lo
-// (a_hi = bf16(a), a_lo = bf16(a - a_hi), both round-to-nearest-even), and three bf16 MFMA
-// products per K chunk, hi·hi + hi·lo + lo·hi, accumulated in FP32 (a bf16 x bf16 product is
-// exact in FP32). The dropped lo·lo term and the two parts' residuals stay below
-// 3·2^-16·|x·w| per product, so
-//   |gates - exact| <= (3·2^-16·(1 + 2^-7) + (3K + 2)·2^-24) · sum_k |x_k w_k| (+ bias rounding).
-// W arrives already split (two [1024][kpad] bf16 planes, packed at plan creation); x is split
-// while staging into LDS. v_mfma_f32_32x32x16_bf16: lane l supplies row (or column) l % 32 and
-// eight consecutive k of half l / 32 of each 16-wide K chunk, for A and B alike.
+// The same projection with every FP32 operand split into bf16 parts and the products of the
+// parts accumulated in FP32 on the bf16 matrix cores (a bf16 x bf16 product is exact in FP32).
+// Each part is the round-to-nearest-even bf16 of what the earlier parts leave: a_0 = bf16(a),
+// a_1 = bf16(a - a_0), a_2 = bf16(a - a_0 - a_1) (each difference is exact in FP32), and each
+// part removes all but 2^-8 of the remainder, so after P parts |a - sum a_p| <= 2^-8P·|a|.
+//   PARTS = 2: three products per K chunk, a_0·b_0 + a_0·b_1 + a_1·b_0 (the dropped a_1·b_1 and
+//     the residuals stay below 3·2^-16·|a·b|):
+//     |gates - exact| <= (3·2^-16·(1 + 2^-7) + (3K + 2)·2^-24) · sum_k |x_k w_k|;
+//   PARTS = 3: six products, every a_p·b_q with p + q <= 2 (the dropped a_1·b_2, a_2·b_1,
+//     a_2·b_2 and the residuals stay below 4·2^-24·|a·b|(1 + 2^-7)): the truncation is then
+//     of the order of one FP32 rounding per product,
+//     |gates - exact| <= (4·2^-24·(1 + 2^-7) + (6K + 2)·2^-24) · sum_k |x_k w_k|.
+// W arrives already split (PARTS [1024][kpad] bf16 planes, packed at plan creation); x is
+// split while staging into LDS. v_mfma_f32_32x32x16_bf16: lane l supplies row (or column)
+// l % 32 and eight consecutive k of half l / 32 of each 16-wide K chunk, for A and B alike.
 constexpr int kSplitStride = BK + 8;  // LDS row stride, bf16 elements (80 bytes: conflict-free)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-template <int KSTEPS>
+template <int KSTEPS, int PARTS>
 __global__ __launch_bounds__(kProjThreads, 1) void projection_split_kernel(ProjArgs a) {
-    // [stage][hi, lo][row][k]
-    __shared__ __attribute__((aligned(16))) __bf16 lds_a[2][2][BM * kSplitStride];
-    __shared__ __attribute__((aligned(16))) __bf16 lds_b[2][2][BN * kSplitStride];
+    static_assert(PARTS == 2 || PARTS == 3, "two or three bf16 parts");
+    // [stage][part][row][k]
+    __shared__ __attribute__((aligned(16))) __bf16 lds_a[2][PARTS][BM * kSplitStride];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_b[2][PARTS][BN * kSplitStride];
 
     const int nwg = gridDim.x;  // a multiple of 8
     const int per_xcd = nwg >> 3;
@@ -267,11 +274,12 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_split_kernel(ProjA
     const int wave = tid >> 6;
     const int wm = wave >> 1;
     const int wn = wave & 1;
+    const __bf16 *const w_part[3] = {a.w_hi, a.w_lo, a.w_lo2};
 
     // x: 4 float4 per thread per K step (row f / 8, k 4·(f % 8)); W: per plane 2 x 16 bytes
     // (8 bf16) per thread (row f / 4, k 8·(f % 4))
     v4f ra[kLoadsPerThread];
-    u32x4 rb[2][2];  // [plane][i]
+    u32x4 rb[PARTS][2];  // [plane][i]
     auto load = [&](int m0, int n0, int k0) {
 #pragma unroll
         for (int j = 0; j < kLoadsPerThread; ++j) {
@@ -288,8 +296,8 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_split_kernel(ProjA
         for (int i = 0; i < 2; ++i) {
             const int f = tid + kProjThreads * i;
             const size_t off = static_cast<size_t>(n0 + (f >> 2)) * a.kpad + k0 + (f & 3) * 8;
-            rb[0][i] = *reinterpret_cast<const u32x4 *>(a.w_hi + off);
-            rb[1][i] = *reinterpret_cast<const u32x4 *>(a.w_lo + off);
+#pragma unroll
+            for (int pl = 0; pl < PARTS; ++pl) rb[pl][i] = *reinterpret_cast<const u32x4 *>(w_part[pl] + off);
         }
     };
     auto store = [&](int buf) {
@@ -297,30 +305,34 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_split_kernel(ProjA
         for (int j = 0; j < kLoadsPerThread; ++j) {
             const int f = tid + kProjThreads * j;
             const int off = (f / kThreadsPerRow) * kSplitStride + (f % kThreadsPerRow) * 4;
-            bf16x4 hi, lo;
+            bf16x4 part[PARTS];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                hi[e] = static_cast<__bf16>(ra[j][e]);
-                lo[e] = static_cast<__bf16>(ra[j][e] - static_cast<float>(hi[e]));
+                float rest = ra[j][e];
+#pragma unroll
+                for (int pl = 0; pl < PARTS; ++pl) {
+                    part[pl][e] = static_cast<__bf16>(rest);
+                    rest -= static_cast<float>(part[pl][e]);  // exact
+                }
             }
-            *reinterpret_cast<bf16x4 *>(&lds_a[buf][0][off]) = hi;
-            *reinterpret_cast<bf16x4 *>(&lds_a[buf][1][off]) = lo;
+#pragma unroll
+            for (int pl = 0; pl < PARTS; ++pl) *reinterpret_cast<bf16x4 *>(&lds_a[buf][pl][off]) = part[pl];
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int f = tid + kProjThreads * i;
             const int off = (f >> 2) * kSplitStride + (f & 3) * 8;
-            *reinterpret_cast<u32x4 *>(&lds_b[buf][0][off]) = rb[0][i];
-            *reinterpret_cast<u32x4 *>(&lds_b[buf][1][off]) = rb[1][i];
+#pragma unroll
+            for (int pl = 0; pl < PARTS; ++pl) *reinterpret_cast<u32x4 *>(&lds_b[buf][pl][off]) = rb[pl][i];
         }
     };
 
     const int frag_row = lane & 31;
     const int frag_k = (lane >> 5) * 8;
     // fragments of K chunk c (16 wide): [plane][block]
-    auto frags = [&](int buf, int c, bf16x8 (&af)[2][2], bf16x8 (&bf)[2][2]) {
+    auto frags = [&](int buf, int c, bf16x8 (&af)[PARTS][2], bf16x8 (&bf)[PARTS][2]) {
 #pragma unroll
-        for (int pl = 0; pl < 2; ++pl)
+        for (int pl = 0; pl < PARTS; ++pl)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 af[pl][t] = *reinterpret_cast<const bf16x8 *>(
@@ -347,10 +359,13 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_split_kernel(ProjA
         }
     };
 
+    // K steps in the order of kstep_at, as every projection kernel takes them (the streamed
+    // split kernel too, so streamed and unstreamed split gates are bitwise the same)
     int q = first;
     int base = 0;
     if (q < a.tiles) {
-        load((q / kColTiles) * BM, (q % kColTiles) * BN, 0);
+        const int n0 = (q % kColTiles) * BN;
+        load((q / kColTiles) * BM, n0, kstep_at<KSTEPS>(n0, 0) * BK);
         store(0);
     }
     __syncthreads();
@@ -374,13 +389,14 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_split_kernel(ProjA
             const int cur = (base + kt) & 1;
             const bool more = kt + 1 < KSTEPS;
             if (more) {
-                load(m0, n0, (kt + 1) * BK);
+                load(m0, n0, kstep_at<KSTEPS>(n0, kt + 1) * BK);
             } else if (next) {
-                load((qn / kColTiles) * BM, (qn % kColTiles) * BN, 0);
+                const int nn = (qn % kColTiles) * BN;
+                load((qn / kColTiles) * BM, nn, kstep_at<KSTEPS>(nn, 0) * BK);
             }
 #pragma unroll
             for (int c = 0; c < BK / 16; ++c) {
-                bf16x8 af[2][2], bf[2][2];
+                bf16x8 af[PARTS][2], bf[PARTS][2];
                 frags(cur, c, af, bf);
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
@@ -389,6 +405,11 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_split_kernel(ProjA
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bf[0][j], acc[i][j], 0, 0, 0);
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bf[1][j], acc[i][j], 0, 0, 0);
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bf[0][j], acc[i][j], 0, 0, 0);
+                        if constexpr (PARTS == 3) {
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bf[1][j], acc[i][j], 0, 0, 0);
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bf[2][j], acc[i][j], 0, 0, 0);
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[2][i], bf[0][j], acc[i][j], 0, 0, 0);
+                        }
                     }
                 if (c == 0 && have) put_chunk(kt);
             }
@@ -543,7 +564,24 @@ __device__ __forceinline__ void wait_steps_after(int n) {
     }
 }
 
-template <int KSTEPS>
+// Eight consecutive FP32 values (two LDS chunks) split into PARTS bf16 parts, each the bf16 of
+// what the earlier parts leave: the same parts the plain split kernel and the plan produce.
+template <int PARTS>
+__device__ __forceinline__ void split8(v4f lo, v4f hi, bf16x8 (&out)[PARTS]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float rest = e < 4 ? lo[e] : hi[e - 4];
+#pragma unroll
+        for (int pl = 0; pl < PARTS; ++pl) {
+            out[pl][e] = static_cast<__bf16>(rest);
+            rest -= static_cast<float>(out[pl][e]);  // exact
+        }
+    }
+}
+
+// PARTS = 0: FP32 MFMA products; 2 or 3: split precision as projection_split_kernel, the
+// FP32 operands split in registers after the LDS ring.
+template <int KSTEPS, int PARTS>
 __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(ProjArgs a) {
     __shared__ __attribute__((aligned(16))) float lds[kStages * kStageFloats];
     // K steps loaded ahead of the one being multiplied
@@ -703,6 +741,41 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
             const float *sb = sa + BM * BK;
             int fr = frag_row;
             asm volatile("" : "+v"(fr));
+            if constexpr (PARTS != 0) {
+                // two 16-wide K chunks; lane half h supplies k = 16c + 8h .. 16c + 8h + 7, the
+                // LDS chunks 4c + 2h and 4c + 2h + 1 of its row; the six (three) products of the
+                // parts in the order of projection_split_kernel
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int c0 = 4 * c + 2 * (lane >> 5);
+                    bf16x8 pa[NI][PARTS], pb[NJ][PARTS];
+#pragma unroll
+                    for (int i = 0; i < NI; ++i) {
+                        const int r = row0 + i * 32 + fr;
+                        split8<PARTS>(*reinterpret_cast<const v4f *>(&sa[swizzled(r, c0)]),
+                                      *reinterpret_cast<const v4f *>(&sa[swizzled(r, c0 + 1)]), pa[i]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        const int r = col0 + j * 32 + fr;
+                        split8<PARTS>(*reinterpret_cast<const v4f *>(&sb[swizzled(r, c0)]),
+                                      *reinterpret_cast<const v4f *>(&sb[swizzled(r, c0 + 1)]), pb[j]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < NI; ++i)
+#pragma unroll
+                        for (int j = 0; j < NJ; ++j) {
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i][0], pb[j][0], acc[i][j], 0, 0, 0);
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i][0], pb[j][1], acc[i][j], 0, 0, 0);
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i][1], pb[j][0], acc[i][j], 0, 0, 0);
+                            if constexpr (PARTS == 3) {
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i][1], pb[j][1], acc[i][j], 0, 0, 0);
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i][0], pb[j][2], acc[i][j], 0, 0, 0);
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i][2], pb[j][0], acc[i][j], 0, 0, 0);
+                            }
+                        }
+                }
+            } else {
             v4f af[2][NI], bf[2][NJ];
             auto frags = [&](int gq, v4f (&fa)[NI], v4f (&fb)[NJ]) {
                 const int c = 2 * gq + (lane >> 5);
@@ -728,6 +801,7 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
                         for (int j = 0; j < NJ; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[p][i][e], bf[p][j][e],
                                                                              acc[i][j], 0, 0, 0);
+            }
             }
             // the second half held back: after the first half's last products, wait for it
             // and load every step of it the ring has room for
@@ -813,30 +887,46 @@ hipError_t launch_projection(const ProjArgs &args, int workgroups, hipStream_t s
     int nwg = std::min(workgroups, (args.tiles + 7) / 8 * 8);
     nwg = std::max(8, nwg / 8 * 8);
     if (args.chunk > 0) {
-        // streamed order: FP32 kernel only
-        if (args.w_hi != nullptr || args.ready == nullptr ||
-            args.chunk * args.group_windows != kProjTileM || (1 << args.chunk_shift) != args.chunk) {
+        // streamed order: FP32 MFMA or split precision (W as FP32, split in registers)
+        if (args.ready == nullptr || args.chunk * args.group_windows != kProjTileM ||
+            (1 << args.chunk_shift) != args.chunk ||
+            (args.split_parts != 0 && args.split_parts != 2 && args.split_parts != 3)) {
             return hipErrorInvalidValue;
         }
-        switch (args.kpad / kProjTileK) {
-            case 2:
-                hipLaunchKernelGGL(projection_stream_kernel<2>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
-                break;
-            case 8:
-                hipLaunchKernelGGL(projection_stream_kernel<8>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
-                break;
+#define BL_STREAM(KS, PARTS) \
+    hipLaunchKernelGGL((projection_stream_kernel<KS, PARTS>), dim3(nwg), dim3(kProjThreads), 0, stream, args)
+        switch ((args.kpad / kProjTileK) * 4 + args.split_parts) {
+            case 2 * 4 + 0: BL_STREAM(2, 0); break;
+            case 2 * 4 + 2: BL_STREAM(2, 2); break;
+            case 2 * 4 + 3: BL_STREAM(2, 3); break;
+            case 8 * 4 + 0: BL_STREAM(8, 0); break;
+            case 8 * 4 + 2: BL_STREAM(8, 2); break;
+            case 8 * 4 + 3: BL_STREAM(8, 3); break;
             default:
                 return hipErrorInvalidValue;
         }
+#undef BL_STREAM
         return hipGetLastError();
     }
-    if (args.w_hi != nullptr) {
+    if (args.split_parts != 0) {
+        if (args.w_hi == nullptr || args.w_lo == nullptr || (args.split_parts == 3) != (args.w_lo2 != nullptr)) {
+            return hipErrorInvalidValue;
+        }
+        const bool three = args.split_parts == 3;
         switch (args.kpad / kProjTileK) {
             case 2:
-                hipLaunchKernelGGL(projection_split_kernel<2>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
+                if (three) {
+                    hipLaunchKernelGGL((projection_split_kernel<2, 3>), dim3(nwg), dim3(kProjThreads), 0, stream, args);
+                } else {
+                    hipLaunchKernelGGL((projection_split_kernel<2, 2>), dim3(nwg), dim3(kProjThreads), 0, stream, args);
+                }
                 break;
             case 8:
-                hipLaunchKernelGGL(projection_split_kernel<8>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
+                if (three) {
+                    hipLaunchKernelGGL((projection_split_kernel<8, 3>), dim3(nwg), dim3(kProjThreads), 0, stream, args);
+                } else {
+                    hipLaunchKernelGGL((projection_split_kernel<8, 2>), dim3(nwg), dim3(kProjThreads), 0, stream, args);
+                }
                 break;
             default:
                 return hipErrorInvalidValue;

@@ -100,14 +100,29 @@ typedef struct {
                              0 = auto (2 when the recurrence leaves at least half of the CUs
                              idle, else 1), 1 = off, at most 8 (beyond the process's hardware
                              queues, 4 by default, streams share queues and run one after
-                             another); needs recur_groups = 1, concurrent != 1 and
-                             projection = 0 */
-    int32_t projection;   /* input projection: 0 the library's own FP32-MFMA kernel (default);
-                             1 the vendor GEMM (hipBLASLt, FP32 compute, bias epilogue) as a
-                             comparator, run unsliced; 2 the own kernel in split precision:
-                             each FP32 operand split into two bf16 parts, three bf16 MFMA
-                             products per K chunk (hi·hi + hi·lo + lo·hi) accumulated in FP32,
-                             |error| <= (3·2^-16·(1 + 2^-7) + (3K + 2)·2^-24)·sum|x·w| per gate */
+                             another); needs recur_groups = 1, concurrent != 1 and the
+                             library's own projection (projection != 1) */
+    int32_t projection;   /* input projection:
+                             0 = the plan's rule (default; speakrs 0.6.0, page `lstmproj.rs`,
+                                 `projection_rule`): 3 where the split is accurate on this device
+                                 (development checks: within 1.1x the FP32 kernel's largest error
+                                 against an fp64 reference on every workload measured), at least
+                                 2048 projection rows amortize it and the projection is on the
+                                 forward's critical path (unstreamed, or streamed with more work per
+                                 recurrence step than the FP32 kernel keeps up with on the CUs the
+                                 recurrence leaves); else 4. A function of batch, steps and the
+                                 device only, so every plan for one workload computes the same gates;
+                             1 = the vendor GEMM (hipBLASLt, FP32 compute, bias epilogue) as a
+                                 comparator, run unsliced and unstreamed;
+                             2 = the own kernel in split precision, two bf16 parts per FP32
+                                 operand, three bf16 MFMA products per K chunk (a0·b0 + a0·b1 +
+                                 a1·b0) accumulated in FP32:
+                                 |error| <= (3·2^-16·(1 + 2^-7) + (3K + 2)·2^-24)·sum|x·w| per gate;
+                             3 = three bf16 parts, six products (every ap·bq with p + q <= 2):
+                                 |error| <= (4·2^-24·(1 + 2^-7) + (6K + 2)·2^-24)·sum|x·w| per gate,
+                                 the truncation of the order of one FP32 rounding per product;
+                             4 = the own kernel's FP32 MFMA products:
+                                 |error| <= (K + 2)·2^-24·sum|x·w| per gate */
     int32_t pipeline;     /* streamed gates for bilstm_forward: each layer's projection runs beside
                              that layer's recurrence on the CUs the recurrence leaves free, computes
                              the gates in the order the recurrence reads them (chunks of steps,
@@ -119,9 +134,9 @@ typedef struct {
                              running one still reads. The output is bitwise the same as without
                              it.
                              0 = auto (on when recur_groups = 1, concurrent = 2, the
-                             recurrence's grid leaves at least a quarter of the CUs free and
-                             projection = 0), 1 = off,
-                             2 = on (BILSTM_UNSUPPORTED unless recur_groups = 1, projection = 0,
+                             recurrence's grid leaves at least a quarter of the CUs free and the
+                             projection is the library's own), 1 = off,
+                             2 = on (BILSTM_UNSUPPORTED unless recur_groups = 1, projection != 1,
                              slices <= 1 and at least 8 CUs stay free), with the next layer's
                              projection starting during this layer's recurrence; 3 = on, with it
                              starting after this layer's recurrence; 4 = as 2, with the four
@@ -160,7 +175,8 @@ typedef struct {
     uint64_t device_bytes;   /* device memory the plan owns */
     int32_t slices;          /* batch slices bilstm_forward runs as concurrent chains */
     int32_t slice_windows;   /* windows per slice (the last slice may hold fewer) */
-    int32_t projection;      /* 0 own FP32-MFMA kernel, 1 vendor GEMM, 2 own split-precision */
+    int32_t projection;      /* the projection the plan runs (never 0): 1 vendor GEMM, 2 and 3 own
+                                split-precision kernel with two or three bf16 parts, 4 own FP32 MFMA */
     int32_t pipeline;        /* 1 when bilstm_forward streams the gates (see bilstm_options) */
     int32_t stream_chunk;    /* streamed gates: recurrence steps per published chunk (128 /
                                 windows per projection row block); 0 when not streamed */
@@ -283,8 +299,10 @@ const char *bilstm_last_error(void);
  * (e.g. 39 windows of 589 frames); larger calls return BILSTM_DIMENSION_OVERFLOW. Calls that
  * overlap on one device race on that array (serialize them, e.g. on one stream); calls on
  * different devices do not. Runs the projection and the single-workgroup recurrence on
- * `stream`, both directions per layer in one launch; the output is bitwise the same as a
- * plan's bilstm_forward for the same inputs.
+ * `stream`, both directions per layer in one launch, with FP32 projection products: the output
+ * is bitwise the same as a plan's bilstm_forward for the same inputs wherever the plan computes
+ * its projection with FP32 products (bilstm_options.projection = 4, or the plan's rule where it
+ * chooses them: every workload of up to 48 windows of 589 frames).
  */
 bilstm_status bilstm_forward_noalloc(int device, uint32_t batch, uint32_t steps,
                                      const bilstm_layer layers[BILSTM_LAYERS], const float *x, size_t x_len,

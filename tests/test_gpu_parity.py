@@ -61,26 +61,34 @@ def to_packed(oracle_gates):
     return np.ascontiguousarray(g.transpose(0, 1, 3, 2).reshape(rows, 1024))
 
 
-def projection_bound(x, layer, split=False):
-    """|gpu - exact| bound of a gate pre-activation. FP32: (K + 2)·u·(sum|w x| + |bias|), any
-    summation order. Split precision (bf16 x 3): the dropped lo·lo term and the parts'
-    residuals add 3·2^-16·(1 + 2^-7)·sum|w x|, the FP32 sum runs over 3K products."""
+def projection_bound(x, layer, parts=0):
+    """|gpu - exact| bound of a gate pre-activation. FP32 (parts = 0): (K + 2)·u·(sum|w x| +
+    |bias|), any summation order. Split precision in two bf16 parts (three products): the
+    dropped part products and the parts' residuals add 3·2^-16·(1 + 2^-7)·sum|w x|, the FP32 sum
+    runs over 3K products. Three parts (six products): 4·2^-24·(1 + 2^-7)·sum|w x| for what is
+    dropped, over 6K products."""
     w = layer["w"].astype(np.float64)
     b = layer["b"].astype(np.float64)
     k = x.shape[1]
     mag = np.einsum("mk,drk->mdr", np.abs(x.astype(np.float64)), np.abs(w)) + np.abs(b[:, 0] + b[:, 1])[None]
-    if not split:
+    if parts == 0:
         return to_packed((k + 2) * 2.0 ** -24 * mag * 1.01 + 1e-30)
-    coeff = 3 * 2.0 ** -16 * (1 + 2.0 ** -7) + (3 * k + 2) * 2.0 ** -24 * 1.01
+    if parts == 2:
+        coeff = 3 * 2.0 ** -16 * (1 + 2.0 ** -7) + (3 * k + 2) * 2.0 ** -24 * 1.01
+    else:
+        coeff = 4 * 2.0 ** -24 * (1 + 2.0 ** -7) + (6 * k + 2) * 2.0 ** -24 * 1.01
     return to_packed(coeff * mag * 1.01 + 1e-30)
 
 
-@pytest.mark.parametrize("layer_index,rows,projection", [(0, 200, 0), (0, 589, 0), (1, 333, 0), (1, 4712, 0),
-                                                         (1, 18848, 0), (0, 589, 1), (1, 4712, 1),
-                                                         (0, 589, 2), (1, 333, 2), (1, 18848, 2)])
+@pytest.mark.parametrize("layer_index,rows,projection", [(0, 200, 4), (0, 589, 4), (1, 333, 4), (1, 4712, 4),
+                                                         (1, 18848, 4), (0, 589, 0), (1, 18848, 0),
+                                                         (0, 589, 1), (1, 4712, 1),
+                                                         (0, 589, 2), (1, 333, 2), (1, 18848, 2),
+                                                         (0, 589, 3), (0, 18848, 3), (1, 333, 3), (1, 18848, 3)])
 def test_projection_matches_oracle(bl, orc, layer_index, rows, projection):
-    """The projection alone (projection = 1: the vendor-GEMM comparator) against the oracle,
-    within the summation-order-free fp32 bound."""
+    """The projection alone against the oracle, within the summation-order-free bound of the
+    arithmetic the plan runs: FP32 products (4, and the vendor-GEMM comparator 1), two or three
+    bf16 parts (2, 3); 0 checks the bound of what the plan's rule chose."""
     layers = workloads.make_layers(31)
     width = 60 if layer_index == 0 else 256
     x = np.random.default_rng(rows).standard_normal((rows, width)).astype(np.float32)
@@ -88,11 +96,13 @@ def test_projection_matches_oracle(bl, orc, layer_index, rows, projection):
         x = np.tanh(x).astype(np.float32)  # later layers see hidden states in (-1, 1)
     note(f"projection layer={layer_index} rows={rows} projection={projection}")
     plan = bl.Plan(layers, rows, 1, projection=projection)
+    assert projection == 0 or plan.info()["projection"] == projection
     gates = plan.project(layer_index, torch.from_numpy(x).cuda())
     torch.cuda.synchronize()
     ref = to_packed(orc.projection(x, layers[layer_index]["w"], layers[layer_index]["b"]))
     err = np.abs(gates.cpu().numpy().astype(np.float64) - ref)
-    bound = projection_bound(x, layers[layer_index], split=projection == 2)
+    chosen = plan.info()["projection"]
+    bound = projection_bound(x, layers[layer_index], parts=chosen if chosen in (2, 3) else 0)
     assert np.all(err <= bound), f"max err {err.max():.3e}, worst ratio {(err / bound).max():.2f}"
     note(f"projection layer={layer_index} rows={rows} projection={projection} max err {err.max():.3e} "
          f"worst ratio to bound {(err / bound).max():.3f}")
@@ -222,17 +232,19 @@ def test_stack_batch_invariant(bl):
     assert np.array_equal(y8.view(np.uint32), y32[:8].view(np.uint32))
 
 
+@pytest.mark.parametrize("projection", [2, 3])
 @pytest.mark.parametrize("name", ALL_WORKLOADS)
-def test_stack_with_split_projection_matches_oracle(bl, orc, name):
-    """Split-precision projections (bf16 x 3) keep every element of the whole stack's output
-    within the output tolerance, bit-stable over three forwards."""
+def test_stack_with_split_projection_matches_oracle(bl, orc, name, projection):
+    """Split-precision projections (two bf16 parts, three products; three parts, six products),
+    streamed where the plan streams: every element of the whole stack's output within the
+    output tolerance, bit-stable over three forwards."""
     x, layers = workloads.make_workload(name)
-    note(f"stack {name} projection=2: 3 forwards, whole output against the oracle")
-    runs, info = run_repeated(bl, x, layers, projection=2)
-    assert info["projection"] == 2
+    note(f"stack {name} projection={projection}: 3 forwards, whole output against the oracle")
+    runs, info = run_repeated(bl, x, layers, projection=projection)
+    assert info["projection"] == projection
     assert_bitwise_equal(runs, f"{name} split projection")
     err = assert_close(runs[0], oracle_reference(orc, name), f"{name} split projection")
-    note(f"stack {name} projection=2 max abs err {err:.3e}")
+    note(f"stack {name} projection={projection} streamed={info['pipeline']} max abs err {err:.3e}")
 
 
 EXCHANGE_SPLITS = [(2, 1), (2, 2), (2, 4), (4, 1), (4, 2), (4, 4)]
@@ -289,6 +301,25 @@ def test_multi_launch_schedule_matches_oracle(bl, orc, batch, steps, groups, til
     base, _ = run_stack(bl, x, layers)
     assert np.array_equal(runs[0].view(np.uint32), base.view(np.uint32))
     note(f"multi-launch batch={batch} launches={info['recur_launches']} max abs err {err:.3e}")
+
+
+@pytest.mark.parametrize("name", ["b8", "b32", "b256", "b64_t4096"])
+def test_three_part_split_is_as_accurate_as_fp32(bl, orc, name):
+    """The accuracy side of the projection rule, rerun: on each workload the rule may split
+    (at least 2048 rows), the stack with the three-part split stays within 1.1 times the
+    largest error of the stack with FP32 products against the fp64 oracle (the factor of the
+    pages' own check); the two-part split does not, and the rule never picks it."""
+    x, layers = workloads.make_workload(name)
+    ref = oracle_reference(orc, name)
+    errs = {}
+    for mode in (4, 3, 2):
+        got, info = run_stack(bl, x, layers, projection=mode)
+        errs[mode] = float(np.max(np.abs(got.astype(np.float64) - ref)))
+    note(f"rule check {name}: largest error fp32 {errs[4]:.3e}, three parts {errs[3]:.3e} "
+         f"({errs[3] / errs[4]:.3f}x), two parts {errs[2]:.3e} ({errs[2] / errs[4]:.3f}x)")
+    assert errs[3] <= 1.1 * errs[4]
+    assert errs[2] > 1.1 * errs[4]
+    assert bl.schedule(x.shape[0], x.shape[1], 256, 1)["projection"] in (3, 4)
 
 
 def test_split_projection_batch_invariant(bl):

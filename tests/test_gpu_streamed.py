@@ -85,6 +85,22 @@ def test_streamed_equals_unstreamed_bitwise(bl, batch, steps, tile, pipeline):
     assert np.array_equal(got[0].view(np.uint32), base[0].view(np.uint32))
 
 
+@pytest.mark.parametrize("projection", [2, 3])
+@pytest.mark.parametrize("pipeline", [2, 4, 5])
+@pytest.mark.parametrize("batch,steps,tile", [(1, 129, 0), (3, 150, 0), (8, 97, 2), (32, 150, 0), (64, 70, 0)])
+def test_streamed_split_equals_unstreamed_split_bitwise(bl, batch, steps, tile, pipeline, projection):
+    """The streamed kernel splits its FP32 operands into bf16 parts after the LDS ring, the
+    plain split kernel while staging x (W split at plan creation): the same parts, the same
+    products in the same order, so the gates, and the stack's output, are bitwise the same."""
+    x = workloads.make_input(60 + batch, batch, steps)
+    layers = workloads.make_layers(61)
+    note(f"streamed split projection={projection} pipeline={pipeline} batch={batch} steps={steps} tile={tile}")
+    got, info = run(bl, x, layers, pipeline=pipeline, tile=tile, projection=projection)
+    base, binfo = run(bl, x, layers, pipeline=1, slices=1, tile=tile, projection=projection)
+    assert info["pipeline"] == 1 and binfo["pipeline"] == 0 and info["projection"] == projection
+    assert np.array_equal(got[0].view(np.uint32), base[0].view(np.uint32))
+
+
 @pytest.mark.parametrize("pipeline", [2, 4, 3])
 def test_streamed_repeated_forwards_are_bit_stable(bl, pipeline):
     """Five forwards on one plan: each pass's counters reach the next target exactly once."""

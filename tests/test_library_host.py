@@ -150,12 +150,47 @@ def test_schedule_slices_need_single_workgroup_tiles(bl):
 def test_schedule_library_projection_runs_unsliced(bl):
     s = bl.schedule(32, 589, 256, 1, projection=1)
     assert s["projection"] == 1 and s["slices"] == 1
-    assert bl.schedule(32, 589, 256, 1)["projection"] == 0
-    s = bl.schedule(32, 589, 256, 1, projection=2)  # own split-precision kernel: sliced, not streamed
-    assert s["projection"] == 2 and s["slices"] == 2 and s["pipeline"] == 0
+    assert bl.schedule(32, 589, 256, 1)["projection"] == 4
+    for mode in (2, 3):  # the own split-precision kernels stream like the FP32 one
+        s = bl.schedule(32, 589, 256, 1, projection=mode)
+        assert s["projection"] == mode and s["slices"] == 1 and s["pipeline"] == 1
+        s = bl.schedule(32, 589, 256, 1, projection=mode, pipeline=1)  # unstreamed: sliced
+        assert s["projection"] == mode and s["slices"] == 2 and s["pipeline"] == 0
     with pytest.raises(bl.BilstmError) as e:
         bl.schedule(32, 589, 256, 1, projection=1, slices=2)
     assert e.value.name == "BILSTM_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("batch,steps,chosen", [
+    (1, 589, 4),        # 589 rows: below the rows that amortize the split
+    (3, 5, 4),
+    (8, 589, 4),        # streamed, the FP32 projection keeps up beside the recurrence
+    (32, 589, 4),       # the headline workload
+    (48, 589, 4),
+    (56, 589, 3),       # streamed, more projection work per step than the free CUs do in FP32
+    (64, 4096, 3),      # the long workload
+    (128, 589, 3),      # unstreamed: the projection runs between the recurrences
+    (256, 589, 3),
+    (1024, 24, 3)])
+def test_projection_rule(bl, batch, steps, chosen):
+    """projection = 0: the three-part split where it amortizes and the projection is on the
+    forward's critical path, else FP32; never the two-part split or the vendor GEMM."""
+    assert bl.schedule(batch, steps, 256, 1)["projection"] == chosen
+
+
+@pytest.mark.parametrize("batch,steps", [(32, 589), (64, 4096), (256, 589), (128, 64)])
+def test_projection_rule_ignores_the_plans_other_options(bl, batch, steps):
+    """The rule depends on the workload and the device only: streaming, slices, the recurrence
+    split and the direction mode leave its choice alone, so every plan of a workload computes
+    the same gates (the bitwise-equality properties across those options hold)."""
+    base = bl.schedule(batch, steps, 256, 1)["projection"]
+    for kwargs in (dict(pipeline=1), dict(pipeline=1, slices=2), dict(groups=2), dict(groups=4, tile=1),
+                   dict(concurrent=0), dict(tile=4)):
+        try:
+            s = bl.schedule(batch, steps, 256, 4, **kwargs)
+        except bl.BilstmError:
+            continue
+        assert s["projection"] == base, kwargs
 
 
 @pytest.mark.parametrize("batch,steps,on,chunk", [(1, 589, 1, 128), (2, 589, 1, 64), (3, 589, 1, 32),
@@ -182,7 +217,7 @@ def test_schedule_forced_streaming_checks_its_conditions(bl):
         assert bl.schedule(batch, 589, 256, 1, pipeline=2)["stream_chunk"] == chunk
     s = bl.schedule(120, 589, 256, 1, pipeline=2)  # 240 + 8 <= 256: allowed when asked for
     assert s["pipeline"] == 1
-    for kwargs in (dict(groups=2), dict(projection=1), dict(projection=2), dict(slices=2)):
+    for kwargs in (dict(groups=2), dict(projection=1), dict(slices=2)):
         with pytest.raises(bl.BilstmError) as e:
             bl.schedule(32, 589, 256, 1, pipeline=2, **kwargs)
         assert e.value.name == "BILSTM_UNSUPPORTED"
@@ -239,7 +274,7 @@ def test_schedule_first_chunk_split(bl, batch, steps, cus, split):
 @pytest.mark.parametrize("kwargs,status", [
     (dict(groups=3), "BILSTM_UNSUPPORTED"), (dict(tile=3), "BILSTM_UNSUPPORTED"),
     (dict(concurrent=5), "BILSTM_INVALID_ARGUMENT"), (dict(slices=9), "BILSTM_INVALID_ARGUMENT"),
-    (dict(slices=-1), "BILSTM_INVALID_ARGUMENT"), (dict(projection=3), "BILSTM_INVALID_ARGUMENT"),
+    (dict(slices=-1), "BILSTM_INVALID_ARGUMENT"), (dict(projection=5), "BILSTM_INVALID_ARGUMENT"),
     (dict(projection=-1), "BILSTM_INVALID_ARGUMENT"), (dict(pipeline=6), "BILSTM_INVALID_ARGUMENT"),
     (dict(pipeline=-1), "BILSTM_INVALID_ARGUMENT")])
 def test_schedule_rejects_bad_options(bl, kwargs, status):
