@@ -254,7 +254,8 @@ def main() -> int:
     plan.close()
 
     # the other projection modes, each alone on the whole batch: the vendor GEMM (hipBLASLt,
-    # FP32, bias epilogue) and the own kernel in split precision (bf16 x 3)
+    # FP32, bias epilogue), the own kernel in split precision (two and three bf16 parts) and, when
+    # the plan chose a split, the own FP32 kernel
     def other_projection(mode):
         ms = [[] for _ in range(4)]
         try:
@@ -278,6 +279,7 @@ def main() -> int:
     library_projection = other_projection(1)
     split_projection = other_projection(2)
     split3_projection = other_projection(3)
+    fp32_projection = other_projection(4) if info["projection"] != 4 else None
 
     # the fused segmentation heads after the stack, alone, on this workload's stack output
     heads = bl.Heads(workloads.make_heads(wl.seed))
@@ -357,14 +359,17 @@ def main() -> int:
                             "frac_of_bound": bound_us / us_per_step, "exchange_one_way_ns": xchg_ns,
                             "bound_terms": f"FMA {fma_clk:.0f} clk at {FMA_PER_CLK_PER_CU} FMA/clk/CU, "
                                            f"{CLOCK_GHZ} GHz" + (" + one exchange" if groups > 1 else "")},
-        "projection": {"mode": {2: "split, two bf16 parts", 3: "split, three bf16 parts",
-                                4: "FP32 MFMA"}.get(info["projection"], str(info["projection"])),
-                       "ms_total": proj_total_ms, "ms_per_layer": proj_med, "achieved_tflops": proj_tflops,
-                       "tflops_per_layer": proj_layer_tflops,
-                       "peak_tflops": PEAK_FP32_MFMA_TFLOPS, "frac": proj_tflops / PEAK_FP32_MFMA_TFLOPS},
+        "projection": dict({"mode": {2: "split, two bf16 parts", 3: "split, three bf16 parts",
+                                     4: "FP32 MFMA"}.get(info["projection"], str(info["projection"])),
+                            "ms_total": proj_total_ms, "ms_per_layer": proj_med, "achieved_tflops": proj_tflops,
+                            "tflops_per_layer": proj_layer_tflops,
+                            "peak_tflops": PEAK_FP32_MFMA_TFLOPS, "frac": proj_tflops / PEAK_FP32_MFMA_TFLOPS},
+                           **(split_bf16_rates({"achieved_tflops": proj_tflops}, 3 if info["projection"] == 2 else 6)
+                              if info["projection"] in (2, 3) else {})),
         "projection_vendor_gemm": library_projection,
         "projection_split_bf16x3": dict(split_projection, **split_bf16_rates(split_projection, 3)),
         "projection_split_bf16x6": dict(split3_projection, **split_bf16_rates(split3_projection, 6)),
+        **({"projection_fp32": fp32_projection} if fp32_projection is not None else {}),
         "heads": {"ms": heads_med, "achieved_tflops": heads_tflops, "peak_tflops": PEAK_FP32_MFMA_TFLOPS,
                   "frac": heads_tflops / PEAK_FP32_MFMA_TFLOPS,
                   "hbm_gbs": HEAD_BYTES_PER_FRAME * frames / (heads_med / 1e3) / 1e9,
