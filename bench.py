@@ -143,6 +143,9 @@ def main() -> int:
                          "5 on with every kernel after the previous one (for counter collection)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--fma-probe", action="store_true",
+                    help="only measure the FP32 FMA issue rate the recurrence's bound rests on: shader clocks per "
+                         "wave64 FMA per SIMD with 1, 2 and 4 waves per SIMD, on one CU and on every CU")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate the HBM "
                          "byte counters of a profiler run against a known size")
@@ -157,6 +160,20 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4}))
+        return 0
+
+    if args.fma_probe:
+        import torch
+        import bidirectional_lstm_sequence_amd as bl
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        rows = []
+        for wg in (1, 64, cus):
+            for wps in (1, 2, 4):
+                r = bl.probe_fma_rate(0, wps, wg, 20000)
+                rows.append({"workgroups": wg, "waves_per_simd": wps, **r,
+                             "fma_per_clk_per_cu": 4 * 64 / r["clocks_per_fma"]})
+        print(json.dumps({"fma_probe": rows, "note": "128 FP32 FMAs per lane per round over 8 accumulators "
+                          "(v_fmac_f32, register operands), 20000 rounds; median workgroup"}))
         return 0
 
     if args.gpus != 1:

@@ -32,7 +32,7 @@ EXPORTS = ["bilstm_plan_create", "bilstm_plan_create_ex", "bilstm_forward", "bil
            "bilstm_recur", "bilstm_plan_get_info", "bilstm_check", "bilstm_set_phase_events",
            "bilstm_phase_times", "bilstm_destroy", "bilstm_last_error", "bilstm_pack_layer",
            "bilstm_schedule", "bilstm_probe_exchange", "bilstm_heads_create", "bilstm_heads_forward",
-           "bilstm_heads_destroy", "bilstm_forward_noalloc"]
+           "bilstm_heads_destroy", "bilstm_forward_noalloc", "bilstm_probe_fma_rate"]
 HEAD_IN, HEAD_MID, HEAD_CLASSES = 256, 128, 7
 
 
@@ -128,6 +128,8 @@ def library():
         "bilstm_heads_destroy": ([P], None),
         "bilstm_forward_noalloc": ([ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(Layer), P,
                                     ctypes.c_size_t, P, ctypes.c_size_t, P], st),
+        "bilstm_probe_fma_rate": ([ctypes.c_int, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -243,6 +245,16 @@ def probe_exchange(device: int = 0, same_xcd: bool = True, round_trips: int = 20
     _check(lib.bilstm_probe_exchange(device, 1 if same_xcd else 0, round_trips, ctypes.byref(ns),
                                      ctypes.byref(a), ctypes.byref(b)))
     return {"one_way_ns": ns.value, "xcd_a": a.value, "xcd_b": b.value}
+
+
+def probe_fma_rate(device: int = 0, waves_per_simd: int = 2, workgroups: int = 1, iterations: int = 20000) -> dict:
+    """Shader clocks per wave64 FP32 FMA per SIMD, and the shader clock in GHz (see bilstm.h)."""
+    lib = library()
+    cpf = ctypes.c_double()
+    ghz = ctypes.c_double()
+    _check(lib.bilstm_probe_fma_rate(device, waves_per_simd, workgroups, iterations, ctypes.byref(cpf),
+                                     ctypes.byref(ghz)))
+    return {"clocks_per_fma": cpf.value, "ghz": ghz.value}
 
 
 def _stream_handle(stream):

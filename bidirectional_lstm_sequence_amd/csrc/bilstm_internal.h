@@ -238,5 +238,7 @@ hipError_t launch_exchange_clear(unsigned long long *words, size_t count, hipStr
 hipError_t recurrence_occupancy(int groups, int tile, int *per_cu);
 hipError_t run_exchange_probe(int same_xcd, int round_trips, unsigned long long timeout_ticks,
                               double ticks_per_ns, double *one_way_ns, int *xcd_a, int *xcd_b);
+hipError_t run_fma_probe(int waves_per_simd, int workgroups, int iters, double wall_khz, double *clocks_per_fma,
+                         double *ghz);
 
 }  // namespace bl

@@ -1022,4 +1022,27 @@ bilstm_status bilstm_probe_exchange(int device, int same_xcd, int32_t round_trip
     return BILSTM_OK;
 }
 
+bilstm_status bilstm_probe_fma_rate(int device, int waves_per_simd, int32_t workgroups, int32_t iterations,
+                                    double *clocks_per_fma, double *ghz) {
+    if (clocks_per_fma == nullptr || ghz == nullptr) return fail(BILSTM_INVALID_ARGUMENT, "probe_fma_rate: NULL output");
+    if (waves_per_simd != 1 && waves_per_simd != 2 && waves_per_simd != 4) {
+        return fail(BILSTM_INVALID_ARGUMENT, "probe_fma_rate: waves_per_simd %d is not 1, 2 or 4", waves_per_simd);
+    }
+    if (workgroups < 1 || workgroups > 4096 || iterations < 1 || iterations > 1000000) {
+        return fail(BILSTM_INVALID_ARGUMENT, "probe_fma_rate: workgroups %d or iterations %d out of range", workgroups,
+                    iterations);
+    }
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || device < 0 || device >= count) {
+        return fail(BILSTM_INVALID_ARGUMENT, "probe_fma_rate: no device %d", device);
+    }
+    if (!is_gfx950(device)) return fail(BILSTM_UNSUPPORTED, "probe_fma_rate: device %d is not gfx950", device);
+    DeviceScope scope(device);
+    BL_HIP(scope.error(), "probe_fma_rate: hipSetDevice");
+    int wall_khz = 0;
+    BL_HIP(hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, device), "probe_fma_rate");
+    BL_HIP(run_fma_probe(waves_per_simd, workgroups, iterations, wall_khz, clocks_per_fma, ghz), "probe_fma_rate");
+    return BILSTM_OK;
+}
+
 }  // extern "C"

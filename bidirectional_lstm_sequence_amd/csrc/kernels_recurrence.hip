@@ -47,6 +47,9 @@
 //
 // Waits are bounded: a poll that sees no progress for `timeout_ticks` wall-clock ticks
 // sets the error word and stops waiting, so the grid always drains.
+#include <algorithm>
+#include <vector>
+
 #include "bilstm_internal.h"
 
 namespace bl {
@@ -609,6 +612,43 @@ __global__ void exchange_probe_kernel(unsigned long long *words, int partner, in
     }
 }
 
+// FMA issue rate: each wave runs `iters` rounds of 128 FMAs over 8 independent accumulators per
+// lane, the shape of the recurrence's product loop (128 FMAs per lane and step, 8 sums). The
+// workgroup's waves are dealt over the CU's four SIMDs, so a workgroup of 256·w threads puts w
+// waves on each. Thread 0 records the elapsed shader clocks and wall-clock ticks of the timed
+// loop, between two barriers.
+__global__ __launch_bounds__(1024) void fma_rate_kernel(int iters, float seed, unsigned long long *out, float *sink) {
+    // acc += w·h with register operands, as the recurrence's products (v_fmac_f32)
+    float acc[8], w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        acc[i] = seed * static_cast<float>(i + 1) + 1e-7f * static_cast<float>(threadIdx.x);
+        w[i] = 1e-3f * seed * static_cast<float>(i + 2);
+    }
+    float h = seed + 1e-9f * static_cast<float>(threadIdx.x);
+    __syncthreads();
+    const unsigned long long t0 = __builtin_readcyclecounter();
+    const unsigned long long w0 = wall_clock64();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[i], h, acc[i]);
+        asm volatile("" : "+v"(h));  // a fresh operand each round: the products are not hoisted
+    }
+    __syncthreads();
+    const unsigned long long t1 = __builtin_readcyclecounter();
+    const unsigned long long w1 = wall_clock64();
+    if (threadIdx.x == 0) {
+        out[2 * blockIdx.x] = t1 - t0;
+        out[2 * blockIdx.x + 1] = w1 - w0;
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sum += acc[i];
+    if (sum == 12345.0f) sink[threadIdx.x] = sum;  // keeps the products live; never true here
+}
+
 template <int KG, int BT>
 hipError_t launch_typed(const RecurArgs &args, int directions, size_t lds, hipStream_t stream) {
     const int nwg = KG == 1 ? args.tile_count : (args.tile_count + 7) / 8 * 8 * KG;
@@ -738,6 +778,40 @@ hipError_t run_exchange_probe(int same_xcd, int round_trips, unsigned long long 
     *one_way_ns = static_cast<double>(host[0]) / ticks_per_ns / (2.0 * round_trips);
     *xcd_a = static_cast<int>(host[2]);
     *xcd_b = static_cast<int>(host[3]);
+    return hipSuccess;
+}
+
+hipError_t run_fma_probe(int waves_per_simd, int workgroups, int iters, double wall_khz, double *clocks_per_fma,
+                         double *ghz) {
+    unsigned long long *out = nullptr;
+    float *sink = nullptr;
+    hipError_t e = hipMalloc(&out, 2 * static_cast<size_t>(workgroups) * sizeof(unsigned long long));
+    if (e != hipSuccess) return e;
+    e = hipMalloc(&sink, 1024 * sizeof(float));
+    if (e != hipSuccess) {
+        (void)hipFree(out);
+        return e;
+    }
+    std::vector<unsigned long long> host(2 * static_cast<size_t>(workgroups));
+    hipLaunchKernelGGL(fma_rate_kernel, dim3(workgroups), dim3(256 * waves_per_simd), 0, nullptr, iters, 0.5f, out,
+                       sink);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(host.data(), out, host.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost);
+    (void)hipFree(out);
+    (void)hipFree(sink);
+    if (e != hipSuccess) return e;
+    // the median workgroup: clocks per wave64 FMA per SIMD, and shader clocks per wall-clock tick
+    std::vector<double> cpf(workgroups), rate(workgroups);
+    const double fmas_per_simd = static_cast<double>(waves_per_simd) * iters * 128.0;
+    for (int g = 0; g < workgroups; ++g) {
+        cpf[g] = static_cast<double>(host[2 * g]) / fmas_per_simd;
+        rate[g] = host[2 * g + 1] > 0 ? static_cast<double>(host[2 * g]) / static_cast<double>(host[2 * g + 1]) : 0.0;
+    }
+    std::nth_element(cpf.begin(), cpf.begin() + workgroups / 2, cpf.end());
+    std::nth_element(rate.begin(), rate.begin() + workgroups / 2, rate.end());
+    *clocks_per_fma = cpf[workgroups / 2];
+    *ghz = rate[workgroups / 2] * wall_khz * 1e-6;
     return hipSuccess;
 }
 

@@ -392,6 +392,16 @@ bilstm_status bilstm_schedule(uint32_t batch, uint32_t steps, int32_t cu_count, 
 bilstm_status bilstm_probe_exchange(int device, int same_xcd, int32_t round_trips,
                                     double *one_way_ns, int32_t *xcd_a, int32_t *xcd_b);
 
+/*
+ * FMA issue-rate probe, the rate the recurrence's on-chip bound rests on: one or `workgroups`
+ * workgroups of 256·waves_per_simd threads (waves_per_simd = 1, 2 or 4 waves on each of a CU's
+ * four SIMDs) each run `iterations` rounds of 128 FP32 FMAs over 8 independent accumulators per
+ * lane, the shape of the recurrence's product loop. Writes the median workgroup's shader clocks
+ * per wave64 FMA per SIMD and its shader clock in GHz (shader clocks over wall-clock time).
+ */
+bilstm_status bilstm_probe_fma_rate(int device, int waves_per_simd, int32_t workgroups, int32_t iterations,
+                                    double *clocks_per_fma, double *ghz);
+
 #ifdef __cplusplus
 }
 #endif

@@ -521,6 +521,17 @@ def test_exchange_probe(bl):
     assert 0 < same["one_way_ns"] < 100000 and 0 < cross["one_way_ns"] < 100000
 
 
+def test_fma_rate_probe(bl):
+    """The FMA issue rate behind the recurrence's bound: with two or more waves per SIMD a SIMD
+    retires one wave64 FP32 FMA about every two shader clocks (128 per clock per CU, the rate the
+    published FP32 vector peak implies); a single wave issues at most every clock."""
+    out = {wps: bl.probe_fma_rate(0, wps, 1, 4000) for wps in (1, 2, 4)}
+    note(f"fma rate probe: {out}")
+    for wps, r in out.items():
+        assert 1.0 <= r["clocks_per_fma"] < 16 and 0.5 < r["ghz"] < 4.0
+    assert out[2]["clocks_per_fma"] < 3.0
+
+
 @pytest.mark.parametrize("steps", [1, 2, 3, 5, 7])
 @pytest.mark.parametrize("groups,tile", [(1, 1), (1, 2), (1, 4), (2, 2), (4, 1)])
 def test_recurrence_short_sequences(bl, orc, steps, groups, tile):
