@@ -40,6 +40,7 @@
 //    the LDS bit, rows swizzled instead of padded), three steps ahead of the products, with
 //    explicit counter waits and bare barriers.
 #include <algorithm>
+#include <type_traits>
 
 #include "bilstm_internal.h"
 
@@ -53,6 +54,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // and the cache-policy bit of an agent-scope (sc1) access.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 constexpr int kCachePolicySc1 = 16;
+constexpr unsigned int kOutOfRange = 0x80000000u;  // a buffer offset past every buffer here
 
 
 constexpr int BM = kProjTileM;
@@ -249,191 +251,263 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a)
 //     of the order of one FP32 rounding per product,
 //     |gates - exact| <= (4·2^-24·(1 + 2^-7) + (6K + 2)·2^-24) · sum_k |x_k w_k|.
 // W arrives already split (PARTS [1024][kpad] bf16 planes, packed at plan creation); x is
-// split while staging into LDS. v_mfma_f32_32x32x16_bf16: lane l supplies row (or column)
-// l % 32 and eight consecutive k of half l / 32 of each 16-wide K chunk, for A and B alike.
-constexpr int kSplitStride = BK + 8;  // LDS row stride, bf16 elements (80 bytes: conflict-free)
-
+// split in registers on its way into LDS. v_mfma_f32_32x32x16_bf16: lane l supplies row (or
+// column) l % 32 and eight consecutive k of half l / 32 of a 16-wide K chunk, for A and B alike.
+//
+// Layout for gfx950: two 256-thread workgroups per CU (each wave shares its SIMD with a wave of
+// the other workgroup, which issues its matrix products while this one splits, waits or
+// stores), each walking 128x128 tiles like projection_kernel. A stage of the LDS ring is one
+// 16-wide K chunk: PARTS planes of x and PARTS planes of W, 128 rows of 32 bytes each, the two
+// 16-byte halves of row r stored in swapped order when bit 2 xor bit 3 of r is set: a
+// fragment read serves 16 lanes (16 consecutive rows, one half) per LDS cycle over 64 banks,
+// and those 16 halves then fill the 256 bytes once (with bit 2 alone, rows r and r + 8 met on
+// the same banks: two cycles per 16 lanes, measured as bank conflicts). Three stages: the W
+// planes of the chunk two ahead go from memory straight into LDS (buffer loads with the LDS
+// bit, no registers); the x rows go into registers four chunks ahead (their first read comes
+// from memory, not L2), and the x rows of the next chunk are split into their parts and
+// written to LDS while the matrix products of the current chunk run. The stage walk runs on
+// across tiles, so a tile's first chunks are loaded during the previous tile's last ones.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+constexpr int kSplitThreads = 256;
+constexpr int kSplitStages = 3;
+constexpr int kSplitPlane = BM * 16;  // bf16 elements of one plane of one stage
+
+// bf16 element offset, within a plane, of the 16-byte half h of row r
+__device__ __forceinline__ int split_half(int r, int h) { return h ^ ((r >> 2) & 1) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int split_slot(int r, int h) { return r * 16 + (split_half(r, h) << 3); }
+
+// Wait until at most n of this wave's vector memory operations are outstanding (0 <= n <= 15).
+__device__ __forceinline__ void wait_vm(int n) {
+    switch (n) {
+        case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+}
+
+// Stage s of a split-kernel workgroup's walk: its tile's first row and gate column and its K
+// offset. The workgroup's tiles are first, first + nwg, ...; a stage past its last one gives a
+// tile past the last tile, which has no rows.
+struct SplitStage {
+    int m0, n0, k0;
+};
+template <int KSTEPS>
+__device__ __forceinline__ SplitStage split_stage(int s, int first, int nwg) {
+    constexpr int NC = 2 * KSTEPS;
+    const int q = first + (s / NC) * nwg;
+    const int j = s % NC;
+    SplitStage t;
+    t.m0 = (q / (kGateCols / BN)) * BM;
+    t.n0 = (q % (kGateCols / BN)) * BN;
+    t.k0 = kstep_at<KSTEPS>(t.n0, j >> 1) * BK + (j & 1) * 16;
+    return t;
+}
+
 template <int KSTEPS, int PARTS>
-__global__ __launch_bounds__(kProjThreads, 1) void projection_split_kernel(ProjArgs a) {
+__global__ __launch_bounds__(kSplitThreads, 2) void projection_split_kernel(ProjArgs a) {
     static_assert(PARTS == 2 || PARTS == 3, "two or three bf16 parts");
-    // [stage][part][row][k]
-    __shared__ __attribute__((aligned(16))) __bf16 lds_a[2][PARTS][BM * kSplitStride];
-    __shared__ __attribute__((aligned(16))) __bf16 lds_b[2][PARTS][BN * kSplitStride];
+    constexpr int NC = 2 * KSTEPS;                      // 16-wide K chunks per tile
+    constexpr int kStage = 2 * PARTS * kSplitPlane;     // x planes, then W planes
+    constexpr bool kMaskK = KSTEPS * BK != kWidth;      // layer 0: k past the 60 inputs reads 0
+    // one LDS array (the ring, then the bias): with a second one the compiler waits for every
+    // LDS-bound load before each ring read, as it then tells the arrays apart but not the slots
+    __shared__ __attribute__((aligned(16))) __bf16 ring[kSplitStages * kStage + 2 * kGateCols];
+    float *const sbias = reinterpret_cast<float *>(ring + kSplitStages * kStage);
 
     const int nwg = gridDim.x;  // a multiple of 8
     const int per_xcd = nwg >> 3;
     const int first = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     constexpr int kColTiles = kGateCols / BN;
+    const int my_tiles = first < a.tiles ? (a.tiles - first + nwg - 1) / nwg : 0;
+    const int stages = my_tiles * NC;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1;
     const int wn = wave & 1;
-    const __bf16 *const w_part[3] = {a.w_hi, a.w_lo, a.w_lo2};
 
-    // x: 4 float4 per thread per K step (row f / 8, k 4·(f % 8)); W: per plane 2 x 16 bytes
-    // (8 bf16) per thread (row f / 4, k 8·(f % 4))
-    v4f ra[kLoadsPerThread];
-    u32x4 rb[PARTS][2];  // [plane][i]
-    auto load = [&](int m0, int n0, int k0) {
+    // W: each wave fills 32 rows of each plane, lane i the 16-byte slot i % 2 of row i / 2
+    const int wrow = wave * 32 + (lane >> 1);
+    const unsigned int wlane = (static_cast<unsigned int>(wrow) * a.kpad + 8 * split_half(wrow, lane & 1)) * 2u;
+    // x: this thread's two float4 of a stage, rows tid / 4 and tid / 4 + 64, k = 4·(tid % 4)
+    const int xq = tid & 3;
+    const int xrow = tid >> 2;
+
+    // stage s's W planes into ring stage `slot` (from L2: W is small and read by every tile)
+    auto issue_w = [&](int s, int slot) {
+        const SplitStage t = split_stage<KSTEPS>(s, first, nwg);
+        __bf16 *const sb = ring + slot * kStage + PARTS * kSplitPlane + wave * 512;
 #pragma unroll
-        for (int j = 0; j < kLoadsPerThread; ++j) {
-            const int f = tid + kProjThreads * j;
-            const int m = m0 + f / kThreadsPerRow;
-            const int k = k0 + (f % kThreadsPerRow) * 4;
-            v4f va = {0.f, 0.f, 0.f, 0.f};
-            if (m < a.rows && k < a.in) {
-                va = *reinterpret_cast<const v4f *>(a.x + static_cast<size_t>(m) * a.in + k);
-            }
-            ra[j] = va;
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int f = tid + kProjThreads * i;
-            const size_t off = static_cast<size_t>(n0 + (f >> 2)) * a.kpad + k0 + (f & 3) * 8;
-#pragma unroll
-            for (int pl = 0; pl < PARTS; ++pl) rb[pl][i] = *reinterpret_cast<const u32x4 *>(w_part[pl] + off);
+        for (int p = 0; p < PARTS; ++p) {
+            // (the descriptor is made here: an array of descriptors, or a helper producing one,
+            // keeps the host pass from emitting the kernel's launch stub)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16 *>(p == 0 ? a.w_hi : (p == 1 ? a.w_lo : a.w_lo2)), 0,
+                                                  kGateCols * a.kpad * 2, kBufferRsrcWord3),
+                sb + p * kSplitPlane, 16, wlane + static_cast<unsigned int>(t.n0) * a.kpad * 2u, t.k0 * 2, 0, 0);
         }
     };
-    auto store = [&](int buf) {
+    // stage s's x rows into registers (from memory the first time a row block is read: these go
+    // out four stages ahead). Rows past the last one read zeros (the buffer ends at the tile's
+    // last row), and so does every stage past the workgroup's last one, which keeps the number
+    // of memory operations between two waits the same on every path.
+    auto issue_x = [&](int s, v4f (&xv)[2]) {
+        const SplitStage t = split_stage<KSTEPS>(s, first, nwg);
+        // (uniform; readfirstlane keeps the clamp, which has no scalar form, off the vector
+        // registers, so the descriptor stays scalar)
+        const int rows = __builtin_amdgcn_readfirstlane(max(0, min(BM, a.rows - t.m0)));
+        const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(a.x + static_cast<size_t>(t.m0) * a.in), 0, rows * a.in * 4, kBufferRsrcWord3);
 #pragma unroll
-        for (int j = 0; j < kLoadsPerThread; ++j) {
-            const int f = tid + kProjThreads * j;
-            const int off = (f / kThreadsPerRow) * kSplitStride + (f % kThreadsPerRow) * 4;
+        for (int i = 0; i < 2; ++i) {
+            const unsigned int off = (static_cast<unsigned int>(xrow + 64 * i) * a.in + t.k0 + 4 * xq) * 4u;
+            const bool in_k = !kMaskK || t.k0 + 4 * xq < a.in;
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xrsrc, in_k ? off : kOutOfRange, 0, 0);
+            xv[i] = __builtin_bit_cast(v4f, v);
+        }
+    };
+    // x rows of a stage, split into their parts, into ring stage `slot`
+    auto put_x = [&](int slot, const v4f (&xv)[2]) {
+        __bf16 *const sa = ring + slot * kStage;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = xrow + 64 * i;
+            const int off = split_slot(r, xq >> 1) + (xq & 1) * 4;
             bf16x4 part[PARTS];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float rest = ra[j][e];
+                float rest = xv[i][e];
 #pragma unroll
-                for (int pl = 0; pl < PARTS; ++pl) {
-                    part[pl][e] = static_cast<__bf16>(rest);
-                    rest -= static_cast<float>(part[pl][e]);  // exact
+                for (int p = 0; p < PARTS; ++p) {
+                    part[p][e] = static_cast<__bf16>(rest);
+                    rest -= static_cast<float>(part[p][e]);  // exact
                 }
             }
 #pragma unroll
-            for (int pl = 0; pl < PARTS; ++pl) *reinterpret_cast<bf16x4 *>(&lds_a[buf][pl][off]) = part[pl];
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int f = tid + kProjThreads * i;
-            const int off = (f >> 2) * kSplitStride + (f & 3) * 8;
-#pragma unroll
-            for (int pl = 0; pl < PARTS; ++pl) *reinterpret_cast<u32x4 *>(&lds_b[buf][pl][off]) = rb[pl][i];
+            for (int p = 0; p < PARTS; ++p) *reinterpret_cast<bf16x4 *>(sa + p * kSplitPlane + off) = part[p];
         }
     };
 
-    const int frag_row = lane & 31;
-    const int frag_k = (lane >> 5) * 8;
-    // fragments of K chunk c (16 wide): [plane][block]
-    auto frags = [&](int buf, int c, bf16x8 (&af)[PARTS][2], bf16x8 (&bf)[PARTS][2]) {
-#pragma unroll
-        for (int pl = 0; pl < PARTS; ++pl)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                af[pl][t] = *reinterpret_cast<const bf16x8 *>(
-                    &lds_a[buf][pl][(wm * 64 + t * 32 + frag_row) * kSplitStride + c * 16 + frag_k]);
-                bf[pl][t] = *reinterpret_cast<const bf16x8 *>(
-                    &lds_b[buf][pl][(wn * 64 + t * 32 + frag_row) * kSplitStride + c * 16 + frag_k]);
-            }
-    };
-
-    float pend[2][2][16];
-    int pm0 = 0, pn0 = 0;
-    bool have = false;
-    auto put = [&](int i, int j, int r) {
-        const int m = pm0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int n = pn0 + wn * 64 + j * 32 + (lane & 31);
-        if (m < a.rows) a.gates[static_cast<size_t>(m) * kGateCols + n] = pend[i][j][r];
-    };
-    constexpr int kChunk = 64 / KSTEPS;
-    auto put_chunk = [&](int s) {
-#pragma unroll
-        for (int c = 0; c < kChunk; ++c) {
-            const int idx = s * kChunk + c;
-            put(idx >> 5, (idx >> 4) & 1, idx & 15);
-        }
-    };
-
-    // K steps in the order of kstep_at, as every projection kernel takes them (the streamed
-    // split kernel too, so streamed and unstreamed split gates are bitwise the same)
-    int q = first;
-    int base = 0;
-    if (q < a.tiles) {
-        const int n0 = (q % kColTiles) * BN;
-        load((q / kColTiles) * BM, n0, kstep_at<KSTEPS>(n0, 0) * BK);
-        store(0);
-    }
-    __syncthreads();
-
-    for (; q < a.tiles; q += nwg) {
-        const int m0 = (q / kColTiles) * BM;
-        const int n0 = (q % kColTiles) * BN;
-        const int qn = q + nwg;
-        const bool next = qn < a.tiles;
-
-        v16f acc[2][2];
+    const int fr = lane & 31;
+    const int flane = split_slot(fr, lane >> 5);  // rows of a block start at multiples of 32
+    v16f acc[2][2];
+    auto zero = [&] {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
+    };
+    // the six (three) products of the parts of one chunk, in the order every split kernel uses
+    auto products = [&](int slot) {
+        const __bf16 *const sa = ring + slot * kStage;
+        const __bf16 *const sb = sa + PARTS * kSplitPlane;
+        bf16x8 af[PARTS][2], bf[PARTS][2];
 #pragma unroll
-        for (int kt = 0; kt < KSTEPS; ++kt) {
-            const int cur = (base + kt) & 1;
-            const bool more = kt + 1 < KSTEPS;
-            if (more) {
-                load(m0, n0, kstep_at<KSTEPS>(n0, kt + 1) * BK);
-            } else if (next) {
-                const int nn = (qn % kColTiles) * BN;
-                load((qn / kColTiles) * BM, nn, kstep_at<KSTEPS>(nn, 0) * BK);
+        for (int p = 0; p < PARTS; ++p)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                af[p][t] = *reinterpret_cast<const bf16x8 *>(sa + p * kSplitPlane + (wm * 64 + t * 32) * 16 + flane);
+                bf[p][t] = *reinterpret_cast<const bf16x8 *>(sb + p * kSplitPlane + (wn * 64 + t * 32) * 16 + flane);
             }
 #pragma unroll
-            for (int c = 0; c < BK / 16; ++c) {
-                bf16x8 af[PARTS][2], bf[PARTS][2];
-                frags(cur, c, af, bf);
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bf[0][j], acc[i][j], 0, 0, 0);
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bf[1][j], acc[i][j], 0, 0, 0);
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bf[0][j], acc[i][j], 0, 0, 0);
-                        if constexpr (PARTS == 3) {
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bf[1][j], acc[i][j], 0, 0, 0);
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bf[2][j], acc[i][j], 0, 0, 0);
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[2][i], bf[0][j], acc[i][j], 0, 0, 0);
-                        }
-                    }
-                if (c == 0 && have) put_chunk(kt);
+            for (int j = 0; j < 2; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bf[0][j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bf[1][j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bf[0][j], acc[i][j], 0, 0, 0);
+                if constexpr (PARTS == 3) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bf[1][j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bf[2][j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[2][i], bf[0][j], acc[i][j], 0, 0, 0);
+                }
             }
-            if (more || next) store(cur ^ 1);
-            __syncthreads();
-        }
-
+    };
+    // A finished tile: sums plus bias to the gates. The buffer ends at the tile's last row, so
+    // rows past the last one are not written; the row and column offsets of an element are a
+    // per-lane base plus a constant (in the 32x32 output layout one store instruction writes two
+    // full 128-byte row segments).
+    auto finish = [&](int s) {
+        const int q = first + (s / NC) * nwg;
+        const int m0 = (q / kColTiles) * BM;
+        const int n0 = (q % kColTiles) * BN;
+        const int rows = __builtin_amdgcn_readfirstlane(max(0, min(BM, a.rows - m0)));
+        const __amdgpu_buffer_rsrc_t grsrc = __builtin_amdgcn_make_buffer_rsrc(
+            a.gates + static_cast<size_t>(m0) * kGateCols, 0, rows * kGateCols * 4, kBufferRsrcWord3);
+        const int col = n0 + wn * 64 + fr;
+        const unsigned int goff = static_cast<unsigned int>((wm * 64 + (lane >> 5) * 4) * kGateCols + col) * 4u;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const float bv = a.bias[n0 + wn * 64 + j * 32 + (lane & 31)];
+            const float bv = sbias[col + j * 32];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) pend[i][j][r] = acc[i][j][r] + bv;
+                for (int r = 0; r < 16; ++r) {
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, acc[i][j][r] + bv), grsrc,
+                                                          goff,
+                                                          ((i * 32 + (r >> 2) * 8 + (r & 3)) * kGateCols + j * 32) * 4,
+                                                          0);
+                }
         }
-        pm0 = m0;
-        pn0 = n0;
-        have = true;
-        base = (base + KSTEPS) & 1;
+        zero();
+    };
+    // Stage s: issue stage s + 2's W and stage s + 4's x (into the registers stage s's x left),
+    // the products of stage s, then stage s + 1's x into LDS; the barrier at the end makes stage
+    // s + 1 whole (every wave's W loads landed, every wave's x written) and frees stage s's slot.
+    // Per stage the loads go out in the order W(s + 2), x(s + 4), so when stage s + 1's W and x
+    // have landed, only x(s + 3), W(s + 2) and x(s + 4) may still be in flight. The stages past
+    // the last one only load zeros into slots nobody reads again.
+    constexpr int kAfter = PARTS + 4;
+    auto step = [&](int s, v4f (&x_next)[2], v4f (&x_far)[2]) {
+        issue_w(s + 2, (s + 2) % kSplitStages);
+        issue_x(s + 4, x_far);
+        products(s % kSplitStages);
+        wait_vm(kAfter);
+        put_x((s + 1) % kSplitStages, x_next);
+        if (s % NC == NC - 1) finish(s);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt 0: the x parts are in LDS
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    if (stages == 0) return;
+    for (int n = tid; n < kGateCols; n += kSplitThreads) sbias[n] = a.bias[n];
+    zero();
+    // the loads of stages 0 and 1 in the steady order (x(0) and x(1) first)
+    v4f x0[2], x1[2], x2[2], x3[2];
+    issue_x(0, x0);
+    issue_x(1, x1);
+    issue_w(0, 0);
+    issue_x(2, x2);
+    issue_w(1, 1);
+    issue_x(3, x3);
+    wait_vm(kAfter);
+    put_x(0, x0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // stage s's x is in register set s % 4, as stage s + 4's will be. A tile has a multiple of
+    // four stages, so stages is one too.
+    for (int s = 0; s < stages; s += 4) {
+        step(s, x1, x0);
+        step(s + 1, x2, x1);
+        step(s + 2, x3, x2);
+        step(s + 3, x0, x3);
     }
-    if (have) {
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) put_chunk(s);
-    }
+    // no load may still be writing this workgroup's LDS when it ends
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 
@@ -543,7 +617,6 @@ struct TileWidth {
 // batch or the steps, k past the input width, W rows past the last gate).
 constexpr int kStages = 4;                        // K steps in the LDS ring
 constexpr int kStageFloats = 2 * BM * BK;         // x rows, then W rows
-constexpr unsigned int kOutOfRange = 0x80000000u;  // a buffer offset past every buffer here
 
 __device__ __forceinline__ int swizzled(int r, int c) { return r * BK + ((c ^ ((r >> 1) & 7)) << 2); }
 
@@ -913,19 +986,25 @@ hipError_t launch_projection(const ProjArgs &args, int workgroups, hipStream_t s
             return hipErrorInvalidValue;
         }
         const bool three = args.split_parts == 3;
+        // two workgroups per CU
+        const int nsplit = std::max(8, std::min(2 * workgroups, (args.tiles + 7) / 8 * 8) / 8 * 8);
         switch (args.kpad / kProjTileK) {
             case 2:
                 if (three) {
-                    hipLaunchKernelGGL((projection_split_kernel<2, 3>), dim3(nwg), dim3(kProjThreads), 0, stream, args);
+                    hipLaunchKernelGGL((projection_split_kernel<2, 3>), dim3(nsplit), dim3(kSplitThreads), 0, stream,
+                                       args);
                 } else {
-                    hipLaunchKernelGGL((projection_split_kernel<2, 2>), dim3(nwg), dim3(kProjThreads), 0, stream, args);
+                    hipLaunchKernelGGL((projection_split_kernel<2, 2>), dim3(nsplit), dim3(kSplitThreads), 0, stream,
+                                       args);
                 }
                 break;
             case 8:
                 if (three) {
-                    hipLaunchKernelGGL((projection_split_kernel<8, 3>), dim3(nwg), dim3(kProjThreads), 0, stream, args);
+                    hipLaunchKernelGGL((projection_split_kernel<8, 3>), dim3(nsplit), dim3(kSplitThreads), 0, stream,
+                                       args);
                 } else {
-                    hipLaunchKernelGGL((projection_split_kernel<8, 2>), dim3(nwg), dim3(kProjThreads), 0, stream, args);
+                    hipLaunchKernelGGL((projection_split_kernel<8, 2>), dim3(nsplit), dim3(kSplitThreads), 0, stream,
+                                       args);
                 }
                 break;
             default:
