@@ -87,11 +87,12 @@ def test_streamed_equals_unstreamed_bitwise(bl, batch, steps, tile, pipeline):
 
 @pytest.mark.parametrize("projection", [2, 3])
 @pytest.mark.parametrize("pipeline", [2, 4, 5])
-@pytest.mark.parametrize("batch,steps,tile", [(1, 129, 0), (3, 150, 0), (8, 97, 2), (32, 150, 0), (64, 70, 0)])
+@pytest.mark.parametrize("batch,steps,tile", SHAPES)
 def test_streamed_split_equals_unstreamed_split_bitwise(bl, batch, steps, tile, pipeline, projection):
     """The streamed kernel splits its FP32 operands into bf16 parts after the LDS ring, the
     plain split kernel while staging x (W split at plan creation): the same parts, the same
-    products in the same order, so the gates, and the stack's output, are bitwise the same."""
+    products in the same order, so the gates, and the stack's output, are bitwise the same, for
+    every shape the FP32 streamed path is checked on."""
     x = workloads.make_input(60 + batch, batch, steps)
     layers = workloads.make_layers(61)
     note(f"streamed split projection={projection} pipeline={pipeline} batch={batch} steps={steps} tile={tile}")
@@ -155,15 +156,17 @@ def test_streamed_phase_times(bl, pipeline):
         assert abs((rec[3] - rec[0]) - sum(t["recurrence_launch_ms"][1:])) < 1e-2
 
 
+@pytest.mark.parametrize("projection", [4, 3])
 @pytest.mark.parametrize("pipeline", [2, 4, 3])
-def test_streamed_watchdog_reports_timeout_and_grid_drains(bl, pipeline):
+def test_streamed_watchdog_reports_timeout_and_grid_drains(bl, pipeline, projection):
     """Counter waits forced to time out from the host (watchdog_us = -1: every wait expects a
     count no pass reaches and gives up on its first poll): the kernels finish and the plan
-    reports BILSTM_TIMEOUT; a normal plan afterwards is unaffected."""
+    reports BILSTM_TIMEOUT; a normal plan afterwards is unaffected. Both streamed projection
+    kernels (FP32 and split precision)."""
     x, layers = workloads.make_workload("b8")
     xs = np.ascontiguousarray(x[:, :64])
-    note(f"streamed watchdog first-miss pipeline={pipeline}")
-    plan = bl.Plan(layers, 8, 64, pipeline=pipeline, watchdog_us=-1)
+    note(f"streamed watchdog first-miss pipeline={pipeline} projection={projection}")
+    plan = bl.Plan(layers, 8, 64, pipeline=pipeline, watchdog_us=-1, projection=projection)
     plan.forward(torch.from_numpy(xs).cuda())
     with pytest.raises(bl.BilstmError) as e:
         plan.check()
