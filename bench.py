@@ -177,8 +177,8 @@ def main() -> int:
         return 0
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the stack shards by windows "
-                                   "(see DESIGN.md) but no multi-GPU path is built",
+        print(json.dumps({"error": "one GPU only: the stack would shard by windows (each GPU its own "
+                                   "windows, no collective on the hot path), but no multi-GPU path is built",
                           "n_gpus": args.gpus}))
         return 2
 
