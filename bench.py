@@ -146,6 +146,9 @@ def main() -> int:
     ap.add_argument("--fma-probe", action="store_true",
                     help="only measure the FP32 FMA issue rate the recurrence's bound rests on: shader clocks per "
                          "wave64 FMA per SIMD with 1, 2 and 4 waves per SIMD, on one CU and on every CU")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only measure the matrix-core rates the projection's peaks rest on: bf16 32x32x16 and "
+                         "FP32 32x32x2 MFMAs on every CU with zero, constant and random operands")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate the HBM "
                          "byte counters of a profiler run against a known size")
@@ -160,6 +163,17 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4}))
+        return 0
+
+    if args.mfma_probe:
+        import bidirectional_lstm_sequence_amd as bl
+        rows = []
+        for kind, name, peak in ((0, "bf16 32x32x16", PEAK_BF16_MFMA_TFLOPS), (1, "fp32 32x32x2", PEAK_FP32_MFMA_TFLOPS)):
+            for data, dname in ((0, "zeros"), (1, "ones"), (2, "uniform [-1, 1)")):
+                r = bl.probe_mfma_rate(kind, data, 0, 20000 if kind == 0 else 5000)
+                rows.append({"mfma": name, "operands": dname, **r, "peak_tflops": peak, "frac": r["tflops"] / peak})
+        print(json.dumps({"mfma_probe": rows, "note": "two 256-thread workgroups per CU on every CU, 16 MFMAs per "
+                          "round over 4 independent accumulators, operands in registers; the second of two launches"}))
         return 0
 
     if args.fma_probe:

@@ -32,7 +32,8 @@ EXPORTS = ["bilstm_plan_create", "bilstm_plan_create_ex", "bilstm_forward", "bil
            "bilstm_recur", "bilstm_plan_get_info", "bilstm_check", "bilstm_set_phase_events",
            "bilstm_phase_times", "bilstm_destroy", "bilstm_last_error", "bilstm_pack_layer",
            "bilstm_schedule", "bilstm_probe_exchange", "bilstm_heads_create", "bilstm_heads_forward",
-           "bilstm_heads_destroy", "bilstm_forward_noalloc", "bilstm_probe_fma_rate"]
+           "bilstm_heads_destroy", "bilstm_forward_noalloc", "bilstm_probe_fma_rate",
+           "bilstm_probe_mfma_rate"]
 HEAD_IN, HEAD_MID, HEAD_CLASSES = 256, 128, 7
 
 
@@ -130,6 +131,8 @@ def library():
                                     ctypes.c_size_t, P, ctypes.c_size_t, P], st),
         "bilstm_probe_fma_rate": ([ctypes.c_int, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)], st),
+        "bilstm_probe_mfma_rate": ([ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int32,
+                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -255,6 +258,16 @@ def probe_fma_rate(device: int = 0, waves_per_simd: int = 2, workgroups: int = 1
     _check(lib.bilstm_probe_fma_rate(device, waves_per_simd, workgroups, iterations, ctypes.byref(cpf),
                                      ctypes.byref(ghz)))
     return {"clocks_per_fma": cpf.value, "ghz": ghz.value}
+
+
+def probe_mfma_rate(kind: int, data: int, device: int = 0, iterations: int = 20000) -> dict:
+    """Matrix-core rate in TFLOP/s: kind 0 bf16 32x32x16, 1 FP32 32x32x2; data 0 zeros, 1 ones,
+    2 uniform random operands (see bilstm.h)."""
+    lib = library()
+    tf = ctypes.c_double()
+    ms = ctypes.c_double()
+    _check(lib.bilstm_probe_mfma_rate(device, kind, data, iterations, ctypes.byref(tf), ctypes.byref(ms)))
+    return {"tflops": tf.value, "ms": ms.value}
 
 
 def _stream_handle(stream):

@@ -240,5 +240,7 @@ hipError_t run_exchange_probe(int same_xcd, int round_trips, unsigned long long 
                               double ticks_per_ns, double *one_way_ns, int *xcd_a, int *xcd_b);
 hipError_t run_fma_probe(int waves_per_simd, int workgroups, int iters, double wall_khz, double *clocks_per_fma,
                          double *ghz);
+// matrix-core rate: kind 0 bf16 32x32x16, 1 FP32 32x32x2; data 0 zeros, 1 ones, 2 uniform [-1, 1)
+hipError_t run_mfma_probe(int kind, int data, int iters, int cu_count, double *tflops, double *ms);
 
 }  // namespace bl

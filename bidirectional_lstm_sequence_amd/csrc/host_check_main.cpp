@@ -139,6 +139,10 @@ void check_entry_points(const Weights &wt) {
     expect(bilstm_forward_noalloc(0, 3, 5, wt.layers, x.data(), x.size(), x.data(), y.size(), nullptr) ==
                BILSTM_INVALID_ARGUMENT,
            "forward_noalloc overlap");
+    double ta = 0.0, tb = 0.0;
+    expect(bilstm_probe_mfma_rate(0, 2, 0, 10, &ta, &tb) == BILSTM_INVALID_ARGUMENT, "probe_mfma_rate kind");
+    expect(bilstm_probe_mfma_rate(0, 0, 0, 10, nullptr, &tb) == BILSTM_INVALID_ARGUMENT, "probe_mfma_rate NULL");
+    expect(bilstm_probe_fma_rate(0, 3, 1, 10, &ta, &tb) == BILSTM_INVALID_ARGUMENT, "probe_fma_rate waves");
     bilstm_heads *heads = nullptr;
     expect(bilstm_heads_create(0, nullptr, &heads) == BILSTM_INVALID_ARGUMENT, "heads_create NULL");
     bilstm_heads_destroy(nullptr);

@@ -1045,4 +1045,24 @@ bilstm_status bilstm_probe_fma_rate(int device, int waves_per_simd, int32_t work
     return BILSTM_OK;
 }
 
+bilstm_status bilstm_probe_mfma_rate(int device, int kind, int data, int32_t iterations, double *tflops, double *ms) {
+    if (tflops == nullptr || ms == nullptr) return fail(BILSTM_INVALID_ARGUMENT, "probe_mfma_rate: NULL output");
+    if (kind != 0 && kind != 1) return fail(BILSTM_INVALID_ARGUMENT, "probe_mfma_rate: kind %d is not 0 or 1", kind);
+    if (data < 0 || data > 2) return fail(BILSTM_INVALID_ARGUMENT, "probe_mfma_rate: data %d is not 0, 1 or 2", data);
+    if (iterations < 1 || iterations > 1000000) {
+        return fail(BILSTM_INVALID_ARGUMENT, "probe_mfma_rate: iterations %d out of range", iterations);
+    }
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || device < 0 || device >= count) {
+        return fail(BILSTM_INVALID_ARGUMENT, "probe_mfma_rate: no device %d", device);
+    }
+    if (!is_gfx950(device)) return fail(BILSTM_UNSUPPORTED, "probe_mfma_rate: device %d is not gfx950", device);
+    DeviceScope scope(device);
+    BL_HIP(scope.error(), "probe_mfma_rate: hipSetDevice");
+    int cu_count = 0;
+    BL_HIP(hipDeviceGetAttribute(&cu_count, hipDeviceAttributeMultiprocessorCount, device), "probe_mfma_rate");
+    BL_HIP(run_mfma_probe(kind, data, iterations, cu_count, tflops, ms), "probe_mfma_rate");
+    return BILSTM_OK;
+}
+
 }  // extern "C"

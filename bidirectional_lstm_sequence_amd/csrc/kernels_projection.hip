@@ -40,6 +40,7 @@
 //    the LDS bit, rows swizzled instead of padded), three steps ahead of the products, with
 //    explicit counter waits and bare barriers.
 #include <algorithm>
+#include <vector>
 #include <type_traits>
 
 #include "bilstm_internal.h"
@@ -952,6 +953,66 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
     }
 }
 
+
+// ---- matrix-core rate probe ------------------------------------------------------------------
+//
+// The rate the projection's peak rests on: two 256-thread workgroups per CU, each wave running
+// `iters` rounds of 16 MFMAs over four independent 32x32 accumulators, operands in registers
+// from `in` (4096 floats). KIND 0: v_mfma_f32_32x32x16_bf16; 1: v_mfma_f32_32x32x2f32. The
+// operand values matter: the matrix pipes run slower on random data than on zeros.
+template <int KIND>
+__global__ __launch_bounds__(256, 2) void mfma_rate_kernel(const float *in, float *out, int iters) {
+    const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+    v16f acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+    if constexpr (KIND == 0) {
+        bf16x8 a[2], b[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                a[t][e] = static_cast<__bf16>(in[(gid * 32 + t * 8 + e) & 4095]);
+                b[t][e] = static_cast<__bf16>(in[(gid * 32 + 16 + t * 8 + e) & 4095]);
+            }
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[0], acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[1], acc[1], 0, 0, 0);
+                acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[0], acc[2], 0, 0, 0);
+                acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[1], acc[3], 0, 0, 0);
+            }
+        }
+    } else {
+        v4f a[2], b[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[t][e] = in[(gid * 16 + t * 4 + e) & 4095];
+                b[t][e] = in[(gid * 16 + 8 + t * 4 + e) & 4095];
+            }
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0][u], b[0][u], acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0][u], b[1][u], acc[1], 0, 0, 0);
+                acc[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1][u], b[0][u], acc[2], 0, 0, 0);
+                acc[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1][u], b[1][u], acc[3], 0, 0, 0);
+            }
+        }
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum += acc[i][r];
+    out[gid] = sum;
+}
+
 }  // namespace
 
 hipError_t launch_projection(const ProjArgs &args, int workgroups, hipStream_t stream) {
@@ -1023,6 +1084,48 @@ hipError_t launch_projection(const ProjArgs &args, int workgroups, hipStream_t s
             return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+
+hipError_t run_mfma_probe(int kind, int data, int iters, int cu_count, double *tflops, double *ms) {
+    const int workgroups = 2 * cu_count;
+    const size_t threads = static_cast<size_t>(workgroups) * 256;
+    std::vector<float> host(4096);
+    unsigned int st = 12345u;
+    for (float &v : host) {
+        st = st * 1664525u + 1013904223u;
+        v = data == 0 ? 0.0f : data == 1 ? 1.0f : static_cast<float>(st >> 8) / 8388608.0f - 1.0f;
+    }
+    float *in = nullptr, *out = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    hipError_t e = hipMalloc(&in, host.size() * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc(&out, threads * sizeof(float));
+    if (e == hipSuccess) e = hipMemcpy(in, host.data(), host.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    float elapsed = 0.0f;
+    for (int rep = 0; rep < 2 && e == hipSuccess; ++rep) {  // the first launch warms up
+        e = hipEventRecord(e0, nullptr);
+        if (kind == 0) {
+            hipLaunchKernelGGL(mfma_rate_kernel<0>, dim3(workgroups), dim3(256), 0, nullptr, in, out, iters);
+        } else {
+            hipLaunchKernelGGL(mfma_rate_kernel<1>, dim3(workgroups), dim3(256), 0, nullptr, in, out, iters);
+        }
+        if (e == hipSuccess) e = hipGetLastError();
+        if (e == hipSuccess) e = hipEventRecord(e1, nullptr);
+        if (e == hipSuccess) e = hipEventSynchronize(e1);
+        if (e == hipSuccess) e = hipEventElapsedTime(&elapsed, e0, e1);
+    }
+    if (e0 != nullptr) (void)hipEventDestroy(e0);
+    if (e1 != nullptr) (void)hipEventDestroy(e1);
+    if (in != nullptr) (void)hipFree(in);
+    if (out != nullptr) (void)hipFree(out);
+    if (e != hipSuccess) return e;
+    const double flop_per_mfma = kind == 0 ? 32.0 * 32 * 16 * 2 : 32.0 * 32 * 2 * 2;
+    const double flops = static_cast<double>(threads / 64) * iters * 16 * flop_per_mfma;
+    *ms = elapsed;
+    *tflops = flops / (elapsed * 1e-3) / 1e12;
+    return hipSuccess;
 }
 
 }  // namespace bl

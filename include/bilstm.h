@@ -402,6 +402,17 @@ bilstm_status bilstm_probe_exchange(int device, int same_xcd, int32_t round_trip
 bilstm_status bilstm_probe_fma_rate(int device, int waves_per_simd, int32_t workgroups, int32_t iterations,
                                     double *clocks_per_fma, double *ghz);
 
+/*
+ * Matrix-core rate probe, the rate the projection's peak rests on: two 256-thread workgroups
+ * per CU, every wave running `iterations` rounds of 16 MFMAs over four independent 32x32
+ * accumulators with its operands in registers. kind 0: v_mfma_f32_32x32x16_bf16 (the split
+ * projection's instruction); 1: v_mfma_f32_32x32x2f32 (the FP32 projection's). data 0: zero
+ * operands, 1: ones, 2: uniform in [-1, 1) (a fixed sequence): the matrix pipes run slower on
+ * random operands. Writes the rate in TFLOP/s and the timed launch's milliseconds. Allocates
+ * and frees a few kilobytes of device memory; synchronizes the device.
+ */
+bilstm_status bilstm_probe_mfma_rate(int device, int kind, int data, int32_t iterations, double *tflops, double *ms);
+
 #ifdef __cplusplus
 }
 #endif

@@ -532,6 +532,22 @@ def test_fma_rate_probe(bl):
     assert out[2]["clocks_per_fma"] < 3.0
 
 
+def test_mfma_rate_probe(bl):
+    """The matrix-core rates behind the projection's peaks: bf16 32x32x16 MFMAs on zero operands
+    near the published dense bf16 peak, FP32 32x32x2 near the FP32 one, and random operands no
+    faster than zeros; bad arguments are rejected before any launch."""
+    bf16 = bl.probe_mfma_rate(0, 0, 0, 2000)
+    fp32 = bl.probe_mfma_rate(1, 0, 0, 500)
+    rnd = bl.probe_mfma_rate(0, 2, 0, 2000)
+    note(f"mfma rate probe: bf16 zeros {bf16}, fp32 zeros {fp32}, bf16 uniform {rnd}")
+    assert 1500 < bf16["tflops"] < 2700 and 100 < fp32["tflops"] < 170
+    assert rnd["tflops"] < 1.05 * bf16["tflops"]
+    with pytest.raises(bl.BilstmError):
+        bl.probe_mfma_rate(2, 0)
+    with pytest.raises(bl.BilstmError):
+        bl.probe_mfma_rate(0, 3)
+
+
 @pytest.mark.parametrize("steps", [1, 2, 3, 5, 7])
 @pytest.mark.parametrize("groups,tile", [(1, 1), (1, 2), (1, 4), (2, 2), (4, 1)])
 def test_recurrence_short_sequences(bl, orc, steps, groups, tile):

@@ -312,6 +312,19 @@ def test_entry_points_reject_null_plan(bl):
     lib.bilstm_destroy(None)  # NULL-safe
 
 
+def test_probes_check_arguments_before_the_device(bl):
+    """The measurement probes reject bad arguments with BILSTM_INVALID_ARGUMENT (1) before any
+    device call, so these checks run without a GPU."""
+    lib = bl.library()
+    a, b = ctypes.c_double(), ctypes.c_double()
+    assert lib.bilstm_probe_mfma_rate(0, 2, 0, 10, ctypes.byref(a), ctypes.byref(b)) == 1   # kind
+    assert lib.bilstm_probe_mfma_rate(0, 0, 3, 10, ctypes.byref(a), ctypes.byref(b)) == 1   # data
+    assert lib.bilstm_probe_mfma_rate(0, 0, 0, 0, ctypes.byref(a), ctypes.byref(b)) == 1    # iterations
+    assert lib.bilstm_probe_mfma_rate(0, 0, 0, 10, None, ctypes.byref(b)) == 1              # NULL output
+    assert lib.bilstm_probe_fma_rate(0, 3, 1, 10, ctypes.byref(a), ctypes.byref(b)) == 1    # waves per SIMD
+    assert lib.bilstm_probe_fma_rate(0, 2, 0, 10, ctypes.byref(a), ctypes.byref(b)) == 1    # workgroups
+
+
 def _have_gpu():
     try:
         import torch
