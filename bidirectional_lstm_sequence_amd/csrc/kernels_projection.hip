@@ -8,8 +8,10 @@
 // [1024][kpad] (row d·512 + 4j + g, zero padded to kpad), bias [1024] = Wb + Rb.
 //
 // Design for CDNA4:
-//  * Persistent: one 256-thread workgroup per CU (its registers and LDS keep a second one
-//    out) walks the 128x128 output tiles q = wq, wq + grid, ... The walk is XCD-ordered: the
+//  * Persistent: 256-thread workgroups walk the 128x128 output tiles q = wq, wq + grid, ...,
+//    one or two per CU (190 VGPRs, 72 KB of LDS each), whichever takes fewer tile rounds at
+//    the measured rates: two on a CU finish a round of two tiles in about 1.87 times a lone
+//    workgroup's tile time, so two win unless the last round is mostly empty. The walk is XCD-ordered: the
 //    ids congruent mod 8 run on one XCD, and the workgroups of one XCD take consecutive tiles,
 //    so the eight column tiles of a row block are computed on the same XCD and share its L2
 //    for their x rows.
@@ -22,10 +24,10 @@
 //    row with one ds_read_b128; A and B use the same permutation, so the product is unchanged.
 //    Fragments of the next group are read while the current group's MFMAs run.
 //  * The next tile's first K step is loaded during the current tile's last one.
-//  * Output: a finished tile's sums (plus bias) stay in registers and are written out in
-//    chunks during the next tile's K steps, so the stores overlap compute instead of leaving
-//    the matrix pipe idle while every tile of a round drains at once. In the 32x32 output
-//    layout one store instruction writes two full 128-byte row segments.
+//  * Output: a finished tile's sums (plus bias) go straight to memory; with two workgroups on
+//    a CU the other one's products fill the matrix pipe meanwhile. (Holding the sums until the
+//    next tile's K steps, to overlap the stores with one workgroup per CU, measured slower.)
+//    In the 32x32 output layout one store instruction writes two full 128-byte row segments.
 //  * Every row's K order is fixed and independent of the row's position and of the grid, so a
 //    row's gates are bitwise the same whatever the batch, the number of workgroups or the
 //    tile order. (Layers with 256 inputs: reverse-direction columns sum the reverse half of K
@@ -86,7 +88,7 @@ __device__ __forceinline__ int kstep_at(int n0, int kt) {
 }
 
 template <int KSTEPS>
-__global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a) {
+__global__ __launch_bounds__(kProjThreads, 2) void projection_kernel(ProjArgs a) {
     __shared__ __attribute__((aligned(16))) float lds_a[2][BM * kStride];
     __shared__ __attribute__((aligned(16))) float lds_b[2][BN * kStride];
 
@@ -141,23 +143,31 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a)
         }
     };
 
-    // ---- output of the previous tile, written during the current one ----------------------
-    // 32x32 block layout: register r of lane l is row 8·(r / 4) + 4·(l / 32) + r % 4, column
-    // l % 32 of the block.
-    float pend[2][2][16];
-    int pm0 = 0, pn0 = 0;
-    bool have = false;
-    auto put = [&](int i, int j, int r) {
-        const int m = pm0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int n = pn0 + wn * 64 + j * 32 + (lane & 31);
-        if (m < a.rows) a.gates[static_cast<size_t>(m) * kGateCols + n] = pend[i][j][r];
-    };
-    constexpr int kChunk = 64 / KSTEPS;  // pending values written per K step
-    auto put_chunk = [&](int s) {
+    // ---- a finished tile's sums plus bias to the gates (in the 32x32 output layout register r
+    // of lane l is row 8·(r / 4) + 4·(l / 32) + r % 4, column l % 32 of the block; one store
+    // instruction writes two full 128-byte row segments). The other workgroup on the CU
+    // multiplies meanwhile.
+    auto finish = [&](int m0, int n0, const v16f (&acc)[2][2]) {
+        auto put = [&](auto full_tag) {
 #pragma unroll
-        for (int c = 0; c < kChunk; ++c) {
-            const int idx = s * kChunk + c;
-            put(idx >> 5, (idx >> 4) & 1, idx & 15);
+            for (int j = 0; j < 2; ++j) {
+                const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+                const float bv = a.bias[n];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                        if (decltype(full_tag)::value || m < a.rows) {
+                            a.gates[static_cast<size_t>(m) * kGateCols + n] = acc[i][j][r] + bv;
+                        }
+                    }
+            }
+        };
+        if (m0 + BM <= a.rows) {
+            put(std::true_type{});
+        } else {
+            put(std::false_type{});
         }
     };
 
@@ -209,30 +219,14 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_kernel(ProjArgs a)
                         for (int j = 0; j < 2; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[p][i][e], bf[p][j][e],
                                                                              acc[i][j], 0, 0, 0);
-                if (g == kGroups / 2 && have) put_chunk(kt);
             }
             if (more || next) store(cur ^ 1);
             __syncthreads();
             if (more || next) frags(cur ^ 1, 0, af[0], bf[0]);
         }
 
-        // this tile's sums plus bias become the pending output of the next tile
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const float bv = a.bias[n0 + wn * 64 + j * 32 + (lane & 31)];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) pend[i][j][r] = acc[i][j][r] + bv;
-        }
-        pm0 = m0;
-        pn0 = n0;
-        have = true;
+        finish(m0, n0, acc);
         base = (base + KSTEPS) & 1;
-    }
-    if (have) {
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) put_chunk(s);
     }
 }
 
@@ -1073,12 +1067,21 @@ hipError_t launch_projection(const ProjArgs &args, int workgroups, hipStream_t s
         }
         return hipGetLastError();
     }
+    // One or two workgroups per CU, whichever needs less time by tile rounds: two on a CU
+    // finish a round of two tiles in about 1.87 times one tile's time alone (measured).
+    int nfp32 = nwg;
+    {
+        const int two = std::max(8, std::min(2 * workgroups, (args.tiles + 7) / 8 * 8) / 8 * 8);
+        const long r1 = (args.tiles + nwg - 1) / nwg;
+        const long r2 = (args.tiles + two - 1) / two;
+        if (15 * r2 < 8 * r1) nfp32 = two;
+    }
     switch (args.kpad / kProjTileK) {
         case 2:
-            hipLaunchKernelGGL(projection_kernel<2>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
+            hipLaunchKernelGGL(projection_kernel<2>, dim3(nfp32), dim3(kProjThreads), 0, stream, args);
             break;
         case 8:
-            hipLaunchKernelGGL(projection_kernel<8>, dim3(nwg), dim3(kProjThreads), 0, stream, args);
+            hipLaunchKernelGGL(projection_kernel<8>, dim3(nfp32), dim3(kProjThreads), 0, stream, args);
             break;
         default:
             return hipErrorInvalidValue;
