@@ -101,7 +101,7 @@ struct bilstm_plan {
     int proj_workgroups_streamed = 0;
     size_t reserve_lds = 0;  // dynamic LDS of a recurrence workgroup (keeps its CU to itself)
     LibraryProjection *library = nullptr;  // vendor-GEMM projection (comparator), if chosen
-    int proj_workgroups = 0;         // persistent projection workgroups on an idle GPU
+    int proj_workgroups = 0;         // CUs for the persistent projection on an idle GPU
     int proj_workgroups_sliced = 0;  // ... beside the other slices' recurrences
     uint32_t epoch = 0;  // flags of the next pass start above this value
     unsigned long long timeout_ticks = 0;
@@ -691,8 +691,9 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
     info.proj_tile_m = kProjTileM;
     info.proj_tile_n = kProjTileN;
     p->info = info;
-    // One persistent projection workgroup per CU; beside the recurrences of the other slices
-    // (each of their workgroups keeps a CU to itself), one per CU they leave free.
+    // The projection's persistent grid counts CUs (its launch puts one or two workgroups on
+    // each): every CU, or beside the recurrences of the other slices (each of their workgroups
+    // keeps a CU to itself) the CUs they leave free.
     p->proj_workgroups = cu_count;
     {
         const int slice_tiles = (info.slice_windows + info.recur_tile - 1) / info.recur_tile;
