@@ -331,6 +331,23 @@ def test_split_projection_batch_invariant(bl):
     assert np.array_equal(y1[0].view(np.uint32), y32[9].view(np.uint32))
 
 
+@pytest.mark.parametrize("layer_index", [0, 1])
+def test_fp32_projection_rows_independent_of_the_launch(bl, layer_index):
+    """The FP32 projection runs one workgroup per CU when few tile rounds are needed (4,000 rows:
+    256 tiles) and two when that is faster (40,000 rows: 2,504 tiles); a row's gates are
+    bitwise the same either way."""
+    layers = workloads.make_layers(77)
+    width = 60 if layer_index == 0 else 256
+    x = np.tanh(np.random.default_rng(5).standard_normal((40000, width))).astype(np.float32)
+    note(f"fp32 projection launch invariance layer={layer_index}")
+    out = {}
+    for rows in (4000, 40000):
+        plan = bl.Plan(layers, rows, 1, projection=4)
+        out[rows] = plan.project(layer_index, torch.from_numpy(np.ascontiguousarray(x[:rows])).cuda()).cpu().numpy()
+        plan.close()
+    assert np.array_equal(out[4000].view(np.uint32), out[40000][:4000].view(np.uint32))
+
+
 def test_stack_with_library_projection_matches_oracle(bl, orc):
     """The whole stack with the vendor-GEMM projection (comparator) against the oracle."""
     x, layers = workloads.make_workload("b8")
