@@ -274,7 +274,8 @@ constexpr int kSplitPlane = BM * 16;  // bf16 elements of one plane of one stage
 __device__ __forceinline__ int split_half(int r, int h) { return h ^ ((r >> 2) & 1) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int split_slot(int r, int h) { return r * 16 + (split_half(r, h) << 3); }
 
-// Wait until at most n of this wave's vector memory operations are outstanding (0 <= n <= 15).
+// Wait until at most n of this wave's vector memory operations are outstanding (n <= 7; any
+// other n waits for all of them).
 __device__ __forceinline__ void wait_vm(int n) {
     switch (n) {
         case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
@@ -463,7 +464,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void projection_split_kernel(Proj
     // s + 1 whole (every wave's W loads landed, every wave's x written) and frees stage s's slot.
     // Per stage the loads go out in the order W(s + 2), x(s + 4), so when stage s + 1's W and x
     // have landed, only x(s + 3), W(s + 2) and x(s + 4) may still be in flight. The stages past
-    // the last one only load zeros into slots nobody reads again.
+    // the last one load into slots nobody reads again (x as zeros, W rows in bounds).
     constexpr int kAfter = PARTS + 4;
     auto step = [&](int s, v4f (&x_next)[2], v4f (&x_far)[2]) {
         issue_w(s + 2, (s + 2) % kSplitStages);
