@@ -570,6 +570,13 @@ bilstm_status take_timeout_report(bilstm_plan *p, const char *context) {
                 (seen & (1u << kErrCounter)) ? "chunk counter " : "", (seen & (1u << kErrProgress)) ? "progress" : "");
 }
 
+// Event flags. An event that only orders this plan's streams on its own device needs no
+// system-scope fence (by default every record writes back and invalidates the L2, several
+// microseconds on the stream each time, and the next kernel starts on a cold cache); nor does
+// an event that only times. `done`, which the host waits on, keeps the default.
+constexpr unsigned int kOrderEvent = hipEventDisableTiming | hipEventDisableSystemFence;
+constexpr unsigned int kTimingEvent = hipEventDisableSystemFence;
+
 // The end of a call that enqueued work: the plan's completion event goes on the caller's
 // stream (after any join), whatever `st` is, so bilstm_check waits for all of it.
 bilstm_status mark_done(bilstm_plan *p, hipStream_t stream, bilstm_status st, const char *context) {
@@ -774,21 +781,21 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
     }
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking);
     for (int l = 0; l < kLayers && e == hipSuccess; ++l) {
-        e = hipEventCreateWithFlags(&p->fork[l], hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->join[l], hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreate(&p->ev_proj[l]);
-        if (e == hipSuccess) e = hipEventCreate(&p->ev_recur[l]);
-        if (e == hipSuccess) e = hipEventCreate(&p->ev_launch0[l]);
-        if (e == hipSuccess) e = hipEventCreate(&p->ev_launch1[l]);
+        e = hipEventCreateWithFlags(&p->fork[l], kOrderEvent);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->join[l], kOrderEvent);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_proj[l], kTimingEvent);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_recur[l], kTimingEvent);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_launch0[l], kTimingEvent);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_launch1[l], kTimingEvent);
     }
-    if (e == hipSuccess) e = hipEventCreate(&p->ev_start);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_start, kTimingEvent);
     if (info.slices > 1) {
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->slice_fork, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->slice_fork, kOrderEvent);
         for (int i = 0; i < info.slices && e == hipSuccess; ++i) {
             // slice 0 runs on the caller's stream; each other slice gets a stream of its own
             if (i > 0) e = hipStreamCreateWithFlags(&p->slice_stream[i], hipStreamNonBlocking);
-            if (e == hipSuccess) e = hipEventCreateWithFlags(&p->slice_first[i], hipEventDisableTiming);
-            if (e == hipSuccess) e = hipEventCreateWithFlags(&p->slice_join[i], hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&p->slice_first[i], kOrderEvent);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&p->slice_join[i], kOrderEvent);
         }
         // A recurrence workgroup claims enough LDS that no projection workgroup fits beside it
         // on its CU: the projections of other slices then run only on CUs no recurrence uses,
@@ -822,11 +829,11 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
             e = hipMemset(p->progress, 0, kProgressStride * 2 * static_cast<size_t>(batch) * sizeof(unsigned long long));
         }
         if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->proj_stream, hipStreamNonBlocking);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->proj_fork, hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->proj_join, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->proj_fork, kOrderEvent);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->proj_join, kOrderEvent);
         for (int l = 0; l < kLayers && e == hipSuccess; ++l) {
-            e = hipEventCreateWithFlags(&p->layer_done[l], hipEventDisableTiming);
-            if (e == hipSuccess) e = hipEventCreateWithFlags(&p->proj_done[l], hipEventDisableTiming);
+            e = hipEventCreateWithFlags(&p->layer_done[l], kOrderEvent);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&p->proj_done[l], kOrderEvent);
         }
         // Each recurrence workgroup claims enough LDS that no projection workgroup fits beside
         // it, and each streamed projection workgroup enough that no second one shares its CU:
