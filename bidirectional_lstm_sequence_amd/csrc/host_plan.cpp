@@ -798,8 +798,9 @@ bilstm_status bilstm_plan_create_ex(int device, uint32_t batch, uint32_t steps,
             if (e == hipSuccess) e = hipEventCreateWithFlags(&p->slice_join[i], kOrderEvent);
         }
         // A recurrence workgroup claims enough LDS that no projection workgroup fits beside it
-        // on its CU: the projections of other slices then run only on CUs no recurrence uses,
-        // and the latency-bound recurrence keeps its CU's issue slots and LDS to itself.
+        // on its CU (every projection kernel of the library takes at least kProjLdsBytes): the
+        // projections of other slices then run only on CUs no recurrence uses, and the
+        // latency-bound recurrence keeps its CU's issue slots and LDS to itself.
         if (e == hipSuccess) {
             p->reserve_lds = kCuLdsBytes - kProjLdsBytes + 4096;
             e = recurrence_allow_lds(info.recur_groups, info.recur_tile, p->reserve_lds);

@@ -315,8 +315,13 @@ __global__ __launch_bounds__(kSplitThreads, 2) void projection_split_kernel(Proj
     constexpr int kStage = 2 * PARTS * kSplitPlane;     // x planes, then W planes
     constexpr bool kMaskK = KSTEPS * BK != kWidth;      // layer 0: k past the 60 inputs reads 0
     // one LDS array (the ring, then the bias): with a second one the compiler waits for every
-    // LDS-bound load before each ring read, as it then tells the arrays apart but not the slots
-    __shared__ __attribute__((aligned(16))) __bf16 ring[kSplitStages * kStage + 2 * kGateCols];
+    // LDS-bound load before each ring read, as it then tells the arrays apart but not the slots.
+    // At least kProjLdsBytes (two parts need less): a recurrence workgroup's LDS reservation
+    // keeps any projection workgroup of that size off its CU.
+    constexpr int kRingElems = kSplitStages * kStage + 2 * kGateCols;
+    constexpr int kLdsElems = kRingElems * 2 >= static_cast<int>(kProjLdsBytes) ? kRingElems
+                                                                               : static_cast<int>(kProjLdsBytes) / 2;
+    __shared__ __attribute__((aligned(16))) __bf16 ring[kLdsElems];
     float *const sbias = reinterpret_cast<float *>(ring + kSplitStages * kStage);
 
     const int nwg = gridDim.x;  // a multiple of 8
