@@ -18,8 +18,6 @@ import statistics
 import sys
 import time
 
-import numpy as np
-
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -27,7 +25,6 @@ import workloads  # noqa: E402
 
 PEAK_FP32_MFMA_TFLOPS = 157.3      # MI355X dense FP32 matrix peak (published)
 PEAK_FP32_VECTOR_TFLOPS = 157.3    # MI355X FP32 vector peak (published)
-CU_COUNT_NOMINAL = 256
 CLOCK_GHZ = 2.4
 # FP32 FMA per clock per CU implied by the published vector peak:
 # 157.3e12 / (256 CUs x 2.4e9 Hz x 2 flop) = 128
@@ -36,7 +33,6 @@ FMA_PER_CLK_PER_CU = 128
 RECUR_FMA_PER_FRAME_DIR = 512 * 128                   # R·h per step per direction
 HEAD_FLOP_PER_FRAME = 2 * (256 * 128 + 128 * 128 + 128 * 7)   # segmentation heads
 HEAD_BYTES_PER_FRAME = 256 * 4 + 7 * 4                          # stack output read, log-probs written
-PEAK_HBM_GBS = 8000.0
 
 
 def projection_flops(frames: int) -> float:

@@ -9,7 +9,6 @@ mutant. Everything runs on the CPU; the real oracle is never modified.
 import os
 import shutil
 
-import numpy as np
 import pytest
 
 import oracle
