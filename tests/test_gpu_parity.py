@@ -348,6 +348,30 @@ def test_fp32_projection_rows_independent_of_the_launch(bl, layer_index):
     assert np.array_equal(out[4000].view(np.uint32), out[40000][:4000].view(np.uint32))
 
 
+def test_stack_at_the_largest_accepted_size(bl, orc):
+    """1023 windows of 4096 steps, the largest batch of that length the 32-bit indexing
+    accepts (4,190,208 rows; 1024 windows are refused): the default plan's forward, every
+    output finite and within [-1, 1], and the first, a middle and the last window element by
+    element against the oracle."""
+    batch, steps = 1023, 4096
+    layers = workloads.make_layers(4099)
+    x = workloads.make_input(4099, batch, steps)
+    note(f"largest size batch={batch} steps={steps}")
+    plan = bl.Plan(layers, batch, steps)
+    y = plan.forward(torch.from_numpy(x).cuda())
+    plan.check()
+    info = plan.info()
+    assert bool(torch.isfinite(y).all()) and float(y.abs().max()) <= 1.0
+    sample = [0, 511, 1022]
+    ref = orc.stack(x, layers, threads=len(sample), windows=sample)
+    for i, w in enumerate(sample):
+        err = assert_close(y[w].cpu().numpy(), ref[i], f"largest size window {w}")
+        note(f"largest size window {w} max abs err {err:.3e} plan {info}")
+    plan.close()
+    del y
+    torch.cuda.empty_cache()
+
+
 def test_stack_with_library_projection_matches_oracle(bl, orc):
     """The whole stack with the vendor-GEMM projection (comparator) against the oracle."""
     x, layers = workloads.make_workload("b8")

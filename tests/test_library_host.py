@@ -297,8 +297,12 @@ def test_plan_create_argument_checks_without_gpu(bl):
     assert lib.bilstm_plan_create(0, 1, 589, arr, ctypes.byref(h)) == 2
     assert "layer 2 R" in bl.last_error()
     arr[2].r_len = arr[2].r_len + 1
-    # more rows than 32-bit indexing allows
+    # more rows than 32-bit indexing allows: batch·steps·1024 must stay below 2^32, so 1024
+    # windows of 4096 steps are one row too many and 1023 windows pass the size checks
     assert lib.bilstm_plan_create(0, 1 << 16, 1 << 10, arr, ctypes.byref(h)) == 3
+    assert lib.bilstm_plan_create(0, 1024, 4096, arr, ctypes.byref(h)) == 3
+    if not _have_gpu():
+        assert lib.bilstm_plan_create(0, 1023, 4096, arr, ctypes.byref(h)) == 4
     # with valid arguments and no GPU here, the device check answers
     st = lib.bilstm_plan_create(0, 1, 589, arr, ctypes.byref(h))
     if not _have_gpu():
