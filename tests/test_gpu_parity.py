@@ -372,6 +372,30 @@ def test_stack_at_the_largest_accepted_size(bl, orc):
     torch.cuda.empty_cache()
 
 
+def test_streamed_stack_past_two_gigabytes_of_input(bl, orc):
+    """64 windows of 34,000 steps with streamed gates: the layer inputs exceed 2 GiB, so the
+    streamed projection's 32-bit byte offsets pass 2^31. The last window against the oracle;
+    the first and the last bitwise equal to the same window run alone."""
+    batch, steps = 64, 34000
+    layers = workloads.make_layers(34001)
+    x = workloads.make_input(34001, batch, steps)
+    note(f"streamed past 2 GiB batch={batch} steps={steps}")
+    plan = bl.Plan(layers, batch, steps)
+    info = plan.info()
+    assert info["pipeline"] == 1
+    y = plan.forward(torch.from_numpy(x).cuda())
+    plan.check()
+    plan.close()
+    assert bool(torch.isfinite(y).all()) and float(y.abs().max()) <= 1.0
+    for w in (0, batch - 1):
+        one, _ = run_stack(bl, np.ascontiguousarray(x[w:w + 1]), layers, projection=info["projection"])
+        assert np.array_equal(one[0].view(np.uint32), y[w].cpu().numpy().view(np.uint32)), f"window {w}"
+    err = assert_close(y[batch - 1].cpu().numpy(), orc.stack(x, layers, windows=[batch - 1])[0], "last window")
+    note(f"streamed past 2 GiB last window max abs err {err:.3e}")
+    del y
+    torch.cuda.empty_cache()
+
+
 def test_stack_with_library_projection_matches_oracle(bl, orc):
     """The whole stack with the vendor-GEMM projection (comparator) against the oracle."""
     x, layers = workloads.make_workload("b8")
