@@ -68,3 +68,19 @@ def test_forward_noalloc_rejects_sizes_beyond_its_scratch(bl):
     assert e.value.name == "BILSTM_DIMENSION_OVERFLOW" and "static scratch" in str(e.value)
     torch.cuda.synchronize()
     assert bool(torch.all(y == 0)), "a rejected call wrote its output"
+
+
+def test_forward_noalloc_at_its_largest_size(bl):
+    """One window of 23,227 steps: exactly the rows the static scratch holds, bitwise equal to
+    a plan's forward."""
+    layers = workloads.make_layers(504)
+    b, t = 1, 23227
+    x = torch.from_numpy(workloads.make_input(505, b, t)).cuda()
+    y = torch.full((b, t, 256), float("nan"), dtype=torch.float32, device="cuda")
+    note(f"forward_noalloc batch={b} steps={t} (the scratch's limit)")
+    bl.forward_noalloc(bl.device_layers(layers), x, y)
+    torch.cuda.synchronize()
+    with bl.Plan(layers, b, t) as plan:
+        ref = plan.forward(x)
+        plan.check()
+    assert torch.equal(y.view(torch.int32), ref.view(torch.int32))
