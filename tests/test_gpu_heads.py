@@ -64,6 +64,26 @@ def test_heads_match_oracle(bl, orc, rows):
     note(f"heads rows={rows} max abs err {err:.3e}")
 
 
+def test_heads_at_the_long_workload_size(bl, orc):
+    """262,144 rows (the 64 x 4096 stack output): sampled rows (both ends and a random set)
+    against the oracle, and two runs bitwise equal."""
+    rows = 64 * 4096
+    head = workloads.make_heads(4096)
+    y = np.random.default_rng(4096).uniform(-1, 1, size=(rows, 256)).astype(np.float32)
+    note(f"heads rows={rows}")
+    h = bl.Heads(head)
+    yd = torch.from_numpy(y).cuda()
+    out = h.forward(yd).cpu().numpy()
+    again = h.forward(yd).cpu().numpy()
+    h.close()
+    assert np.array_equal(out.view(np.uint32), again.view(np.uint32))
+    pick = np.unique(np.concatenate([np.arange(256), np.arange(rows - 256, rows),
+                                     np.random.default_rng(7).choice(rows, 2048, replace=False)]))
+    ref = orc.heads(np.ascontiguousarray(y[pick]), head)
+    err = assert_close(out[pick], ref, f"heads rows={rows} (sampled)")
+    note(f"heads rows={rows} sampled {len(pick)} max abs err {err:.3e}")
+
+
 def test_heads_zero_rows_and_position_invariance(bl):
     """No rows is a no-op; a row's outputs do not depend on where in the batch it sits."""
     head = workloads.make_heads(9)
