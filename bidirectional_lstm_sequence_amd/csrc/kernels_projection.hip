@@ -656,8 +656,15 @@ __device__ __forceinline__ void split8(v4f lo, v4f hi, bf16x8 (&out)[PARTS]) {
 // PARTS = 0: FP32 MFMA products; 2 or 3: split precision as projection_split_kernel, the
 // FP32 operands split in registers after the LDS ring.
 template <int KSTEPS, int PARTS>
-__global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(ProjArgs a) {
-    __shared__ __attribute__((aligned(16))) float lds[kStages * kStageFloats];
+__global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(ProjArgs a, unsigned int lead0) {
+    // The K-step ring, then thread 0's walk state and the two tiles it chose for the whole
+    // workgroup. One LDS object: with a second one the compiler no longer tells the ring's
+    // fragment reads from the loads still writing later stages and waits for all of them.
+    constexpr int kWalkFloats = 16;
+    static_assert(sizeof(StreamWalk) <= 12 * sizeof(float) && alignof(StreamWalk) <= sizeof(float), "walk state");
+    __shared__ __attribute__((aligned(16))) float lds[kStages * kStageFloats + kWalkFloats];
+    StreamWalk &walk_state = *reinterpret_cast<StreamWalk *>(&lds[kStages * kStageFloats]);
+    int *const order_slot = reinterpret_cast<int *>(&lds[kStages * kStageFloats + 12]);
     // K steps loaded ahead of the one being multiplied
     constexpr int LA = KSTEPS > kStages - 1 ? kStages - 1 : KSTEPS;
     constexpr int kHalf = KSTEPS / 2;
@@ -731,7 +738,19 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
     // blocks of 32 x 32 (128 columns: 2 x 2 waves of 64 x 64; 64: 2 x 2 of 64 x 32; 32: 4 x 1
     // of 32 x 32). Every block runs the same MFMA sequence over K whatever the width, so a
     // gate's sum does not depend on the tile it falls in.
-    auto run = [&](const StreamTile &t, int q, auto width_tag) {
+    // The workgroup's tiles first + k·nwg, k = 0 .. my_tiles - 1, in the walk's order (protocol.h:
+    // with lead0 > 0 the tiles whose rows exist first while the previous layer still runs).
+    const int my_tiles = first < a.tiles ? (a.tiles - first + nwg - 1) / nwg : 0;
+    const bool walk = kHalves && lead0 > 0 && a.progress != nullptr && my_tiles > 1;
+    auto tile_of = [&](int k) { return stream_tile(a, first + k * nwg); };
+    // steps of the previous layer both directions of a window have run, from their words
+    auto both_directions = [&](unsigned long long s0, unsigned long long s1) {
+        const uint32_t p0 = progress_steps(s0, a.progress_pass, static_cast<uint32_t>(a.steps));
+        const uint32_t p1 = progress_steps(s1, a.progress_pass, static_cast<uint32_t>(a.steps));
+        return p0 < p1 ? p0 : p1;
+    };
+
+    auto run = [&](const StreamTile &t, const StreamTile &tn, bool next, int taken, auto width_tag) {
         constexpr int TN = decltype(width_tag)::value;
         constexpr int WN = TN >= 64 ? 2 : 1;
         constexpr int WM = 4 / WN;
@@ -750,9 +769,6 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
         const unsigned long long *pc = watched_word(a, t, lane);
         const unsigned long long seen_cur =
             pc != nullptr ? __hip_atomic_load(pc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : ~0ull;
-        const int qn = q + nwg;
-        const bool next = qn < a.tiles;
-        const StreamTile tn = stream_tile(a, next ? qn : q);
         const unsigned long long *pn = next ? watched_word(a, tn, lane) : nullptr;
         const unsigned long long seen_next =
             pn != nullptr ? __hip_atomic_load(pn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : ~0ull;
@@ -933,6 +949,14 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
             }
         }
         __builtin_amdgcn_s_waitcnt(0);
+        // the tile after the next one, from the progress this tile's start saw (lanes 0 and 1
+        // of wave 0 watch both directions of the tile's first window)
+        const unsigned long long seen_other = __shfl(seen_cur, 1);
+        if (tid == 0 && next) {
+            const uint32_t p = walk ? both_directions(seen_cur, seen_other) : 0u;
+            order_slot[0] = stream_walk_after(walk_state, taken, p,
+                                              static_cast<uint32_t>(chunk_need(a.steps, a.chunk, t.c)));
+        }
         __syncthreads();
         // the tiles of a counter's chunk add kReadyPerPass per pass in all: TN / 32 each
         if (tid == 0) {
@@ -941,15 +965,38 @@ __global__ __launch_bounds__(kProjThreads, 1) void projection_stream_kernel(Proj
         }
     };
 
-    for (int q = first; q < a.tiles; q += nwg) {
-        const StreamTile t = stream_tile(a, q);
-        if (t.width == BN) {
-            run(t, q, TileWidth<BN>{});
-        } else if (t.width == BN / 2) {
-            run(t, q, TileWidth<BN / 2>{});
-        } else {
-            run(t, q, TileWidth<BN / 4>{});
+    if (tid == 0) {
+        const int mid = walk ? stream_walk_mid(my_tiles, a.steps, a.chunk, [&](int k) { return tile_of(k).c; }) : 0;
+        stream_walk_init(walk_state, my_tiles, mid, a.steps, lead0, walk);
+        uint32_t p = 0;
+        if (walk) {
+            const unsigned long long *w0 = a.progress + kProgressStride * 2 * tile_of(0).w0;
+            p = both_directions(__hip_atomic_load(w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                                __hip_atomic_load(w0 + kProgressStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         }
+        stream_walk_start(walk_state, p, order_slot[0], order_slot[1]);
+    }
+    __syncthreads();
+    // order_slot[0] is rewritten at the end of the next tile, after every wave has read it here.
+    // The tiles are the same in every lane: read into scalar registers, so that everything
+    // derived from them (row blocks, K offsets, the width dispatch) stays scalar.
+    int kcur = __builtin_amdgcn_readfirstlane(order_slot[0]);
+    int knext = __builtin_amdgcn_readfirstlane(order_slot[1]);
+    for (int taken = 0; kcur >= 0; ++taken) {
+        const StreamTile t = tile_of(kcur);
+        const bool next = knext >= 0;
+        const StreamTile tn = tile_of(next ? knext : kcur);
+        if (t.width == BN) {
+            run(t, tn, next, taken, TileWidth<BN>{});
+        } else if (t.width == BN / 2) {
+            run(t, tn, next, taken, TileWidth<BN / 2>{});
+        } else {
+            run(t, tn, next, taken, TileWidth<BN / 4>{});
+        }
+        // written by thread 0 before the tile's last barrier
+        const int kafter = next ? __builtin_amdgcn_readfirstlane(order_slot[0]) : -1;
+        kcur = knext;
+        knext = kafter;
     }
 }
 
@@ -1015,6 +1062,12 @@ __global__ __launch_bounds__(256, 2) void mfma_rate_kernel(const float *in, floa
 
 }  // namespace
 
+// The walk's assumed lead (previous-layer steps per streamed tile: about 40 measured for the
+// three-part split and 20-25 for FP32 products at 0.44-0.46 us per step) and the tiles per
+// workgroup from which it is used.
+constexpr unsigned int kWalkLead = 64;
+constexpr int kWalkMinTiles = 8;
+
 hipError_t launch_projection(const ProjArgs &args, int workgroups, hipStream_t stream) {
     if (args.tiles <= 0) return hipSuccess;
     // a multiple of 8 (the XCD-ordered walk), at most one workgroup per tile group of 8
@@ -1027,8 +1080,14 @@ hipError_t launch_projection(const ProjArgs &args, int workgroups, hipStream_t s
             (args.split_parts != 0 && args.split_parts != 2 && args.split_parts != 3)) {
             return hipErrorInvalidValue;
         }
+        // Beside the previous layer's recurrence (progress words), workgroups with several tiles
+        // walk: the tiles whose rows exist first (protocol.h), assuming kWalkLead steps of that
+        // layer per tile until one is measured. With fewer tiles per workgroup the projection
+        // ends well before the recurrence that reads it, and the plain order is kept.
+        const int per_wg = (args.tiles + nwg - 1) / nwg;
+        const unsigned int lead0 = args.progress != nullptr && per_wg >= kWalkMinTiles ? kWalkLead : 0u;
 #define BL_STREAM(KS, PARTS) \
-    hipLaunchKernelGGL((projection_stream_kernel<KS, PARTS>), dim3(nwg), dim3(kProjThreads), 0, stream, args)
+    hipLaunchKernelGGL((projection_stream_kernel<KS, PARTS>), dim3(nwg), dim3(kProjThreads), 0, stream, args, lead0)
         switch ((args.kpad / kProjTileK) * 4 + args.split_parts) {
             case 2 * 4 + 0: BL_STREAM(2, 0); break;
             case 2 * 4 + 2: BL_STREAM(2, 2); break;

@@ -19,6 +19,8 @@
 //    recurrence): {layer pass << 32 | steps whose output has completed}, one per window and
 //    direction. A reader of layer pass p needs a word >= (p << 32 | steps it needs): words of
 //    earlier passes are smaller whatever their step count.
+// 4. Tile order of a streamed projection workgroup beside the previous layer's recurrence:
+//    the tiles whose rows exist first, then the rest in consumption order (section 4 below).
 #pragma once
 
 #include <cstdint>
@@ -84,6 +86,132 @@ BL_HD inline uint64_t progress_pass_bits(uint32_t layer_pass) { return static_ca
 BL_HD inline uint64_t progress_word(uint64_t pass_bits, uint32_t done) { return pass_bits | done; }
 BL_HD inline bool progress_reached(uint64_t seen, uint64_t pass_bits, uint32_t need) {
     return seen >= (pass_bits | need);
+}
+// Steps of pass `pass_bits` that a word shows: 0 for a word of an earlier pass, all `steps` for
+// one of a later pass (that pass can only start once this one has ended).
+BL_HD inline uint32_t progress_steps(uint64_t seen, uint64_t pass_bits, uint32_t steps) {
+    if (seen < pass_bits) return 0;
+    if ((seen >> 32) > (pass_bits >> 32)) return steps;
+    const uint32_t done = static_cast<uint32_t>(seen);
+    return done < steps ? done : steps;
+}
+
+// ---- 4. tile order of a streamed projection workgroup ---------------------------------------
+// A persistent workgroup's streamed tiles k = 0 .. n-1 are numbered in the recurrence's
+// consumption order (their chunk never falls as k rises). Tile k can be computed once the
+// previous layer has run chunk_need(c_k) steps in both directions: the rows of the middle
+// chunks exist from about half of that layer on, those of the first and of the last chunk only
+// at its end. Taken in consumption order, a workgroup's first tile (chunk 0) holds it through
+// the whole second half of the previous layer. The walk instead starts at `mid`, the last tile
+// of least need, and goes down (mid, mid - 1, ...) while the tile being chosen would still end
+// before the previous layer does; the remaining tiles then follow in consumption order
+// (0 .. lo - 1, then mid + 1 .. n - 1), so chunk 0 starts just before its rows are complete.
+// Every tile is taken once, and a tile's sums do not depend on when it is taken.
+BL_HD inline int chunk_need(int steps, int chunk, int c) {
+    const int near = c * chunk + chunk < steps ? c * chunk + chunk : steps;  // own direction
+    const int far = steps - c * chunk;                                      // the other one
+    return near > far ? near : far;
+}
+
+// The last tile of least need; chunk_of(k) is tile k's chunk. near - far rises with the chunk,
+// so the least need is at the first tile where near >= far or at the tile before it.
+template <class ChunkOf>
+BL_HD inline int stream_walk_mid(int n, int steps, int chunk, ChunkOf chunk_of) {
+    int a = 0, b = n;
+    while (a < b) {
+        const int m = (a + b) / 2;
+        const int c = chunk_of(m);
+        const int near = c * chunk + chunk < steps ? c * chunk + chunk : steps;
+        if (near >= steps - c * chunk) {
+            b = m;
+        } else {
+            a = m + 1;
+        }
+    }
+    if (a == n) return n - 1;
+    if (a > 0 && chunk_need(steps, chunk, chunk_of(a - 1)) < chunk_need(steps, chunk, chunk_of(a))) return a - 1;
+    // the last tile of tile a's chunk
+    const int c = chunk_of(a);
+    int lo = a, hi = n;
+    while (lo < hi) {
+        const int m = (lo + hi) / 2;
+        if (chunk_of(m) > c) {
+            hi = m;
+        } else {
+            lo = m + 1;
+        }
+    }
+    return lo - 1;
+}
+
+struct StreamWalk {
+    int n;                   // the workgroup's tiles
+    int lo, hi;              // the walk has taken tiles [lo, hi)
+    int next_in_order;       // the next tile in consumption order, [lo, hi) skipped
+    int steps;               // of the previous layer
+    bool walking;
+    uint32_t lead0;          // steps of the previous layer per tile, assumed until measured
+    uint32_t lead;           // the largest measured so far
+    uint32_t last_progress;  // progress seen at the previous tile's start
+    uint32_t last_need;      // the previous tile's chunk_need
+};
+
+// walk = false: plain consumption order.
+BL_HD inline void stream_walk_init(StreamWalk &w, int n, int mid, int steps, uint32_t lead0, bool walk) {
+    w.n = n;
+    w.lo = mid + 1;
+    w.hi = mid + 1;
+    w.next_in_order = 0;
+    w.steps = steps;
+    w.walking = walk && n > 1;
+    w.lead0 = lead0;
+    w.lead = 0;
+    w.last_progress = 0;
+    w.last_need = 0;
+}
+
+// The next tile (-1: none left). `progress` = steps the previous layer had run when the
+// estimate starts, `lead` = steps it runs per tile of this workgroup, `horizon` = tiles from
+// that moment to the end of the tile being chosen.
+BL_HD inline int stream_walk_next(StreamWalk &w, uint32_t progress, uint32_t lead, int horizon) {
+    if (w.walking) {
+        if (w.lo > 0 && static_cast<uint64_t>(progress) + static_cast<uint64_t>(horizon) * lead <
+                            static_cast<uint64_t>(w.steps)) {
+            return --w.lo;
+        }
+        w.walking = false;
+    }
+    if (w.next_in_order == w.lo) w.next_in_order = w.hi;
+    return w.next_in_order < w.n ? w.next_in_order++ : -1;
+}
+
+// Steps the previous layer ran during one tile: from the tile's start (progress `before`), or
+// from when its rows were complete (`ready_at`) if it waited for them, to `now`.
+BL_HD inline uint32_t stream_walk_lead(uint32_t now, uint32_t before, uint32_t ready_at) {
+    const uint32_t from = before > ready_at ? before : ready_at;
+    return now > from ? now - from : 0;
+}
+
+// A workgroup's first two tiles, chosen at its start (previous layer at `progress`): the first
+// ends one tile from now, the second two.
+BL_HD inline void stream_walk_start(StreamWalk &w, uint32_t progress, int &first, int &second) {
+    first = stream_walk_next(w, progress, w.lead0, 1);
+    second = first < 0 ? -1 : stream_walk_next(w, progress, w.lead0, 2);
+}
+
+// At the end of the workgroup's i-th tile (i = 0 first), whose start saw `progress` and whose
+// rows needed `need` steps: the tile after the next one, which ends three tiles after that
+// start. From the second tile on, the lead is the largest one measured.
+BL_HD inline int stream_walk_after(StreamWalk &w, int i, uint32_t progress, uint32_t need) {
+    uint32_t lead = w.lead0;
+    if (i > 0) {
+        const uint32_t m = stream_walk_lead(progress, w.last_progress, w.last_need);
+        w.lead = m > w.lead ? m : w.lead;
+        lead = w.lead;
+    }
+    w.last_progress = progress;
+    w.last_need = need;
+    return stream_walk_next(w, progress, lead, 3);
 }
 
 }  // namespace bl

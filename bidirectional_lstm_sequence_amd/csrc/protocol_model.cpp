@@ -18,6 +18,7 @@
 #include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <thread>
@@ -365,12 +366,141 @@ int bilstm_model_progress(int windows, int steps, int chunk, int every, uint32_t
     return 0;
 }
 
+// The tile order of one streamed projection workgroup, chosen with the walk functions as the
+// kernel chooses it, against a previous layer that runs `rate` steps per unit of time from time
+// 0 (both directions alike). The workgroup starts at `start`; a tile starts computing once its
+// rows exist and takes `tile_time`. chunks[k] is tile k's chunk (never falling); lead0 = 0:
+// plain consumption order. Writes order[i] (the i-th tile taken) and begin[k] / end[k] (when
+// tile k computed) and returns the number of tiles taken: -1 for bad arguments, -2 when a tile
+// out of range or one already taken comes up.
+int bilstm_model_stream_walk(int n, const int *chunks, int steps, int chunk, uint32_t lead0, double rate,
+                             double start, double tile_time, int *order, double *begin, double *end) {
+    if (n < 0 || chunks == nullptr || steps < 1 || chunk < 1 || rate <= 0.0 || tile_time <= 0.0 ||
+        order == nullptr || begin == nullptr || end == nullptr) {
+        return -1;
+    }
+    for (int k = 1; k < n; ++k) {
+        if (chunks[k] < chunks[k - 1]) return -1;
+    }
+    auto progress_at = [&](double t) {
+        const double s = std::floor(rate * t);
+        return static_cast<uint32_t>(s <= 0.0 ? 0.0 : s >= steps ? steps : s);
+    };
+    auto chunk_of = [&](int k) { return chunks[k]; };
+    bl::StreamWalk w;
+    const int mid = lead0 > 0 && n > 0 ? bl::stream_walk_mid(n, steps, chunk, chunk_of) : 0;
+    bl::stream_walk_init(w, n, mid, steps, lead0, lead0 > 0);
+    double t = start;
+    int cur, next;
+    bl::stream_walk_start(w, progress_at(t), cur, next);
+    std::vector<char> taken(static_cast<size_t>(n), 0);
+    int i = 0;
+    while (cur >= 0) {
+        if (i >= n || cur >= n || taken[static_cast<size_t>(cur)]) return -2;
+        taken[static_cast<size_t>(cur)] = 1;
+        order[i] = cur;
+        const uint32_t seen = progress_at(t);  // read at the tile's start
+        const int need = bl::chunk_need(steps, chunk, chunks[cur]);
+        begin[cur] = std::max(t, need / rate);
+        end[cur] = begin[cur] + tile_time;
+        const int after = next >= 0 ? bl::stream_walk_after(w, i, seen, static_cast<uint32_t>(need)) : -1;
+        t = end[cur];
+        cur = next;
+        next = after;
+        ++i;
+    }
+    return i;
+}
+
 }  // extern "C"
 
 #ifdef BILSTM_MODEL_MAIN
 // Stand-alone driver (the ThreadSanitizer build): every scenario once; exit status 0 when each
 // accepted value was its producer's and watchdogs fired exactly where a producer was missing.
 #include <cstdio>
+
+// The walk against a layout: every tile taken once, in the walk's shape (mid, mid - 1, ..., lo,
+// then 0 .. lo - 1, then mid + 1 .. n - 1; plain consumption order when lead0 = 0).
+static bool walk_is_whole(int n, const int *chunks, int steps, int chunk, uint32_t lead0, double rate, double start,
+                          double tile_time, std::vector<int> &order, std::vector<double> &end) {
+    order.assign(static_cast<size_t>(n), -1);
+    std::vector<double> begin(static_cast<size_t>(n));
+    end.assign(static_cast<size_t>(n), 0.0);
+    if (bilstm_model_stream_walk(n, chunks, steps, chunk, lead0, rate, start, tile_time, order.data(), begin.data(),
+                                 end.data()) != n) {
+        return false;
+    }
+    int i = 0;
+    const int mid = order[0];
+    while (i < n && order[static_cast<size_t>(i)] == mid - i) ++i;  // the walk down from order[0]
+    const int lo = mid - i + 1;
+    if (lead0 == 0 && mid != 0) return false;
+    std::vector<int> want;
+    if (lead0 == 0) {
+        for (int k = 0; k < n; ++k) want.push_back(k);
+    } else {
+        for (int k = mid; k >= lo; --k) want.push_back(k);
+        for (int k = 0; k < lo; ++k) want.push_back(k);
+        for (int k = mid + 1; k < n; ++k) want.push_back(k);
+    }
+    return want == order;
+}
+
+// The next layer's recurrence reading chunk c once its tile has ended (one tile per chunk).
+static double consumer_end(const std::vector<double> &end, double start, double chunk_time) {
+    double t = start;
+    for (double e : end) t = std::max(t, e) + chunk_time;
+    return t;
+}
+
+static int walk_checks() {
+    int failures = 0;
+    auto expect = [&](const char *name, bool ok) {
+        std::printf("%-40s %s\n", name, ok ? "ok" : "FAIL");
+        failures += ok ? 0 : 1;
+    };
+    // 4096 steps of 32-step chunks, one tile per chunk: the previous layer takes 1810 time
+    // units, a tile 17.6, and the workgroup starts at 900
+    std::vector<int> chunks(128);
+    for (int k = 0; k < 128; ++k) chunks[static_cast<size_t>(k)] = k;
+    const double rate = 4096.0 / 1810.0;
+    std::vector<int> plain, walked;
+    std::vector<double> plain_end, walked_end;
+    const bool whole = walk_is_whole(128, chunks.data(), 4096, 32, 0, rate, 900.0, 17.6, plain, plain_end) &&
+                       walk_is_whole(128, chunks.data(), 4096, 32, 64, rate, 900.0, 17.6, walked, walked_end);
+    expect("walk, every tile once", whole);
+    // chunks 63 and 64 need 2080 steps each: the walk starts at the later
+    expect("walk, starts at the last tile of least need", whole && walked[0] == 64);
+    expect("walk, chunk 0 no later", whole && walked_end[0] <= plain_end[0]);
+    expect("walk, the next layer ends earlier",
+           whole && consumer_end(walked_end, 1810.0, 1810.0 / 128) < 0.95 * consumer_end(plain_end, 1810.0, 1810.0 / 128));
+    // a workgroup's tiles on chunks 0, 2, 5, 8, 11, 14, 17 of 589 steps: chunk 8 needs least
+    const int few[] = {0, 2, 5, 8, 11, 14, 17};
+    expect("walk, seven tiles", walk_is_whole(7, few, 589, 32, 64, 589.0 / 270.0, 0.0, 10.0, walked, walked_end) &&
+                                    walked[0] == 3);
+    // random layouts, rates and starts
+    Rng rng(77);
+    bool all = true;
+    for (int trial = 0; trial < 300 && all; ++trial) {
+        const int n = 1 + static_cast<int>(rng.next() % 200);
+        const int chunk = 8 << (rng.next() % 4);
+        const int steps = 1 + static_cast<int>(rng.next() % 5000);
+        const int nchunks = (steps + chunk - 1) / chunk;
+        std::vector<int> layout(static_cast<size_t>(n));
+        for (int k = 0; k < n; ++k) layout[static_cast<size_t>(k)] = static_cast<int>(rng.next() % nchunks);
+        std::sort(layout.begin(), layout.end());
+        const double r = 0.5 + (rng.next() % 1000) / 200.0;
+        const double start = (rng.next() % 1000) / 1000.0 * steps / r;
+        const double tau = 0.5 + (rng.next() % 100);
+        const uint32_t lead0 = trial % 3 == 0 ? 0u : 1u + rng.next() % 200;
+        all = walk_is_whole(n, layout.data(), steps, chunk, lead0, r, start, tau, walked, walked_end);
+    }
+    expect("walk, random layouts", all);
+    // the lead counts from when the tile's rows were complete
+    expect("walk, lead from readiness", bl::stream_walk_lead(100, 40, 70) == 30 && bl::stream_walk_lead(100, 80, 70) == 20 &&
+                                            bl::stream_walk_lead(50, 40, 70) == 0);
+    return failures;
+}
 
 // argv[1]: the watchdog of the scenarios where every producer publishes, in ms (default 2000)
 int main(int argc, char **argv) {
@@ -401,6 +531,7 @@ int main(int argc, char **argv) {
     expect("progress, stale final words", r, false);
     bilstm_model_progress(3, 64, 16, 4, 2, 1, 50, 8, &r);
     expect("progress, a window never published", r, true);
+    failures += walk_checks();
     return failures == 0 ? 0 : 1;
 }
 #endif

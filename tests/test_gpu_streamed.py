@@ -102,6 +102,40 @@ def test_streamed_split_equals_unstreamed_split_bitwise(bl, batch, steps, tile, 
     assert np.array_equal(got[0].view(np.uint32), base[0].view(np.uint32))
 
 
+def tiles_per_projection_workgroup(info):
+    """Most streamed tiles one projection workgroup of a layer holds: chunks of stream_chunk
+    steps, windows in groups of 128 / stream_chunk, four 128-column tiles per chunk, direction
+    and group (chunk 0 cut `stream_split` times), on the CUs the recurrence leaves."""
+    chunk = info["stream_chunk"]
+    chunks = -(-info["steps"] // chunk)
+    groups = -(-info["batch"] // (128 // chunk))
+    tiles = (chunks - 1 + info["stream_split"]) * 2 * groups * 4
+    workgroups = max(8, (info["cu_count"] - 2 * info["recur_tiles"] * info["recur_groups"]) // 8 * 8)
+    return -(-tiles // workgroups)
+
+
+# Shapes whose projection workgroups hold 8 tiles or more each: beside the previous layer's
+# recurrence they take the tiles whose rows exist first (the walk), then the rest in order.
+WALK_SHAPES = [(64, 600), (48, 400), (96, 300), (64, 4096)]
+
+
+@pytest.mark.parametrize("projection", [4, 3])
+@pytest.mark.parametrize("pipeline", [2, 4])
+@pytest.mark.parametrize("batch,steps", WALK_SHAPES)
+def test_streamed_walk_equals_unstreamed_bitwise(bl, batch, steps, pipeline, projection):
+    """The walk changes when tiles are computed, not what they compute: bitwise equal to the
+    unstreamed stack, over two forwards on one plan."""
+    x = workloads.make_input(80 + batch, batch, steps)
+    layers = workloads.make_layers(81)
+    note(f"streamed walk pipeline={pipeline} projection={projection} batch={batch} steps={steps}")
+    got, info = run(bl, x, layers, repeats=2, pipeline=pipeline, projection=projection)
+    assert info["pipeline"] == 1 and info["stream_overlap"] == 1
+    assert tiles_per_projection_workgroup(info) >= 8
+    base, _ = run(bl, x, layers, pipeline=1, slices=1, projection=projection)
+    for g in got:
+        assert np.array_equal(g.view(np.uint32), base[0].view(np.uint32))
+
+
 @pytest.mark.parametrize("pipeline", [2, 4, 3])
 def test_streamed_repeated_forwards_are_bit_stable(bl, pipeline):
     """Five forwards on one plan: each pass's counters reach the next target exactly once."""
@@ -175,6 +209,26 @@ def test_streamed_watchdog_reports_timeout_and_grid_drains(bl, pipeline, project
     plan.close()
     got, _ = run(bl, xs, layers, pipeline=2)
     base, _ = run(bl, xs, layers, pipeline=1)
+    assert np.array_equal(got[0].view(np.uint32), base[0].view(np.uint32))
+
+
+@pytest.mark.parametrize("projection", [4, 3])
+def test_streamed_walk_watchdog_reports_timeout_and_grid_drains(bl, projection):
+    """As above on a shape whose projection workgroups walk (48 windows × 400 steps): with every
+    wait giving up at once the walk still takes each tile once and every workgroup ends."""
+    x = workloads.make_input(90, 48, 400)
+    layers = workloads.make_layers(91)
+    note(f"streamed walk watchdog first-miss projection={projection}")
+    plan = bl.Plan(layers, 48, 400, pipeline=2, watchdog_us=-1, projection=projection)
+    assert tiles_per_projection_workgroup(plan.info()) >= 8
+    plan.forward(torch.from_numpy(x).cuda())
+    with pytest.raises(bl.BilstmError) as e:
+        plan.check()
+    assert e.value.name == "BILSTM_TIMEOUT"
+    plan.check()
+    plan.close()
+    got, _ = run(bl, x, layers, pipeline=2, projection=projection)
+    base, _ = run(bl, x, layers, pipeline=1, slices=1, projection=projection)
     assert np.array_equal(got[0].view(np.uint32), base[0].view(np.uint32))
 
 

@@ -22,6 +22,7 @@ import re
 import shutil
 import subprocess
 
+import numpy as np
 import pytest
 
 from bidirectional_lstm_sequence_amd import _build
@@ -42,7 +43,11 @@ def model():
     lib.bilstm_model_exchange.argtypes = [i, i, i, i, i, i, u32, i, i, i, u32, i, u32, R]
     lib.bilstm_model_counters.argtypes = [i, i, i, i, i, u32, i, u32, i, u32, R]
     lib.bilstm_model_progress.argtypes = [i, i, i, i, u32, i, i, u32, R]
-    for f in (lib.bilstm_model_exchange, lib.bilstm_model_counters, lib.bilstm_model_progress):
+    D = ctypes.c_double
+    lib.bilstm_model_stream_walk.argtypes = [i, ctypes.POINTER(i), i, i, u32, D, D, D, ctypes.POINTER(i),
+                                             ctypes.POINTER(D), ctypes.POINTER(D)]
+    for f in (lib.bilstm_model_exchange, lib.bilstm_model_counters, lib.bilstm_model_progress,
+              lib.bilstm_model_stream_walk):
         f.restype = ctypes.c_int
     return lib
 
@@ -121,6 +126,77 @@ def test_progress_missing_window_ends_at_the_watchdog(model):
     assert r.wrong_values == 0 and r.timeouts == 1
 
 
+# ---- the tile walk of a streamed projection workgroup --------------------------------------
+
+def walk(model, chunks, steps, chunk, lead0, rate, start, tile_time):
+    n = len(chunks)
+    order, begin, end = (ctypes.c_int * n)(), (ctypes.c_double * n)(), (ctypes.c_double * n)()
+    taken = model.bilstm_model_stream_walk(n, (ctypes.c_int * n)(*chunks), steps, chunk, lead0, rate, start,
+                                           tile_time, order, begin, end)
+    assert taken == n, f"{taken} of {n} tiles taken"
+    return list(order), list(begin), list(end)
+
+
+def need(steps, chunk, c):
+    return max(min(c * chunk + chunk, steps), steps - c * chunk)
+
+
+def test_walk_off_is_consumption_order(model):
+    order, _, _ = walk(model, [0, 0, 1, 3, 3, 7], 256, 32, 0, 1.0, 0.0, 5.0)
+    assert order == list(range(6))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_walk_takes_every_tile_once(model, seed):
+    # the walk goes down from the last tile of least need while the previous layer runs, then
+    # the rest in consumption order: every tile once, in that shape
+    rng = np.random.default_rng(seed)
+    for _ in range(40):
+        chunk = int(rng.choice([8, 16, 32, 64]))
+        steps = int(rng.integers(1, 5000))
+        n = int(rng.integers(1, 300))
+        chunks = sorted(int(c) for c in rng.integers(0, (steps + chunk - 1) // chunk, n))
+        rate = float(rng.uniform(0.5, 5.0))
+        order, _, _ = walk(model, chunks, steps, chunk, int(rng.integers(1, 200)), rate,
+                           float(rng.uniform(0, steps / rate)), float(rng.uniform(0.5, 100)))
+        assert sorted(order) == list(range(n))
+        least = min(need(steps, chunk, c) for c in chunks)
+        mid = max(k for k in range(n) if need(steps, chunk, chunks[k]) == least)
+        if order[0] != 0 or mid == 0:
+            # it walked: mid, mid - 1, ..., lo, then 0 .. lo - 1, then mid + 1 .. n - 1
+            assert order[0] == mid
+            i = 0
+            while i < n and order[i] == mid - i:
+                i += 1
+            lo = mid - i + 1
+            assert order == list(range(mid, lo - 1, -1)) + list(range(lo)) + list(range(mid + 1, n))
+        else:
+            assert order == list(range(n))
+
+
+@pytest.mark.parametrize("start", [900.0, 1500.0, 1780.0])
+def test_walk_keeps_chunk_zero_on_time(model, start):
+    # 4096 steps in 32-step chunks, one tile per chunk, the previous layer 1810 time units, a
+    # tile 17.6: chunk 0 ends when it would in consumption order, and the next layer, reading
+    # chunk c once it has ended, finishes earlier the earlier the workgroup starts
+    chunks = list(range(128))
+    rate = 4096 / 1810
+
+    def next_layer_end(end):
+        t = 1810.0
+        for e in end:
+            t = max(t, e) + 1810 / 128
+        return t
+
+    _, _, plain = walk(model, chunks, 4096, 32, 0, rate, start, 17.6)
+    order, _, walked = walk(model, chunks, 4096, 32, 64, rate, start, 17.6)
+    assert order[0] == 64
+    assert walked[0] <= plain[0] == pytest.approx(1810 + 17.6)
+    gain = 1 - next_layer_end(walked) / next_layer_end(plain)
+    assert gain > {900.0: 0.08, 1500.0: 0.05, 1780.0: 0.0}[start] - 1e-12
+    assert max(walked) <= max(plain)
+
+
 # ---- planted mistakes: a copy of protocol.h with one rule broken must fail the model ------
 
 MUTANTS = {
@@ -133,6 +209,15 @@ MUTANTS = {
          "return (passes - 1) * static_cast<uint32_t>(kReadyPerPass) + skew;"),
     "progress compared without its pass number":
         (r"return seen >= \(pass_bits \| need\);", "return static_cast<uint32_t>(seen) >= need;"),
+    "walk resumes one tile past the walked range":
+        (r"if \(w\.next_in_order == w\.lo\) w\.next_in_order = w\.hi;",
+         "if (w.next_in_order == w.lo) w.next_in_order = w.hi + 1;"),
+    "walk ignores the previous layer's end":
+        (r"if \(w\.lo > 0 && static_cast<uint64_t>\(progress\)", "if (w.lo > 0 && true || static_cast<uint64_t>(progress)"),
+    "walk starts at the first tile of least need":
+        (r"chunk_of\(a - 1\)\) < chunk_need", "chunk_of(a - 1)) <= chunk_need"),
+    "walk's lead ignores when the rows were complete":
+        (r"const uint32_t from = before > ready_at \? before : ready_at;", "const uint32_t from = before;"),
 }
 
 
