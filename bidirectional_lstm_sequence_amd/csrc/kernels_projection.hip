@@ -35,8 +35,10 @@
 //  * Streamed order (projection_stream_kernel): the recurrences run at the same time on
 //    other CUs, this layer's reading the gates step by step and the previous layer's still
 //    writing this layer's input. Tiles then cover `group_windows` windows × `chunk`
-//    consecutive recurrence steps of one direction, walked in the order their inputs appear,
-//    and each waits for each K half of its rows before summing it, is computed on its own,
+//    consecutive recurrence steps of one direction, numbered in the order the recurrence reads
+//    them; beside the previous layer, a workgroup with several tiles first walks down from the
+//    chunks whose rows exist first (the middle ones), then takes the rest in that order
+//    (protocol.h). Each tile waits for each K half of its rows before summing it, is computed on its own,
 //    stored with agent-scope stores and, once those have completed, published by one counter
 //    increment. Its K steps go from memory straight into a 4-stage LDS ring (buffer loads with
 //    the LDS bit, rows swizzled instead of padded), three steps ahead of the products, with
@@ -1062,9 +1064,9 @@ __global__ __launch_bounds__(256, 2) void mfma_rate_kernel(const float *in, floa
 
 }  // namespace
 
-// The walk's assumed lead (previous-layer steps per streamed tile: about 40 measured for the
-// three-part split and 20-25 for FP32 products at 0.44-0.46 us per step) and the tiles per
-// workgroup from which it is used.
+// The walk's assumed lead and the tiles per workgroup from which the walk is used. The lead is
+// the previous layer's steps per streamed tile: about 40 for the three-part split (17-18 us per
+// tile beside the recurrence) and 20-25 for FP32 products, at 0.44-0.46 us per step.
 constexpr unsigned int kWalkLead = 64;
 constexpr int kWalkMinTiles = 8;
 
