@@ -198,10 +198,13 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
         }
         pipeline = true;
     } else if (want_pipe == 0) {
-        // auto: when the recurrence leaves at least a quarter of the CUs to the projection
-        // (measured on MI355X, 589 steps, unstreamed against streamed: 1 window 1.187 -> 1.168
-        // ms, 2 windows 1.228 -> 1.174, 4 windows 1.240 -> 1.179, 32 windows 1.405 -> 1.202).
-        pipeline = pipe_possible && concurrent == 2 && 4 * rec_wgs <= 3LL * cu_count;
+        // auto: when the recurrence leaves at least half of the CUs to the projection. Measured
+        // on MI355X at 589 steps, unstreamed against streamed: 1 window 1.187 -> 1.168 ms,
+        // 2 windows 1.228 -> 1.174, 4 windows 1.240 -> 1.179, 32 windows 1.405 -> 1.202,
+        // 48 windows 1.60 -> 1.19, 64 windows 1.48 -> 1.31 (and 64 x 4096 10.2 -> 7.9). With
+        // fewer CUs left the streamed projection sets the pace: 72 windows 1.56 against 1.64,
+        // 80 windows 1.61 against 2.06, 96 windows 1.81 against 3.54.
+        pipeline = pipe_possible && concurrent == 2 && 2 * rec_wgs <= static_cast<long long>(cu_count);
     }
     // windows per projection row block: up to 4, a multiple of the recurrence tile, so a
     // recurrence tile never spans two row blocks; chunk = 128 / that many steps

@@ -134,7 +134,7 @@ typedef struct {
                              running one still reads. The output is bitwise the same as without
                              it.
                              0 = auto (on when recur_groups = 1, concurrent = 2, the
-                             recurrence's grid leaves at least a quarter of the CUs free and the
+                             recurrence's grid leaves at least half of the CUs free and the
                              projection is the library's own), 1 = off,
                              2 = on (BILSTM_UNSUPPORTED unless recur_groups = 1, projection != 1,
                              slices <= 1 and at least 8 CUs stay free), with the next layer's

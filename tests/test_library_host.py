@@ -195,17 +195,18 @@ def test_projection_rule_ignores_the_plans_other_options(bl, batch, steps):
 
 @pytest.mark.parametrize("batch,steps,on,chunk", [(1, 589, 1, 128), (2, 589, 1, 64), (3, 589, 1, 32),
                                                    (7, 589, 1, 32), (8, 589, 1, 32), (16, 589, 1, 32),
-                                                   (32, 589, 1, 32), (64, 4096, 1, 32),
-                                                   (96, 589, 1, 32), (97, 589, 0, 0), (256, 589, 0, 0)])
+                                                   (32, 589, 1, 32), (64, 4096, 1, 32), (64, 589, 1, 32),
+                                                   (65, 589, 0, 0), (96, 589, 0, 0), (256, 589, 0, 0)])
 def test_schedule_streams_gates_when_the_recurrence_leaves_cus(bl, batch, steps, on, chunk):
     """Auto: streamed gates when the recurrence's grid (one workgroup per window and
-    direction) leaves at least a quarter of the 256 CUs to the projection; they replace the
-    batch slices."""
+    direction) leaves at least half of the 256 CUs to the projection; they replace the batch
+    slices. With fewer CUs the streamed projection sets the pace (96 windows: 3.5 ms streamed
+    against 1.8 unstreamed)."""
     s = bl.schedule(batch, steps, 256, 1)
     assert s["pipeline"] == on and s["stream_chunk"] == chunk
     if on:
         assert s["slices"] == 1 and s["recur_groups"] == 1 and s["concurrent"] == 2
-        assert 4 * 2 * s["recur_tiles"] <= 3 * 256
+        assert 2 * 2 * s["recur_tiles"] <= 256
         # a chunk's row block of 128 rows holds whole windows, a whole number of recurrence tiles
         assert 128 % chunk == 0 and (128 // chunk) % s["recur_tile"] == 0 and chunk % 4 == 0
 
@@ -229,7 +230,8 @@ def test_schedule_forced_streaming_checks_its_conditions(bl):
 
 
 @pytest.mark.parametrize("batch,steps,pipeline,overlap", [
-    (32, 589, 0, 1), (16, 589, 0, 1), (64, 4096, 0, 1), (96, 589, 0, 1), (32, 589, 3, 0), (64, 4096, 4, 1),
+    (32, 589, 0, 1), (16, 589, 0, 1), (64, 4096, 0, 1), (64, 589, 0, 1), (96, 589, 2, 1), (32, 589, 3, 0),
+    (64, 4096, 4, 1),
     (8, 589, 2, 1), (1, 589, 2, 1), (32, 589, 1, 0), (8, 589, 0, 1), (4, 589, 0, 1), (1, 589, 0, 1),
     (32, 589, 5, 0), (64, 4096, 5, 0)])
 def test_schedule_layer_overlap(bl, batch, steps, pipeline, overlap):
