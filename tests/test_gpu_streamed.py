@@ -136,6 +136,26 @@ def test_streamed_walk_equals_unstreamed_bitwise(bl, batch, steps, pipeline, pro
         assert np.array_equal(g.view(np.uint32), base[0].view(np.uint32))
 
 
+@pytest.mark.parametrize("batch,steps,forwards,projection", [(64, 600, 60, 4), (64, 600, 60, 3), (64, 4096, 12, 3)])
+def test_streamed_walk_many_forwards_are_bit_stable(bl, batch, steps, forwards, projection):
+    """Many forwards on one plan whose projection workgroups walk: the walk's choices depend
+    on timing, the gates do not, so every forward's output is the first one's, bit for bit
+    (compared as integers on the GPU), and the plan reports no error."""
+    x = workloads.make_input(70, batch, steps)
+    layers = workloads.make_layers(71)
+    note(f"streamed walk {forwards} forwards batch={batch} steps={steps} projection={projection}")
+    plan = bl.Plan(layers, batch, steps, pipeline=2, projection=projection)
+    assert tiles_per_projection_workgroup(plan.info()) >= 8
+    xd = torch.from_numpy(x).cuda()
+    first = plan.forward(xd).view(torch.int32).clone()
+    y = torch.empty((batch, steps, 256), dtype=torch.float32, device="cuda")
+    for _ in range(forwards - 1):
+        plan.forward(xd, y)
+        assert torch.equal(y.view(torch.int32), first)
+    plan.check()
+    plan.close()
+
+
 @pytest.mark.parametrize("pipeline", [2, 4, 3])
 def test_streamed_repeated_forwards_are_bit_stable(bl, pipeline):
     """Five forwards on one plan: each pass's counters reach the next target exactly once."""
