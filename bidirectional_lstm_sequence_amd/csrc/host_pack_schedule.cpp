@@ -254,9 +254,12 @@ bilstm_status schedule(uint32_t batch, uint32_t steps, int cu_count, int per_cu,
     info->stream_overlap = pipeline && want_pipe != 3 && want_pipe != 5 ? 1 : 0;
     info->stream_serial = pipeline && want_pipe == 5 ? 1 : 0;
     // 4: the four layers' recurrences as one launch, when one launch holds both directions of
-    // every tile. Not the default: a layer boundary waits for the next layer's first chunk
-    // either way, which outlasts a kernel launch, and a launch per layer measured faster
-    // (b32 1.2305 against 1.2390 ms, b8 1.2069 against 1.2091, b64_t4096 10.53 against 10.60).
+    // every tile. A layer boundary waits for the next layer's first chunk either way, which
+    // outlasts a kernel launch: on earlier builds a launch per layer measured faster, on the
+    // current one the single launch is 0.3-0.6 % faster at 1-32 windows (b32 1.1205 against
+    // 1.1167 ms). It is not the default because the HBM counters of the recurrence cannot be
+    // taken for it: counter collection runs kernels one at a time, and the single launch waits
+    // for projections that run beside it.
     info->stream_fused = info->stream_overlap && concurrent == 2 && launches == 1 && want_pipe == 4 ? 1 : 0;
     info->recur_groups = groups;
     info->recur_tile = tile;
